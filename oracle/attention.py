@@ -1,0 +1,273 @@
+"""CPU fp64 oracle for exact scaled-dot-product attention.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The GPU library
+never calls it and shares no code with it: the two meet only on the seeded
+inputs that ``exact_attention_24_amd.inputs`` generates.
+
+What is computed, and where the pages define it
+------------------------------------------------
+* Forward: O = softmax(scale * Q K^T + mask) V, with the N x N score matrix
+  S written out in full.  Definition: the attention formula at the top of
+  "Flash-Attention 2/3在ms-swift中的集成与性能提升" (bxzpzcl.cn), the formula in
+  section 一 of the adg.csdn.net flash_attn/Qwen page, and the standard flow of
+  "FlashAttention优化Transformer显存与计算效率" (jsqmd.com) section 2.1.
+  The method is exact, not an approximation (ms-swift long-text page, section
+  3.3; adg.csdn.net page, section 三; MindSpore page, "技术背景与核心优势"), so the
+  plain definition is the oracle.
+* Masks: causal and sliding window are the structured masks of the FA-3
+  paragraph of the ms-swift integration page; ``causal=True`` appears on every
+  API example of the MindSpore page.
+* LSE = m + ln(sum exp(S - m)) per row: the only forward residual the
+  recomputing backward needs ("重计算" in the ms-swift integration page and in
+  section 三 of the adg.csdn.net page).
+* Backward: the pages only say that S is recomputed rather than stored, so the
+  gradients are the textbook chain rule of L = sum(dO * O), written out with
+  this module's own fp64 P and O.
+* ``blocked_fwd``: the blockwise softmax of jsqmd.com section 2.2.2 (per-block
+  max m and exponent sum l, combined in a numerically stable way), with the
+  tile loop of section 2.2.1.  It exists to pin that the tiled recombination
+  equals the direct softmax; it is not the GPU algorithm.
+* fp8: ``e4m3_decode`` follows the OCP 8-bit floating point specification for
+  E4M3 (bias 7, no infinities, S.1111.111 is NaN, max finite 448); the fp8
+  forward is the plain definition applied to code * per-tensor scale (FA-3 FP8
+  paragraph of the ms-swift integration page).
+
+Readings where the pages are silent
+-----------------------------------
+* ``scale`` is applied as given; callers pass 1/sqrt(d) for the pages' default.
+* ``window = W > 0``: a query at aligned position p sees keys j with
+  p - W < j (W keys including itself); a left bound only.
+* Causal with Nq != Nk is bottom-right aligned: query i sits at key position
+  i + Nk - Nq.
+* A query row with no visible key gets O = 0 and LSE = -inf.
+
+Every function here is pinned by ``tests/test_oracle_*.py`` against closed
+forms, hand-derived golden values, finite differences, invariants and
+torch's CPU attention routine.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "visible",
+    "attention_fwd",
+    "attention_probs",
+    "attention_bwd",
+    "blocked_fwd",
+    "mha_fwd",
+    "mha_bwd",
+    "varlen_fwd",
+    "e4m3_decode",
+    "fp8_dequant",
+]
+
+
+def visible(q_pos, nk, causal, window, offset=0):
+    """Boolean [len(q_pos), nk] matrix: may query q_pos[a] see key j?
+
+    q_pos are query indices in [0, Nq); offset = Nk - Nq aligns them to key
+    positions (bottom-right).  Causal: j <= p.  Window W > 0: j > p - W.
+    """
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    p = (q_pos + offset)[:, None]
+    j = np.arange(nk, dtype=np.int64)[None, :]
+    ok = np.ones((q_pos.shape[0], nk), dtype=bool)
+    if causal:
+        ok &= j <= p
+    if window > 0:
+        ok &= j > p - window
+    return ok
+
+
+def _scores(q, k, scale, causal, window, q_pos, nq):
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    if q_pos is None:
+        q_pos = np.arange(q.shape[0])
+    if nq is None:
+        nq = q.shape[0]
+    s = float(scale) * (q @ k.T)
+    ok = visible(q_pos, k.shape[0], causal, window, offset=k.shape[0] - nq)
+    return np.where(ok, s, -np.inf)
+
+
+def _softmax_rows(s):
+    """Stable row softmax of masked scores; returns (P, m, l)."""
+    m = s.max(axis=1)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    p = np.exp(s - m_safe[:, None])  # exp(-inf) = 0 on masked entries
+    l = p.sum(axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        p = np.where(l[:, None] > 0, p / l[:, None], 0.0)
+    return p, m_safe, l
+
+
+def attention_probs(q, k, scale, causal=False, window=0, q_pos=None, nq=None):
+    """P = softmax(scale * Q K^T + mask), row by row (fp64)."""
+    p, _, _ = _softmax_rows(_scores(q, k, scale, causal, window, q_pos, nq))
+    return p
+
+
+def attention_fwd(q, k, v, scale, causal=False, window=0, q_pos=None, nq=None):
+    """One head: q [nq_sel, d], k [nk, d], v [nk, dv] -> (O [nq_sel, dv], LSE [nq_sel]).
+
+    ``q_pos`` (default 0..nq_sel-1) gives the index of each given row in a
+    query sequence of length ``nq`` (default nq_sel), so that sampled rows of a
+    long sequence can be checked one by one.  LSE is natural-log.
+    """
+    s = _scores(q, k, scale, causal, window, q_pos, nq)
+    p, m, l = _softmax_rows(s)
+    o = p @ np.asarray(v, dtype=np.float64)
+    with np.errstate(divide="ignore"):
+        lse = np.where(l > 0, m + np.log(l), -np.inf)
+    return o, lse
+
+
+def attention_bwd(q, k, v, dout, scale, causal=False, window=0):
+    """One head, all rows: gradients of L = sum(dout * O) w.r.t. q, k, v (fp64).
+
+    D_i = sum_c dO_ic O_ic;  dV = P^T dO;  dP = dO V^T;  dS = P * (dP - D);
+    dQ = scale dS K;  dK = scale dS^T Q.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(dout, dtype=np.float64)
+    p = attention_probs(q, k, scale, causal, window)
+    o = p @ v
+    d_row = (do * o).sum(axis=1)
+    dv = p.T @ do
+    dp = do @ v.T
+    ds = p * (dp - d_row[:, None])
+    dq = float(scale) * (ds @ k)
+    dk = float(scale) * (ds.T @ q)
+    return dq, dk, dv
+
+
+def blocked_fwd(q, k, v, scale, causal=False, window=0, br=16, bc=16):
+    """Blockwise online softmax over key blocks (jsqmd.com section 2.2.2).
+
+    For each block of ``br`` query rows, keep per row a running max m, a
+    running exponent sum l and an unnormalised output acc.  Each key block of
+    ``bc`` keys that the mask leaves at least partly visible updates them:
+      m' = max(m, rowmax S_blk);  alpha = exp(m - m') (0 while m = -inf);
+      P~ = exp(S_blk - m') (0 where masked);  l = alpha l + rowsum P~;
+      acc = alpha acc + P~ V_blk;  m = m'.
+    Key blocks the mask hides entirely for the whole row block are skipped.
+    At the end O = acc / l and LSE = m + ln l.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    nq, nk, dv = q.shape[0], k.shape[0], v.shape[1]
+    o = np.zeros((nq, dv))
+    lse = np.full(nq, -np.inf)
+    for r0 in range(0, nq, br):
+        rows = np.arange(r0, min(r0 + br, nq))
+        m = np.full(rows.size, -np.inf)
+        l = np.zeros(rows.size)
+        acc = np.zeros((rows.size, dv))
+        for c0 in range(0, nk, bc):
+            cols = np.arange(c0, min(c0 + bc, nk))
+            ok = visible(rows, nk, causal, window, offset=nk - nq)[:, cols]
+            if not ok.any():
+                continue  # tile skipping: nothing visible in this block
+            s = float(scale) * (q[rows] @ k[cols].T)
+            s = np.where(ok, s, -np.inf)
+            m_new = np.maximum(m, s.max(axis=1))
+            finite = np.isfinite(m_new)
+            m_ref = np.where(finite, m_new, 0.0)
+            alpha = np.where(np.isfinite(m), np.exp(m - m_ref), 0.0)
+            pt = np.exp(s - m_ref[:, None])
+            l = alpha * l + pt.sum(axis=1)
+            acc = alpha[:, None] * acc + pt @ v[cols]
+            m = m_new
+        has = l > 0
+        o[rows[has]] = acc[has] / l[has, None]
+        lse[rows[has]] = m[has] + np.log(l[has])
+    return o, lse
+
+
+def mha_fwd(q, k, v, scale, causal=False, window=0, heads=None):
+    """Dense multi-head forward in [B, N, H, d] layout.
+
+    Returns O [B, Nq, H, dv] and LSE [B, H, Nq].  ``heads`` restricts the
+    computation to a list of (b, h) pairs (others are left NaN), for large
+    shapes where only sampled heads are checked.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    b_, nq, h_, _ = q.shape
+    o = np.full((b_, nq, h_, v.shape[3]), np.nan)
+    lse = np.full((b_, h_, nq), np.nan)
+    pairs = heads if heads is not None else [(b, h) for b in range(b_) for h in range(h_)]
+    for b, h in pairs:
+        o[b, :, h], lse[b, h] = attention_fwd(q[b, :, h], k[b, :, h], v[b, :, h], scale, causal, window)
+    return o, lse
+
+
+def mha_bwd(q, k, v, dout, scale, causal=False, window=0, heads=None):
+    """Dense multi-head backward in [B, N, H, d] layout -> (dq, dk, dv)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    dq = np.full(q.shape, np.nan)
+    dk = np.full(k.shape, np.nan)
+    dv = np.full(v.shape, np.nan)
+    b_, _, h_, _ = q.shape
+    pairs = heads if heads is not None else [(b, h) for b in range(b_) for h in range(h_)]
+    for b, h in pairs:
+        dq[b, :, h], dk[b, :, h], dv[b, :, h] = attention_bwd(
+            q[b, :, h], k[b, :, h], v[b, :, h], dout[b, :, h], scale, causal, window)
+    return dq, dk, dv
+
+
+def varlen_fwd(q, k, v, cu_seqlens, scale, causal=False, window=0, heads=None, seqs=None):
+    """Packed sequences: q/k/v [total, H, d]; sequence s spans rows
+    cu_seqlens[s]:cu_seqlens[s+1] and attends only within itself.
+
+    Returns O [total, H, dv] and LSE [H, total].  ``heads`` / ``seqs`` restrict
+    the work to sampled heads / sequences (others left NaN).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    total, h_, _ = q.shape
+    o = np.full((total, h_, v.shape[2]), np.nan)
+    lse = np.full((h_, total), np.nan)
+    hs = range(h_) if heads is None else heads
+    ss = range(cu.size - 1) if seqs is None else seqs
+    for s in ss:
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b == a:
+            continue
+        for h in hs:
+            o[a:b, h], lse[h, a:b] = attention_fwd(q[a:b, h], k[a:b, h], v[a:b, h], scale, causal, window)
+    return o, lse
+
+
+def e4m3_decode(codes):
+    """OCP E4M3 byte codes -> fp64 values.
+
+    Layout s.eeee.mmm, exponent bias 7.  e = 0: subnormal, (-1)^s 2^-6 (m/8).
+    Otherwise (-1)^s 2^(e-7) (1 + m/8), except e = 15 and m = 7, which is NaN
+    (the format has no infinities; max finite = 2^8 * 1.75 = 448).
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    val = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int32)))
+    val = sign * val
+    return np.where((e == 15) & ((c & 0x7) == 7), np.nan, val)
+
+
+def fp8_dequant(codes, scale):
+    """Value an fp8 tensor stands for: decoded code times its per-tensor scale."""
+    return e4m3_decode(codes) * float(scale)

@@ -1,0 +1,79 @@
+"""The pins must be able to fail: plant plausible mistakes in the oracle (on
+the CPU, via monkeypatching) and check that some pin catches each one."""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.attention as oa
+import tests.test_oracle_pins as pins
+
+
+def _wrong_visible_offset(q_pos, nk, causal, window, offset=0):
+    return _ORIG_VISIBLE(q_pos, nk, causal, window, offset=0)  # forgets bottom-right alignment
+
+
+def _wrong_window(q_pos, nk, causal, window, offset=0):
+    return _ORIG_VISIBLE(q_pos, nk, causal, window + 1 if window else 0, offset)  # off by one
+
+
+def _no_scale_scores(q, k, scale, causal, window, q_pos, nq):
+    return _ORIG_SCORES(q, k, 1.0, causal, window, q_pos, nq)
+
+
+def _transposed_bwd(q, k, v, dout, scale, causal=False, window=0):
+    dq, dk, dv = _ORIG_BWD(q, k, v, dout, scale, causal, window)
+    return dq, dk, dv[::-1].copy()  # rows of dV in the wrong order
+
+
+def _bwd_drops_d(q, k, v, dout, scale, causal=False, window=0):
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dout))
+    p = oa.attention_probs(q, k, scale, causal, window)
+    ds = p * (do @ v.T)  # dP - D with the D term dropped
+    return scale * ds @ k, scale * ds.T @ q, p.T @ do
+
+
+_ORIG_VISIBLE = oa.visible
+_ORIG_SCORES = oa._scores
+_ORIG_BWD = oa.attention_bwd
+
+
+def _blocked_no_rescale(q, k, v, scale, causal=False, window=0, br=16, bc=16):
+    """The per-block softmax of jsqmd.com 2.2.1 taken literally: no alpha."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    nq, nk = q.shape[0], k.shape[0]
+    o = np.zeros((nq, v.shape[1]))
+    lse = np.zeros(nq)
+    for r0 in range(0, nq, br):
+        rows = np.arange(r0, min(r0 + br, nq))
+        acc = np.zeros((rows.size, v.shape[1]))
+        l = np.zeros(rows.size)
+        for c0 in range(0, nk, bc):
+            cols = np.arange(c0, min(c0 + bc, nk))
+            ok = oa.visible(rows, nk, causal, window, offset=nk - nq)[:, cols]
+            s = np.where(ok, scale * q[rows] @ k[cols].T, -np.inf)
+            m = np.where(np.isfinite(s.max(1)), s.max(1), 0)
+            pt = np.exp(s - m[:, None])
+            acc += pt @ v[cols]
+            l += pt.sum(1)
+        o[rows] = acc / np.maximum(l, 1e-300)[:, None]
+    return o, lse
+
+
+MUTATIONS = [
+    ("visible", _wrong_visible_offset, lambda: pins.test_forward_matches_torch_sdpa(17, 29, True, 0)),
+    ("visible", _wrong_window, lambda: pins.test_scale_zero_is_mean_over_visible_keys(True, 4)),
+    ("_scores", _no_scale_scores, lambda: pins.test_single_key()),
+    ("attention_bwd", _transposed_bwd, lambda: pins.test_backward_matches_torch_autograd(True, 0)),
+    ("attention_bwd", _bwd_drops_d, lambda: pins.test_backward_identities(True, 0)),
+    ("blocked_fwd", _blocked_no_rescale,
+     lambda: pins.test_blocked_online_softmax_equals_direct(37, 8, 5, False, 0)),
+]
+
+
+@pytest.mark.parametrize("attr,mutant,pin", MUTATIONS, ids=[m[1].__name__ for m in MUTATIONS])
+def test_planted_mistake_is_caught(monkeypatch, attr, mutant, pin):
+    monkeypatch.setattr(oa, attr, mutant)
+    monkeypatch.setattr(oracle, attr, mutant, raising=False)
+    with pytest.raises(AssertionError):
+        pin()

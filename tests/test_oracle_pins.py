@@ -1,0 +1,329 @@
+"""Pins of the CPU oracle against things other than itself (no GPU).
+
+Each test ties an oracle function to a closed form, a hand-derived value, an
+invariant, finite differences or an independent library routine (torch's CPU
+attention and autograd), chosen so that a plausible mistake in the oracle --
+a dropped scale, a wrong mask sign or offset, a transposed operand, a missing
+rescale in the blocked recurrence, a wrong gradient term -- fails at least one.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")
+_EXPR_ENV = {"log": math.log, "sqrt": math.sqrt}
+
+
+def _ev(x):
+    if isinstance(x, list):
+        return np.array([_ev(e) for e in x], dtype=np.float64)
+    return float(eval(x, {"__builtins__": {}}, _EXPR_ENV))  # fixture expressions only
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+# --------------------------------------------------------------------------
+# hand-derived worked examples (tests/golden/hand_examples.json)
+# --------------------------------------------------------------------------
+def _golden_cases():
+    with open(GOLDEN, encoding="utf-8") as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_golden_forward(case):
+    q, k, v = _ev(case["q"]), _ev(case["k"]), _ev(case["v"])
+    o, lse = oracle.attention_fwd(q, k, v, _ev(case["scale"]), case["causal"], case["window"])
+    np.testing.assert_allclose(o, _ev(case["o"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, _ev(case["lse"]), rtol=0, atol=1e-12)
+    ob, lseb = oracle.blocked_fwd(q, k, v, _ev(case["scale"]), case["causal"], case["window"], br=1, bc=1)
+    np.testing.assert_allclose(ob, _ev(case["o"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lseb, _ev(case["lse"]), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", [c for c in _golden_cases() if "dq" in c], ids=lambda c: c["name"])
+def test_golden_backward(case):
+    q, k, v, do = _ev(case["q"]), _ev(case["k"]), _ev(case["v"]), _ev(case["dout"])
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, _ev(case["scale"]), case["causal"], case["window"])
+    np.testing.assert_allclose(dq, _ev(case["dq"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, _ev(case["dk"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, _ev(case["dv"]), rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# invariants and closed forms
+# --------------------------------------------------------------------------
+MASKS = [(False, 0), (True, 0), (True, 5), (False, 4)]
+
+
+@pytest.mark.parametrize("causal,window", MASKS)
+def test_rows_sum_to_one(causal, window):
+    rng = np.random.default_rng(1)
+    q, k = _rand(rng, 23, 16), _rand(rng, 23, 16)
+    p = oracle.attention_probs(q, k, 0.3, causal, window)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-14)
+    assert (p >= 0).all()
+
+
+@pytest.mark.parametrize("causal,window", MASKS)
+def test_constant_v_returns_v(causal, window):
+    rng = np.random.default_rng(2)
+    q, k = _rand(rng, 19, 8), _rand(rng, 19, 8)
+    row = _rand(rng, 8)
+    v = np.tile(row, (19, 1))
+    o, _ = oracle.attention_fwd(q, k, v, 0.5, causal, window)
+    np.testing.assert_allclose(o, np.tile(row, (19, 1)), atol=1e-13)
+
+
+def test_single_key():
+    rng = np.random.default_rng(3)
+    q, k, v = _rand(rng, 7, 8), _rand(rng, 1, 8), _rand(rng, 1, 5)
+    o, lse = oracle.attention_fwd(q, k, v, 0.7)
+    np.testing.assert_allclose(o, np.tile(v[0], (7, 1)), atol=1e-14)
+    np.testing.assert_allclose(lse, 0.7 * (q @ k[0]), atol=1e-13)
+
+
+@pytest.mark.parametrize("window", [0, 3])
+def test_causal_row0_is_v0(window):
+    rng = np.random.default_rng(4)
+    q, k, v = _rand(rng, 9, 8), _rand(rng, 9, 8), _rand(rng, 9, 6)
+    o, lse = oracle.attention_fwd(q, k, v, 0.4, True, window)
+    assert np.array_equal(o[0], v[0])
+    np.testing.assert_allclose(lse[0], 0.4 * q[0] @ k[0], atol=1e-14)
+
+
+@pytest.mark.parametrize("causal,window", [(True, 0), (True, 4), (False, 3), (False, 0)])
+def test_scale_zero_is_mean_over_visible_keys(causal, window):
+    """scale = 0: uniform weights over the visible keys -> cumulative/windowed mean."""
+    rng = np.random.default_rng(5)
+    n = 13
+    q, k, v = _rand(rng, n, 4), _rand(rng, n, 4), _rand(rng, n, 3)
+    o, lse = oracle.attention_fwd(q, k, v, 0.0, causal, window)
+    for i in range(n):
+        lo = max(0, i - window + 1) if window > 0 else 0
+        hi = i + 1 if causal else n
+        np.testing.assert_allclose(o[i], v[lo:hi].mean(axis=0), atol=1e-14)
+        assert lse[i] == pytest.approx(math.log(hi - lo), abs=1e-14)
+
+
+def test_shift_invariance_large_offset():
+    """Adding the same vector u to every key shifts each row's logits by a
+    constant, which softmax ignores; a huge u exercises the max subtraction."""
+    rng = np.random.default_rng(6)
+    q, k, v = _rand(rng, 11, 8), _rand(rng, 11, 8), _rand(rng, 11, 8)
+    u = 300.0 * _rand(rng, 8)
+    for causal, window in MASKS:
+        o1, lse1 = oracle.attention_fwd(q, k, v, 0.9, causal, window)
+        o2, lse2 = oracle.attention_fwd(q, k + u, v, 0.9, causal, window)
+        assert np.isfinite(o2).all()
+        np.testing.assert_allclose(o2, o1, atol=1e-10)
+        np.testing.assert_allclose(lse2 - lse1, 0.9 * q @ u, atol=1e-9)
+
+
+def test_fully_masked_row_zero_and_neg_inf():
+    rng = np.random.default_rng(7)
+    q, k, v = _rand(rng, 4, 4), _rand(rng, 2, 4), _rand(rng, 2, 4)
+    # causal, Nq=4 > Nk=2: bottom-right alignment -> rows 0,1 see nothing
+    o, lse = oracle.attention_fwd(q, k, v, 1.0, True, 0)
+    assert (o[:2] == 0).all() and np.isneginf(lse[:2]).all()
+    assert np.isfinite(o[2:]).all()
+    ob, lseb = oracle.blocked_fwd(q, k, v, 1.0, True, 0, br=3, bc=1)
+    np.testing.assert_allclose(ob, o, atol=1e-14)
+    assert np.isneginf(lseb[:2]).all()
+
+
+@pytest.mark.parametrize("n,br,bc,causal,window", [
+    (37, 8, 5, False, 0), (37, 8, 5, True, 0), (64, 16, 16, True, 0), (64, 8, 16, True, 9),
+    (37, 5, 8, True, 6), (50, 7, 3, False, 11), (1, 4, 4, True, 0),
+])
+def test_blocked_online_softmax_equals_direct(n, br, bc, causal, window):
+    rng = np.random.default_rng(8 + n + br)
+    q, k, v = 2 * _rand(rng, n, 16), 2 * _rand(rng, n, 16), _rand(rng, n, 12)
+    o, lse = oracle.attention_fwd(q, k, v, 0.25, causal, window)
+    ob, lseb = oracle.blocked_fwd(q, k, v, 0.25, causal, window, br=br, bc=bc)
+    np.testing.assert_allclose(ob, o, atol=1e-13)
+    np.testing.assert_allclose(lseb, lse, atol=1e-13)
+
+
+def test_sampled_rows_match_full():
+    rng = np.random.default_rng(9)
+    q, k, v = _rand(rng, 30, 8), _rand(rng, 30, 8), _rand(rng, 30, 8)
+    o, lse = oracle.attention_fwd(q, k, v, 0.3, True, 7)
+    idx = np.array([0, 5, 17, 29])
+    os_, ls_ = oracle.attention_fwd(q[idx], k, v, 0.3, True, 7, q_pos=idx, nq=30)
+    np.testing.assert_allclose(os_, o[idx], atol=1e-15)
+    np.testing.assert_allclose(ls_, lse[idx], atol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# torch's CPU attention routine and autograd as an independent reference
+# --------------------------------------------------------------------------
+def _torch_mask(nq, nk, causal, window):
+    i = torch.arange(nq)[:, None] + (nk - nq)
+    j = torch.arange(nk)[None, :]
+    ok = torch.ones(nq, nk, dtype=torch.bool)
+    if causal:
+        ok &= j <= i
+    if window > 0:
+        ok &= j > i - window
+    return ok
+
+
+@pytest.mark.parametrize("nq,nk,causal,window", [
+    (33, 33, False, 0), (33, 33, True, 0), (40, 40, True, 8), (17, 29, True, 0), (16, 48, True, 5),
+])
+def test_forward_matches_torch_sdpa(nq, nk, causal, window):
+    g = torch.Generator().manual_seed(nq * 7 + nk)
+    q = torch.randn(nq, 16, generator=g, dtype=torch.float64)
+    k = torch.randn(nk, 16, generator=g, dtype=torch.float64)
+    v = torch.randn(nk, 10, generator=g, dtype=torch.float64)
+    mask = _torch_mask(nq, nk, causal, window)
+    ref = F.scaled_dot_product_attention(q[None], k[None], v[None], attn_mask=mask[None], scale=0.35)[0]
+    o, lse = oracle.attention_fwd(q.numpy(), k.numpy(), v.numpy(), 0.35, causal, window)
+    np.testing.assert_allclose(o, ref.numpy(), atol=1e-12)
+    s = (0.35 * q @ k.T).masked_fill(~mask, float("-inf"))
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=1).numpy(), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 6)])
+def test_backward_matches_torch_autograd(causal, window):
+    g = torch.Generator().manual_seed(11)
+    n, d = 21, 8
+    q = torch.randn(n, d, generator=g, dtype=torch.float64, requires_grad=True)
+    k = torch.randn(n, d, generator=g, dtype=torch.float64, requires_grad=True)
+    v = torch.randn(n, d, generator=g, dtype=torch.float64, requires_grad=True)
+    do = torch.randn(n, d, generator=g, dtype=torch.float64)
+    mask = _torch_mask(n, n, causal, window)
+    out = F.scaled_dot_product_attention(q[None], k[None], v[None], attn_mask=mask[None], scale=0.6)[0]
+    out.backward(do)
+    dq, dk, dv = oracle.attention_bwd(q.detach().numpy(), k.detach().numpy(), v.detach().numpy(),
+                                      do.numpy(), 0.6, causal, window)
+    np.testing.assert_allclose(dq, q.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, k.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, v.grad.numpy(), atol=1e-12)
+
+
+def test_mha_layout_matches_torch_bhnd():
+    """mha_fwd takes [B, N, H, d]; torch's routine takes [B, H, N, d]."""
+    g = torch.Generator().manual_seed(12)
+    q = torch.randn(2, 24, 3, 8, generator=g, dtype=torch.float64)
+    k = torch.randn(2, 24, 3, 8, generator=g, dtype=torch.float64)
+    v = torch.randn(2, 24, 3, 8, generator=g, dtype=torch.float64)
+    ref = F.scaled_dot_product_attention(q.transpose(1, 2), k.transpose(1, 2), v.transpose(1, 2),
+                                         is_causal=True, scale=0.5).transpose(1, 2)
+    o, lse = oracle.mha_fwd(q.numpy(), k.numpy(), v.numpy(), 0.5, causal=True)
+    np.testing.assert_allclose(o, ref.numpy(), atol=1e-12)
+    assert lse.shape == (2, 3, 24)
+
+
+def test_varlen_matches_block_diagonal_sdpa():
+    """Packed sequences attend only within themselves: the same as one long
+    sequence under a block-diagonal (and causal, windowed) mask."""
+    lengths = [5, 1, 12, 7]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    total = int(cu[-1])
+    g = torch.Generator().manual_seed(13)
+    q = torch.randn(total, 2, 8, generator=g, dtype=torch.float64)
+    k = torch.randn(total, 2, 8, generator=g, dtype=torch.float64)
+    v = torch.randn(total, 2, 8, generator=g, dtype=torch.float64)
+    seg = torch.repeat_interleave(torch.arange(len(lengths)), torch.tensor(lengths))
+    pos = torch.arange(total) - torch.tensor(cu[:-1])[seg]
+    window = 4
+    same = seg[:, None] == seg[None, :]
+    causal = pos[None, :] <= pos[:, None]
+    win = pos[None, :] > pos[:, None] - window
+    mask = same & causal & win
+    ref = F.scaled_dot_product_attention(q.transpose(0, 1), k.transpose(0, 1), v.transpose(0, 1),
+                                         attn_mask=mask[None], scale=0.4).transpose(0, 1)
+    o, lse = oracle.varlen_fwd(q.numpy(), k.numpy(), v.numpy(), cu, 0.4, True, window)
+    np.testing.assert_allclose(o, ref.numpy(), atol=1e-12)
+    assert lse.shape == (2, total)
+
+
+# --------------------------------------------------------------------------
+# backward: finite differences and identities
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("causal,window", [(True, 0), (False, 0), (True, 3)])
+def test_backward_finite_differences(causal, window):
+    rng = np.random.default_rng(14)
+    n, d, scale, h = 6, 4, 0.7, 1e-6
+    q, k, v, do = (_rand(rng, n, d) for _ in range(4))
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.attention_fwd(qq, kk, vv, scale, causal, window)
+        return float((do * o).sum())
+
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, scale, causal, window)
+    for which, g in ((0, dq), (1, dk), (2, dv)):
+        num = np.zeros_like(g)
+        for idx in np.ndindex(g.shape):
+            plus = [q.copy(), k.copy(), v.copy()]
+            minus = [q.copy(), k.copy(), v.copy()]
+            plus[which][idx] += h
+            minus[which][idx] -= h
+            num[idx] = (loss(*plus) - loss(*minus)) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8)
+
+
+@pytest.mark.parametrize("causal,window", [(True, 0), (False, 0), (True, 5)])
+def test_backward_identities(causal, window):
+    rng = np.random.default_rng(15)
+    n, d = 17, 8
+    q, k, v, do = (_rand(rng, n, d) for _ in range(4))
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, 0.5, causal, window)
+    # each softmax-Jacobian row sums to zero -> sum over keys of dK vanishes
+    np.testing.assert_allclose(dk.sum(axis=0), 0.0, atol=1e-12)
+    # every row of P sums to one -> sum over keys of dV equals sum over queries of dO
+    np.testing.assert_allclose(dv.sum(axis=0), do.sum(axis=0), atol=1e-12)
+    # D_i = rowsum(dO * O) = sum_j P_ij dP_ij
+    p = oracle.attention_probs(q, k, 0.5, causal, window)
+    o, _ = oracle.attention_fwd(q, k, v, 0.5, causal, window)
+    np.testing.assert_allclose((do * o).sum(1), (p * (do @ v.T)).sum(1), atol=1e-12)
+
+
+def test_mha_bwd_layout():
+    rng = np.random.default_rng(16)
+    q, k, v, do = (_rand(rng, 1, 9, 2, 4) for _ in range(4))
+    dq, dk, dv = oracle.mha_bwd(q, k, v, do, 0.5, causal=True)
+    for h in range(2):
+        r = oracle.attention_bwd(q[0, :, h], k[0, :, h], v[0, :, h], do[0, :, h], 0.5, True)
+        np.testing.assert_allclose(dq[0, :, h], r[0], atol=0)
+        np.testing.assert_allclose(dk[0, :, h], r[1], atol=0)
+        np.testing.assert_allclose(dv[0, :, h], r[2], atol=0)
+
+
+# --------------------------------------------------------------------------
+# fp8 e4m3 decoding (OCP definition) vs torch's float8_e4m3fn
+# --------------------------------------------------------------------------
+def test_e4m3_decode_known_values():
+    assert oracle.e4m3_decode(np.uint8(0x7E)) == 448.0
+    assert oracle.e4m3_decode(np.uint8(0xFE)) == -448.0
+    assert oracle.e4m3_decode(np.uint8(0x38)) == 1.0
+    assert oracle.e4m3_decode(np.uint8(0x08)) == 2.0 ** -6
+    assert oracle.e4m3_decode(np.uint8(0x01)) == 2.0 ** -9
+    assert oracle.e4m3_decode(np.uint8(0x00)) == 0.0
+    assert np.isnan(oracle.e4m3_decode(np.uint8(0x7F)))
+    assert np.isnan(oracle.e4m3_decode(np.uint8(0xFF)))
+
+
+def test_e4m3_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.e4m3_decode(codes)
+    both_nan = np.isnan(ref) & np.isnan(got)
+    assert (both_nan | (ref == got)).all()
+
+
+def test_fp8_dequant():
+    codes = np.array([0x38, 0x40, 0xB8], dtype=np.uint8)  # 1, 2, -1
+    np.testing.assert_array_equal(oracle.fp8_dequant(codes, 0.5), [0.5, 1.0, -0.5])

@@ -1,0 +1,15 @@
+"""Exact attention for AMD Instinct MI355X (gfx950).
+
+The computation runs in hand-written HIP kernels behind the C ABI of
+``include/fa.h`` (``libfa.so``, built in-tree by ``build.py``); this package is
+the thin Python binding over it.  Importing the package does not load the
+library; the first call does, and raises if it is not built.
+"""
+
+from .binding import (  # noqa: F401
+    FA_BF16, FA_F32, FA_FP8_E4M3, FaError, fa_bwd, fa_bwd_workspace_bytes, fa_check_bwd,
+    fa_check_fwd, fa_check_varlen_fwd, fa_fwd, fa_varlen_fwd, lib,
+)
+
+__all__ = ["fa_fwd", "fa_varlen_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_check_fwd",
+           "fa_check_varlen_fwd", "fa_check_bwd", "lib", "FaError"]

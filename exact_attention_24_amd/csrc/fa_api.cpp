@@ -1,0 +1,312 @@
+// C ABI of the exact-attention library (declared in include/fa.h).
+//
+// Host side only: argument validation that never touches a device, the
+// per-device architecture check, translation of the public parameter structs
+// into the kernels' argument structs, and launches on the caller's stream.
+// Error classes mirror the pages' conventions (ms-swift long-text page,
+// section 4.3): mixed dtypes are a "same dtype" error, a missing or
+// unsupported GPU build is a runtime error.
+
+#include "fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "fa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fa_status fail(fa_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+fa_status ok() {
+  g_last_error.clear();
+  return FA_OK;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool valid_dtype(int d) { return d == FA_F32 || d == FA_BF16 || d == FA_FP8_E4M3; }
+
+int dtype_bytes(fa_dtype d) { return d == FA_F32 ? 4 : d == FA_BF16 ? 2 : 1; }
+
+// Common checks of the forward parameters shared by the dense and varlen
+// entry points.
+fa_status check_fwd_common(fa_dtype qkv, fa_dtype o, int32_t heads, int32_t head_dim,
+                           float scale, int32_t causal, int32_t window, float qd, float kd,
+                           float vd) {
+  if (!valid_dtype(qkv) || !valid_dtype(o))
+    return fail(FA_ERR_INVALID_ARGUMENT, "unknown dtype code (qkv_dtype=%d, o_dtype=%d)", (int)qkv, (int)o);
+  const bool combo = (qkv == FA_F32 && o == FA_F32) || (qkv == FA_BF16 && o == FA_BF16) ||
+                     (qkv == FA_FP8_E4M3 && o == FA_BF16);
+  if (!combo)
+    return fail(FA_ERR_DTYPE_MISMATCH,
+                "Input and output tensors must have the same dtype (fp8 inputs give bf16 output); "
+                "got qkv_dtype=%d o_dtype=%d", (int)qkv, (int)o);
+  if (heads < 0) return fail(FA_ERR_INVALID_ARGUMENT, "heads must be >= 0 (got %d)", heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  if (!(std::isfinite(scale) && scale > 0.f))
+    return fail(FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0 (got %g)", (double)scale);
+  if (causal != 0 && causal != 1)
+    return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", causal);
+  if (window < 0) return fail(FA_ERR_INVALID_ARGUMENT, "window must be >= 0 (got %d)", window);
+  if (qkv == FA_FP8_E4M3) {
+    if (!(std::isfinite(qd) && qd > 0.f && std::isfinite(kd) && kd > 0.f && std::isfinite(vd) && vd > 0.f))
+      return fail(FA_ERR_INVALID_ARGUMENT, "fp8 descales must be finite and > 0 (got %g, %g, %g)",
+                  (double)qd, (double)kd, (double)vd);
+  } else if (qd != 1.f || kd != 1.f || vd != 1.f) {
+    return fail(FA_ERR_INVALID_ARGUMENT, "descales must be 1 for non-fp8 inputs (got %g, %g, %g)",
+                (double)qd, (double)kd, (double)vd);
+  }
+  return FA_OK;
+}
+
+// Row alignment: every row the kernels load with 16-byte accesses must start
+// 16-byte aligned, i.e. pointer and all token/head/batch strides.
+fa_status check_tensor(const char *name, const void *ptr, const int64_t *stride, int nstride,
+                       int elem_bytes, bool empty) {
+  if (empty) return FA_OK;
+  if (!ptr) return fail(FA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  for (int i = 0; i < nstride; ++i)
+    if (stride[i] < 0) return fail(FA_ERR_INVALID_ARGUMENT, "%s stride[%d] must be >= 0 (got %lld)",
+                                   name, i, (long long)stride[i]);
+  if (elem_bytes < 4) {
+    const int64_t a = 16 / elem_bytes;
+    if (reinterpret_cast<uintptr_t>(ptr) % 16)
+      return fail(FA_ERR_INVALID_ARGUMENT, "%s must be 16-byte aligned", name);
+    for (int i = 0; i < nstride; ++i)
+      if (stride[i] % a)
+        return fail(FA_ERR_INVALID_ARGUMENT, "%s stride[%d] must be a multiple of %lld elements (got %lld)",
+                    name, i, (long long)a, (long long)stride[i]);
+  }
+  return FA_OK;
+}
+
+// Per-device architecture check, cached.
+std::mutex g_arch_mu;
+int g_arch_ok[64];  // 0 unknown, 1 gfx950, -1 other
+
+fa_status check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(FA_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_arch_mu);
+  if (g_arch_ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+    g_arch_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    if (g_arch_ok[dev] < 0)
+      return fail(FA_ERR_UNSUPPORTED, "this library is built for gfx950 only (device %d is %s)", dev,
+                  prop.gcnArchName);
+  }
+  if (g_arch_ok[dev] < 0) return fail(FA_ERR_UNSUPPORTED, "this library is built for gfx950 only");
+  return FA_OK;
+}
+
+fa_status launched(hipError_t e) {
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+const char *fa_last_error(void) { return g_last_error.c_str(); }
+
+fa_status fa_check_fwd(const fa_fwd_params *p) {
+  if (!p) return fail(FA_ERR_INVALID_ARGUMENT, "params is NULL");
+  fa_status st = check_fwd_common(p->qkv_dtype, p->o_dtype, p->heads, p->head_dim, p->softmax_scale,
+                                  p->causal, p->window, p->q_descale, p->k_descale, p->v_descale);
+  if (st != FA_OK) return st;
+  if (p->batch < 0 || p->seqlen_q < 0 || p->seqlen_k < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "sizes must be >= 0 (batch=%d seqlen_q=%d seqlen_k=%d)", p->batch,
+                p->seqlen_q, p->seqlen_k);
+  const bool q_empty = (int64_t)p->batch * p->seqlen_q * p->heads == 0;
+  const bool k_empty = (int64_t)p->batch * p->seqlen_k * p->heads == 0;
+  const int eb = dtype_bytes(p->qkv_dtype), ob = dtype_bytes(p->o_dtype);
+  if ((st = check_tensor("q", p->q, p->q_stride, 3, eb, q_empty)) != FA_OK) return st;
+  if ((st = check_tensor("k", p->k, p->k_stride, 3, eb, k_empty)) != FA_OK) return st;
+  if ((st = check_tensor("v", p->v, p->v_stride, 3, eb, k_empty)) != FA_OK) return st;
+  if ((st = check_tensor("o", p->o, p->o_stride, 3, ob, q_empty)) != FA_OK) return st;
+  const int64_t items = ceil_div(p->seqlen_q, fa::fwd_block_rows(p->qkv_dtype, p->head_dim)) *
+                        (int64_t)p->heads * p->batch;
+  if (items > INT32_MAX) return fail(FA_ERR_INVALID_ARGUMENT, "problem too large for one launch");
+  return ok();
+}
+
+fa_status fa_check_varlen_fwd(const fa_varlen_fwd_params *p) {
+  if (!p) return fail(FA_ERR_INVALID_ARGUMENT, "params is NULL");
+  fa_status st = check_fwd_common(p->qkv_dtype, p->o_dtype, p->heads, p->head_dim, p->softmax_scale,
+                                  p->causal, p->window, p->q_descale, p->k_descale, p->v_descale);
+  if (st != FA_OK) return st;
+  if (p->num_seqs < 0 || p->total_tokens < 0 || p->max_seqlen < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "sizes must be >= 0 (num_seqs=%d total_tokens=%d max_seqlen=%d)",
+                p->num_seqs, p->total_tokens, p->max_seqlen);
+  if (p->max_seqlen > p->total_tokens)
+    return fail(FA_ERR_INVALID_ARGUMENT, "max_seqlen (%d) exceeds total_tokens (%d)", p->max_seqlen,
+                p->total_tokens);
+  const bool empty = (int64_t)p->total_tokens * p->heads == 0 || p->num_seqs == 0;
+  if (!empty && !p->cu_seqlens) return fail(FA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
+  const int eb = dtype_bytes(p->qkv_dtype), ob = dtype_bytes(p->o_dtype);
+  if ((st = check_tensor("q", p->q, p->q_stride, 2, eb, empty)) != FA_OK) return st;
+  if ((st = check_tensor("k", p->k, p->k_stride, 2, eb, empty)) != FA_OK) return st;
+  if ((st = check_tensor("v", p->v, p->v_stride, 2, eb, empty)) != FA_OK) return st;
+  if ((st = check_tensor("o", p->o, p->o_stride, 2, ob, empty)) != FA_OK) return st;
+  const int64_t items = ceil_div(p->max_seqlen, fa::fwd_block_rows(p->qkv_dtype, p->head_dim)) *
+                        (int64_t)p->heads * p->num_seqs;
+  if (items > INT32_MAX) return fail(FA_ERR_INVALID_ARGUMENT, "problem too large for one launch");
+  return ok();
+}
+
+fa_status fa_check_bwd(const fa_bwd_params *p) {
+  if (!p) return fail(FA_ERR_INVALID_ARGUMENT, "params is NULL");
+  if (!valid_dtype(p->qkv_dtype) || !valid_dtype(p->grad_dtype))
+    return fail(FA_ERR_INVALID_ARGUMENT, "unknown dtype code (qkv_dtype=%d, grad_dtype=%d)",
+                (int)p->qkv_dtype, (int)p->grad_dtype);
+  if (p->qkv_dtype == FA_FP8_E4M3)
+    return fail(FA_ERR_UNSUPPORTED, "the backward pass is not available for fp8 inputs");
+  if (p->qkv_dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "the backward pass takes bf16 q/k/v/o/dout (got qkv_dtype=%d)",
+                (int)p->qkv_dtype);
+  if (p->grad_dtype != FA_F32 && p->grad_dtype != FA_BF16)
+    return fail(FA_ERR_DTYPE_MISMATCH, "gradients must be fp32 or bf16 (got grad_dtype=%d)", (int)p->grad_dtype);
+  if (p->heads < 0 || p->batch < 0 || p->seqlen_q < 0 || p->seqlen_k < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "sizes must be >= 0 (batch=%d seqlen_q=%d seqlen_k=%d heads=%d)",
+                p->batch, p->seqlen_q, p->seqlen_k, p->heads);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", p->head_dim);
+  if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f))
+    return fail(FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0 (got %g)", (double)p->softmax_scale);
+  if (p->causal != 0 && p->causal != 1)
+    return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", p->causal);
+  if (p->window < 0) return fail(FA_ERR_INVALID_ARGUMENT, "window must be >= 0 (got %d)", p->window);
+  if (p->deterministic != 0 && p->deterministic != 1)
+    return fail(FA_ERR_INVALID_ARGUMENT, "deterministic must be 0 or 1 (got %d)", p->deterministic);
+  const bool q_empty = (int64_t)p->batch * p->seqlen_q * p->heads == 0;
+  const bool k_empty = (int64_t)p->batch * p->seqlen_k * p->heads == 0;
+  const int gb = dtype_bytes(p->grad_dtype);
+  fa_status st;
+  if ((st = check_tensor("q", p->q, p->q_stride, 3, 2, q_empty)) != FA_OK) return st;
+  if ((st = check_tensor("k", p->k, p->k_stride, 3, 2, k_empty)) != FA_OK) return st;
+  if ((st = check_tensor("v", p->v, p->v_stride, 3, 2, k_empty)) != FA_OK) return st;
+  if ((st = check_tensor("o", p->o, p->o_stride, 3, 2, q_empty)) != FA_OK) return st;
+  if ((st = check_tensor("dout", p->dout, p->do_stride, 3, 2, q_empty)) != FA_OK) return st;
+  if ((st = check_tensor("dq", p->dq, p->dq_stride, 3, gb, q_empty)) != FA_OK) return st;
+  if ((st = check_tensor("dk", p->dk, p->dk_stride, 3, gb, k_empty)) != FA_OK) return st;
+  if ((st = check_tensor("dv", p->dv, p->dv_stride, 3, gb, k_empty)) != FA_OK) return st;
+  if (!q_empty && !p->lse) return fail(FA_ERR_INVALID_ARGUMENT, "lse is NULL");
+  return ok();
+}
+
+fa_status fa_fwd(const fa_fwd_params *p, void *stream) {
+  fa_status st = fa_check_fwd(p);
+  if (st != FA_OK) return st;
+  if ((int64_t)p->batch * p->heads * p->seqlen_q == 0) return ok();
+  if ((st = check_device()) != FA_OK) return st;
+  fa::FwdArgs a{};
+  a.q = p->q; a.k = p->k; a.v = p->v; a.o = p->o; a.lse = p->lse; a.cu_seqlens = nullptr;
+  a.q_sb = p->q_stride[0]; a.q_st = p->q_stride[1]; a.q_sh = p->q_stride[2];
+  a.k_sb = p->k_stride[0]; a.k_st = p->k_stride[1]; a.k_sh = p->k_stride[2];
+  a.v_sb = p->v_stride[0]; a.v_st = p->v_stride[1]; a.v_sh = p->v_stride[2];
+  a.o_sb = p->o_stride[0]; a.o_st = p->o_stride[1]; a.o_sh = p->o_stride[2];
+  a.lse_sb = (int64_t)p->heads * p->seqlen_q; a.lse_sh = p->seqlen_q;
+  a.batch = p->batch; a.heads = p->heads; a.nq = p->seqlen_q; a.nk = p->seqlen_k;
+  a.nqt = (int32_t)ceil_div(p->seqlen_q, fa::fwd_block_rows(p->qkv_dtype, p->head_dim));
+  a.causal = p->causal; a.window = p->window;
+  a.scale_log2 = p->softmax_scale * kLog2e * p->q_descale * p->k_descale;
+  a.v_descale = p->v_descale;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  switch (p->qkv_dtype) {
+    case FA_F32: return launched(fa::launch_fwd_f32(a, p->head_dim, s));
+    case FA_BF16: return launched(fa::launch_fwd_bf16(a, p->head_dim, s));
+    default: return launched(fa::launch_fwd_fp8(a, p->head_dim, s));
+  }
+}
+
+fa_status fa_varlen_fwd(const fa_varlen_fwd_params *p, void *stream) {
+  fa_status st = fa_check_varlen_fwd(p);
+  if (st != FA_OK) return st;
+  if ((int64_t)p->num_seqs * p->heads * p->max_seqlen == 0) return ok();
+  if ((st = check_device()) != FA_OK) return st;
+  fa::FwdArgs a{};
+  a.q = p->q; a.k = p->k; a.v = p->v; a.o = p->o; a.lse = p->lse; a.cu_seqlens = p->cu_seqlens;
+  a.q_sb = 0; a.q_st = p->q_stride[0]; a.q_sh = p->q_stride[1];
+  a.k_sb = 0; a.k_st = p->k_stride[0]; a.k_sh = p->k_stride[1];
+  a.v_sb = 0; a.v_st = p->v_stride[0]; a.v_sh = p->v_stride[1];
+  a.o_sb = 0; a.o_st = p->o_stride[0]; a.o_sh = p->o_stride[1];
+  a.lse_sb = 0; a.lse_sh = p->total_tokens;
+  a.batch = p->num_seqs; a.heads = p->heads; a.nq = p->max_seqlen; a.nk = p->max_seqlen;
+  a.nqt = (int32_t)ceil_div(p->max_seqlen, fa::fwd_block_rows(p->qkv_dtype, p->head_dim));
+  a.causal = p->causal; a.window = p->window;
+  a.scale_log2 = p->softmax_scale * kLog2e * p->q_descale * p->k_descale;
+  a.v_descale = p->v_descale;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  switch (p->qkv_dtype) {
+    case FA_F32: return launched(fa::launch_fwd_f32(a, p->head_dim, s));
+    case FA_BF16: return launched(fa::launch_fwd_bf16(a, p->head_dim, s));
+    default: return launched(fa::launch_fwd_fp8(a, p->head_dim, s));
+  }
+}
+
+size_t fa_bwd_workspace_bytes(const fa_bwd_params *p) {
+  if (fa_check_bwd(p) != FA_OK) return 0;
+  return fa::bwd_workspace_bytes(p->batch, p->heads, p->seqlen_q, p->head_dim, p->deterministic);
+}
+
+fa_status fa_bwd(const fa_bwd_params *p, void *workspace, size_t workspace_bytes, void *stream) {
+  fa_status st = fa_check_bwd(p);
+  if (st != FA_OK) return st;
+  const size_t need = fa::bwd_workspace_bytes(p->batch, p->heads, p->seqlen_q, p->head_dim, p->deterministic);
+  if (workspace_bytes < need)
+    return fail(FA_ERR_INVALID_ARGUMENT, "workspace too small (%zu bytes, need %zu)", workspace_bytes, need);
+  if (need && !workspace) return fail(FA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(FA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if ((int64_t)p->batch * p->heads * (p->seqlen_q + (int64_t)p->seqlen_k) == 0) return ok();
+  if ((st = check_device()) != FA_OK) return st;
+  fa::BwdArgs a{};
+  a.q = p->q; a.k = p->k; a.v = p->v; a.o = p->o; a.dout = p->dout; a.lse = p->lse;
+  a.dq = p->dq; a.dk = p->dk; a.dv = p->dv;
+  const size_t dsz = ((size_t)p->batch * p->heads * p->seqlen_q * sizeof(float) + 255) / 256 * 256;
+  a.dpsum = static_cast<float *>(workspace);
+  a.dq_accum = need > dsz ? reinterpret_cast<float *>(static_cast<char *>(workspace) + dsz) : nullptr;
+  a.q_sb = p->q_stride[0]; a.q_st = p->q_stride[1]; a.q_sh = p->q_stride[2];
+  a.k_sb = p->k_stride[0]; a.k_st = p->k_stride[1]; a.k_sh = p->k_stride[2];
+  a.v_sb = p->v_stride[0]; a.v_st = p->v_stride[1]; a.v_sh = p->v_stride[2];
+  a.o_sb = p->o_stride[0]; a.o_st = p->o_stride[1]; a.o_sh = p->o_stride[2];
+  a.do_sb = p->do_stride[0]; a.do_st = p->do_stride[1]; a.do_sh = p->do_stride[2];
+  a.dq_sb = p->dq_stride[0]; a.dq_st = p->dq_stride[1]; a.dq_sh = p->dq_stride[2];
+  a.dk_sb = p->dk_stride[0]; a.dk_st = p->dk_stride[1]; a.dk_sh = p->dk_stride[2];
+  a.dv_sb = p->dv_stride[0]; a.dv_st = p->dv_stride[1]; a.dv_sh = p->dv_stride[2];
+  a.batch = p->batch; a.heads = p->heads; a.nq = p->seqlen_q; a.nk = p->seqlen_k;
+  a.causal = p->causal; a.window = p->window; a.deterministic = p->deterministic;
+  a.grad_f32 = p->grad_dtype == FA_F32;
+  a.scale = p->softmax_scale;
+  a.scale_log2 = p->softmax_scale * kLog2e;
+  return launched(fa::launch_bwd_bf16(a, p->head_dim, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,427 @@
+// Forward kernels: exact attention by tiling with an online softmax.
+//
+// What is computed (per query row i of one (batch, head)):
+//   O_i = sum_j softmax_j(scale * q_i . k_j + mask_ij) v_j,   LSE_i = ln sum_j e^{...}
+// Definition: the attention formula of "Flash-Attention 2/3在ms-swift中的集成与性能提升"
+// and section 2.1 of "FlashAttention优化Transformer显存与计算效率" (jsqmd.com).
+// Method: Q/K/V are split into tiles held on chip (jsqmd.com 2.2.1), each key
+// tile updates a running row max m and exponent sum l (jsqmd.com 2.2.2), and
+// QK^T, mask, softmax and the P.V product run in one kernel (jsqmd.com 2.2.3),
+// so S never reaches HBM.  bf16 operands with fp32 softmax accumulation and a
+// conversion only at the output follow jsqmd.com 3.2.  Causal / sliding-window
+// tiles that the mask hides entirely are skipped (FA-3 paragraph of the
+// ms-swift integration page).
+//
+// gfx950 mapping of the bf16 kernel (one work-group = NW waves, 32 query rows
+// per wave, key tiles of 64):
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims read as
+//     16-byte rows of the K tile in LDS, B = Q^T held in VGPRs for the whole
+//     loop.  The 32x32 accumulator then gives every lane ONE query (lane % 32)
+//     and 16 keys, so the row max / row sum need only in-lane work plus one
+//     exchange with lane ^ 32.
+//   * O^T += V^T P^T on the same MFMA: B = P^T comes straight from the S^T
+//     accumulator registers (converted to bf16), A = V^T read from a
+//     transposed copy of the V tile in LDS whose key order inside each group
+//     of 16 keys matches the accumulator's layout, so no register shuffles are
+//     needed.  O^T again gives each lane one query, so the rescale by
+//     alpha = 2^(m_old - m_new) is a per-lane scalar.
+//   * K/V tiles stream global -> VGPR -> LDS with 16-byte coalesced loads,
+//     issued one tile ahead and double-buffered in LDS (one barrier per tile).
+//   * Work-group ids are renumbered so each XCD (own L2) processes a
+//     contiguous range of (head, query-tile) items, keeping a head's K/V in one
+//     L2; causal items run heaviest first.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma_bf16(uint4 a, uint4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint32_t u16_at(const uint4 &v, int e) {
+  const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+// Renumber the linear block id so that XCD x (blocks x, x+8, x+16, ...) gets
+// one contiguous range of logical items; then split the item into
+// (batch, head, query tile), heaviest causal tiles first.
+__device__ __forceinline__ void decode_item(const FwdArgs &a, int &b, int &h, int &qt) {
+  const int total = a.nqt * a.heads * a.batch;
+  const int bid = blockIdx.x;
+  const int per = total / 8, rem = total % 8;
+  const int xcd = bid % 8, idx = bid / 8;
+  const int item = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+  const int bh = item / a.nqt, t = item % a.nqt;
+  qt = a.causal ? a.nqt - 1 - t : t;
+  b = bh / a.heads;
+  h = bh % a.heads;
+}
+
+// Position of key group g (4 keys) inside the transposed V tile: within each
+// group of 16 keys the 32x32 MFMA accumulator lists keys 0-3, 8-11 for lanes
+// 0-31 and 4-7, 12-15 for lanes 32-63, so groups 1 and 2 trade places.
+__device__ __forceinline__ int vt_group_pos(int g) {
+  const int gi = g & 3;
+  const int sw = gi == 1 ? 2 : gi == 2 ? 1 : gi;
+  return (g >> 2) * 16 + sw * 4;
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
+  constexpr int BC = 64;            // keys per tile
+  constexpr int BR = 32 * NW;       // query rows per work-group
+  constexpr int T = NW * 64;        // threads
+  constexpr int KP = D + 8;         // K tile row pitch (bf16), +16 B against bank conflicts
+  constexpr int VP = BC + 8;        // V^T tile row pitch (bf16)
+  constexpr int KS = BC * KP;
+  constexpr int VS = D * VP;
+  constexpr int STAGE = KS + VS;
+  constexpr int DCH = D / 8;                       // 16-byte chunks per row
+  constexpr int KCH = (BC * DCH + T - 1) / T;      // K chunks per thread
+  constexpr int VUNITS = (BC / 4) * DCH;           // (4 keys x 8 dims) units per V tile
+  constexpr int VCH = (VUNITS + T - 1) / T;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ql = lane & 31, hf = lane >> 5;
+
+  int b, h, qt;
+  decode_item(a, b, h, qt);
+  int seq0 = 0, nq = a.nq, nk = a.nk;
+  if (a.cu_seqlens) {
+    seq0 = a.cu_seqlens[b];
+    nq = nk = a.cu_seqlens[b + 1] - seq0;
+  }
+  const int q0 = qt * BR;
+  if (q0 >= nq) return;  // uniform for the whole work-group
+  const int off = nk - nq;
+  const int causal = a.causal, window = a.window;
+
+  const uint16_t *qbase = (const uint16_t *)a.q + b * a.q_sb + (int64_t)seq0 * a.q_st + h * a.q_sh;
+  const uint16_t *kbase = (const uint16_t *)a.k + b * a.k_sb + (int64_t)seq0 * a.k_st + h * a.k_sh;
+  const uint16_t *vbase = (const uint16_t *)a.v + b * a.v_sb + (int64_t)seq0 * a.v_st + h * a.v_sh;
+
+  // key range the whole work-group needs
+  const int p_lo = q0 + off, p_hi = min(q0 + BR, nq) - 1 + off;
+  int kv_lo = 0, kv_hi = nk;
+  if (causal) kv_hi = min(nk, p_hi + 1);
+  if (window > 0) kv_lo = max(0, p_lo - window + 1);
+  const int jt0 = kv_lo / BC;
+  const int jt1 = kv_hi > kv_lo ? (kv_hi + BC - 1) / BC : jt0;
+
+  // this wave's rows
+  const int wq0 = q0 + 32 * wave;
+  const bool wave_rows = wq0 < nq;
+  const int wp_lo = wq0 + off, wp_hi = min(wq0 + 31, nq - 1) + off;
+  const int my_q = wq0 + ql;
+  const int my_p = my_q + off;
+
+  uint4 qreg[D / 16];
+  {
+    const uint4 z = {0u, 0u, 0u, 0u};
+    const uint16_t *qrow = qbase + (int64_t)my_q * a.q_st + hf * 8;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      qreg[kk] = my_q < nq ? *(const uint4 *)(qrow + kk * 16) : z;
+  }
+
+  uint4 kreg[KCH];
+  uint4 vreg[VCH][4];
+  auto load_tile = [&](int k0) {
+    const uint4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + i * T;
+      const int row = c / DCH, col = (c % DCH) * 8;
+      const int key = k0 + row;
+      kreg[i] = (c < BC * DCH && key < nk) ? *(const uint4 *)(kbase + (int64_t)key * a.k_st + col) : z;
+    }
+#pragma unroll
+    for (int u = 0; u < VCH; ++u) {
+      const int unit = tid + u * T;
+      const int g = unit / DCH, dc = unit % DCH;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = k0 + 4 * g + i;
+        vreg[u][i] = (unit < VUNITS && key < nk)
+                         ? *(const uint4 *)(vbase + (int64_t)key * a.v_st + dc * 8) : z;
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    uint16_t *ks = smem + buf * STAGE;
+    uint16_t *vt = ks + KS;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + i * T;
+      if (c < BC * DCH) {
+        const int row = c / DCH, col = (c % DCH) * 8;
+        *(uint4 *)(ks + row * KP + col) = kreg[i];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < VCH; ++u) {
+      const int unit = tid + u * T;
+      if (unit < VUNITS) {
+        const int g = unit / DCH, dc = unit % DCH;
+        const int pos = vt_group_pos(g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          uint2 w;
+          w.x = u16_at(vreg[u][0], e) | (u16_at(vreg[u][1], e) << 16);
+          w.y = u16_at(vreg[u][2], e) | (u16_at(vreg[u][3], e) << 16);
+          *(uint2 *)(vt + (dc * 8 + e) * VP + pos) = w;
+        }
+      }
+    }
+  };
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
+  float m = -INFINITY, l = 0.f;
+  const float c = a.scale_log2;
+
+  if (jt0 < jt1) {
+    load_tile(jt0 * BC);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int jt = jt0; jt < jt1; ++jt) {
+    const int buf = (jt - jt0) & 1;
+    const int k0 = jt * BC;
+    const bool more = jt + 1 < jt1;
+    if (more) load_tile(k0 + BC);
+    const uint16_t *ks = smem + buf * STAGE;
+    const uint16_t *vt = ks + KS;
+
+    const bool active = wave_rows && (!causal || k0 <= wp_hi) &&
+                        (window <= 0 || k0 + BC - 1 > wp_lo - window);
+    if (active) {
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = (f32x16){};
+        const uint16_t *krow = ks + (kb * 32 + ql) * KP + hf * 8;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+          s[kb] = mfma_bf16(*(const uint4 *)(krow + kk * 16), qreg[kk], s[kb]);
+      }
+      const bool need_mask = (causal && k0 + BC - 1 > wp_lo) ||
+                             (window > 0 && k0 <= wp_hi - window) || (k0 + BC > nk);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+            const bool ok = key < nk && (!causal || key <= my_p) &&
+                            (window <= 0 || key > my_p - window);
+            if (!ok) s[kb][r] = -INFINITY;
+          }
+      }
+      float mx = s[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m, mx * c);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m - m_use);
+      m = m_new;
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
+          s[kb][r] = p;
+          rs += p;
+        }
+      l = l * alpha + rs;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+      uint4 pb[4];
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const int kb = cc >> 1, r0 = (cc & 1) * 8;
+        pb[cc].x = pack_bf16x2(s[kb][r0 + 0], s[kb][r0 + 1]);
+        pb[cc].y = pack_bf16x2(s[kb][r0 + 2], s[kb][r0 + 3]);
+        pb[cc].z = pack_bf16x2(s[kb][r0 + 4], s[kb][r0 + 5]);
+        pb[cc].w = pack_bf16x2(s[kb][r0 + 6], s[kb][r0 + 7]);
+      }
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const uint16_t *vrow = vt + (db * 32 + ql) * VP + hf * 8;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+          acc[db] = mfma_bf16(*(const uint4 *)(vrow + cc * 16), pb[cc], acc[db]);
+      }
+    }
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: O = acc / l (bf16, round to nearest even), LSE = (m + log2 l) ln 2
+  const float lt = l + __shfl_xor(l, 32);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (my_q < nq) {
+    uint16_t *orow = (uint16_t *)a.o + b * a.o_sb + (int64_t)(seq0 + my_q) * a.o_st + h * a.o_sh;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        uint2 w;
+        w.x = pack_bf16x2(acc[db][4 * rb + 0] * inv, acc[db][4 * rb + 1] * inv);
+        w.y = pack_bf16x2(acc[db][4 * rb + 2] * inv, acc[db][4 * rb + 3] * inv);
+        *(uint2 *)(orow + db * 32 + 8 * rb + 4 * hf) = w;
+      }
+    if (hf == 0 && a.lse)
+      a.lse[b * a.lse_sb + h * a.lse_sh + seq0 + my_q] =
+          lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+  }
+}
+
+// fp32 forward (small workloads): 4 waves x 16 query rows; a query's dot
+// product is split over 4 lanes (one quarter of the head dim each) and
+// combined with two lane exchanges.  Key tiles of 32 in LDS, the same online
+// softmax as the bf16 kernel, all arithmetic in fp32 FMA.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
+  constexpr int BC = 32, BR = 64, DQ = D / 4, KP = D + 4;
+  __shared__ float ks[BC * KP];
+  __shared__ float vs[BC * KP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qr = lane & 15, quarter = lane >> 4;
+
+  int b, h, qt;
+  decode_item(a, b, h, qt);
+  int seq0 = 0, nq = a.nq, nk = a.nk;
+  if (a.cu_seqlens) {
+    seq0 = a.cu_seqlens[b];
+    nq = nk = a.cu_seqlens[b + 1] - seq0;
+  }
+  const int q0 = qt * BR;
+  if (q0 >= nq) return;
+  const int off = nk - nq;
+  const int causal = a.causal, window = a.window;
+  const float *qbase = (const float *)a.q + b * a.q_sb + (int64_t)seq0 * a.q_st + h * a.q_sh;
+  const float *kbase = (const float *)a.k + b * a.k_sb + (int64_t)seq0 * a.k_st + h * a.k_sh;
+  const float *vbase = (const float *)a.v + b * a.v_sb + (int64_t)seq0 * a.v_st + h * a.v_sh;
+
+  const int p_lo = q0 + off, p_hi = min(q0 + BR, nq) - 1 + off;
+  int kv_lo = 0, kv_hi = nk;
+  if (causal) kv_hi = min(nk, p_hi + 1);
+  if (window > 0) kv_lo = max(0, p_lo - window + 1);
+
+  const int my_q = q0 + wave * 16 + qr;
+  const int my_p = my_q + off;
+  float qv[DQ], acc[DQ];
+#pragma unroll
+  for (int e = 0; e < DQ; ++e) {
+    qv[e] = my_q < nq ? qbase[(int64_t)my_q * a.q_st + quarter * DQ + e] : 0.f;
+    acc[e] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  const float c = a.scale_log2;
+
+  for (int k0 = (kv_lo / BC) * BC; k0 < kv_hi; k0 += BC) {
+    __syncthreads();
+    for (int i = tid; i < BC * D; i += 256) {
+      const int row = i / D, col = i % D, key = k0 + row;
+      ks[row * KP + col] = key < nk ? kbase[(int64_t)key * a.k_st + col] : 0.f;
+      vs[row * KP + col] = key < nk ? vbase[(int64_t)key * a.v_st + col] : 0.f;
+    }
+    __syncthreads();
+    float s[BC];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < BC; ++j) {
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < DQ; ++e) part = __builtin_fmaf(qv[e], ks[j * KP + quarter * DQ + e], part);
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      const int key = k0 + j;
+      const bool ok = key < nk && (!causal || key <= my_p) && (window <= 0 || key > my_p - window);
+      s[j] = ok ? part : -INFINITY;
+      mx = fmaxf(mx, s[j]);
+    }
+    const float m_new = fmaxf(m, mx * c);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2f(m - m_use);
+    m = m_new;
+    float rs = 0.f;
+#pragma unroll
+    for (int j = 0; j < BC; ++j) {
+      s[j] = exp2f(__builtin_fmaf(s[j], c, -m_use));
+      rs += s[j];
+    }
+    l = l * alpha + rs;
+#pragma unroll
+    for (int e = 0; e < DQ; ++e) {
+      float t = acc[e] * alpha;
+#pragma unroll
+      for (int j = 0; j < BC; ++j) t = __builtin_fmaf(s[j], vs[j * KP + quarter * DQ + e], t);
+      acc[e] = t;
+    }
+  }
+  if (my_q < nq) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float *orow = (float *)a.o + b * a.o_sb + (int64_t)(seq0 + my_q) * a.o_st + h * a.o_sh;
+#pragma unroll
+    for (int e = 0; e < DQ; ++e) orow[quarter * DQ + e] = acc[e] * inv;
+    if (quarter == 0 && a.lse)
+      a.lse[b * a.lse_sb + h * a.lse_sh + seq0 + my_q] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
+}  // namespace
+
+int fwd_block_rows(int qkv_dtype, int head_dim) {
+  (void)head_dim;
+  return qkv_dtype == 0 ? 64 : 128;
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs &a, int head_dim, hipStream_t s) {
+  const dim3 grid((unsigned)(a.nqt * a.heads * a.batch));
+  if (head_dim == 128)
+    hipLaunchKernelGGL((fwd_bf16_kernel<128, 4>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<64, 4>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_f32(const FwdArgs &a, int head_dim, hipStream_t s) {
+  const dim3 grid((unsigned)(a.nqt * a.heads * a.batch));
+  if (head_dim == 128)
+    hipLaunchKernelGGL((fwd_f32_kernel<128>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_f32_kernel<64>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -1,0 +1,55 @@
+// Internal declarations shared by the C-ABI layer (fa_api.cpp) and the
+// kernel translation units.  Not part of the public interface (include/fa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Kernel-side view of one forward call.  Dense and packed-varlen calls share
+// it: for varlen, batch = number of sequences, the batch strides are 0 and
+// each work-group reads its sequence's token offset from cu_seqlens.
+struct FwdArgs {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  const int32_t *cu_seqlens;  // null for dense calls
+  int64_t q_sb, q_st, q_sh;   // element strides: batch, token, head
+  int64_t k_sb, k_st, k_sh;
+  int64_t v_sb, v_st, v_sh;
+  int64_t o_sb, o_st, o_sh;
+  int64_t lse_sb, lse_sh;     // lse element strides: batch, head (token stride 1)
+  int32_t batch, heads, nq, nk;  // varlen: nq = nk = max_seqlen (grid sizing only)
+  int32_t nqt;                   // query tiles per (batch, head)
+  int32_t causal, window;
+  float scale_log2;              // softmax_scale * log2(e) (* q, k descales for fp8)
+  float v_descale;               // fp8 only, 1 otherwise
+};
+
+// Kernel-side view of one backward call (dense).
+struct BwdArgs {
+  const void *q, *k, *v, *o, *dout;
+  const float *lse;
+  void *dq, *dk, *dv;
+  float *dpsum;      // workspace: D_i = rowsum(dO * O), [batch, heads, nq] fp32
+  float *dq_accum;   // workspace: fp32 dQ accumulator [batch, heads, nq, d] (atomic mode)
+  int64_t q_sb, q_st, q_sh, k_sb, k_st, k_sh, v_sb, v_st, v_sh, o_sb, o_st, o_sh;
+  int64_t do_sb, do_st, do_sh, dq_sb, dq_st, dq_sh, dk_sb, dk_st, dk_sh, dv_sb, dv_st, dv_sh;
+  int32_t batch, heads, nq, nk;
+  int32_t causal, window, deterministic, grad_f32;
+  float scale, scale_log2;
+};
+
+// Launchers (defined in the kernel translation units).  Each returns the
+// HIP status of its launch(es).
+hipError_t launch_fwd_bf16(const FwdArgs &a, int head_dim, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs &a, int head_dim, hipStream_t s);
+hipError_t launch_fwd_fp8(const FwdArgs &a, int head_dim, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdArgs &a, int head_dim, hipStream_t s);
+size_t bwd_workspace_bytes(int batch, int heads, int nq, int head_dim, int deterministic);
+
+// Query-tile rows per work-group of each forward kernel (grid sizing).
+int fwd_block_rows(int qkv_dtype, int head_dim);
+
+}  // namespace fa

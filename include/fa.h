@@ -1,0 +1,174 @@
+/*
+ * fa.h -- C ABI of the exact-attention library for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes exact scaled-dot-product attention
+ *     O = softmax(softmax_scale * Q K^T + mask) V
+ * by tiling Q, K and V through on-chip memory with an online (running max,
+ * running sum) softmax, so the N x N score matrix never reaches HBM, and the
+ * backward pass that recomputes the scores from the saved log-sum-exp.
+ *
+ * Where each operation is defined:
+ *   - the attention formula: top of "Flash-Attention 2/3在ms-swift中的集成与性能提升"
+ *     (bxzpzcl.cn); section 一 of the adg.csdn.net flash_attn/Qwen page;
+ *     section 2.1 of "FlashAttention优化Transformer显存与计算效率" (jsqmd.com);
+ *   - tiling, blockwise softmax and fusion: jsqmd.com sections 2.2.1-2.2.3;
+ *     section 三 of the adg.csdn.net page;
+ *   - recomputation in the backward: the three techniques listed in the
+ *     ms-swift integration page; section 三 (step 5) of the adg.csdn.net page;
+ *   - causal and sliding-window masks, FP8 operands: the FA-3 paragraph of the
+ *     ms-swift integration page; causal=True in every API example of
+ *     "突破AI算力瓶颈：FlashAttention与MindSpore 2.0全场景融合方案" (核心API与使用示例);
+ *   - packed variable-length sequences: flash_attn_varlen_func and --packing
+ *     in "ms-swift长文本训练优化，Flash-Attention显存省一半" sections 4.3 and 5.1;
+ *   - the [batch, seqlen, nheads, headdim] layout and packed QKV
+ *     (batch, seqlen, 3, nheads, headdim): the MindSpore page, 核心API与使用示例;
+ *   - the precision recipe (bf16 operands, fp32 softmax accumulation, convert
+ *     at output): jsqmd.com section 3.2;
+ *   - error conventions (mixed dtypes -> "same dtype" error, missing GPU build
+ *     -> runtime error): ms-swift long-text page section 4.3.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronises; every call only enqueues kernels
+ *     on `stream` (a hipStream_t; NULL = the default stream) and returns.
+ *   - Strides are in ELEMENTS; the last (head_dim) dimension must be
+ *     contiguous (stride 1) and every row must start 16-byte aligned.
+ *   - head_dim must be 64 or 128.  softmax_scale must be finite and > 0
+ *     (callers pass 1/sqrt(head_dim) for the usual default).
+ *   - causal: key j is visible to query i iff j <= i + (Nk - Nq)
+ *     (bottom-right alignment; for Nq == Nk this is j <= i).
+ *   - window W > 0: additionally j > i + (Nk - Nq) - W, i.e. each query sees
+ *     at most W keys ending at its own position; W = 0 means unlimited.
+ *   - A query row that sees no key gets O = 0 and LSE = -inf.
+ *   - LSE is the natural-log log-sum-exp of the scaled, masked scores, fp32.
+ *   - Errors: a non-FA_OK status is returned and fa_last_error() describes it.
+ *     FA_ERR_INVALID_ARGUMENT and FA_ERR_DTYPE_MISMATCH are detected on the
+ *     host before anything is launched; kernel faults surface at the caller's
+ *     next synchronisation.
+ *   - Calls on different streams may run concurrently; the library keeps no
+ *     state between calls other than the thread-local error message and a
+ *     per-device architecture check.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum {
+  FA_F32 = 0,       /* IEEE binary32 */
+  FA_BF16 = 1,      /* bfloat16 */
+  FA_FP8_E4M3 = 2   /* OCP FP8 E4M3 (max finite 448, no infinities) */
+} fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size/stride/flag/scale */
+  FA_ERR_DTYPE_MISMATCH = 2,   /* q/k/v (and o) dtypes are not an allowed combination */
+  FA_ERR_UNSUPPORTED = 3,      /* head_dim not 64/128, device not gfx950, fp8 backward */
+  FA_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
+} fa_status;
+
+/* Dense forward.
+ *   q [batch, seqlen_q, heads, head_dim]; k, v [batch, seqlen_k, heads, head_dim];
+ *   o [batch, seqlen_q, heads, head_dim]; lse [batch, heads, seqlen_q] fp32,
+ *   contiguous, or NULL when the caller does not need it.
+ *   x_stride = {batch, token, head} element strides of each tensor.
+ *   Allowed dtypes (qkv_dtype, o_dtype): (F32, F32), (BF16, BF16),
+ *   (FP8_E4M3, BF16).  For fp8 the values are code * descale (per tensor);
+ *   for the other dtypes the descales must be 1.
+ *   Packed QKV (batch, seqlen, 3, heads, head_dim) is expressed by pointing
+ *   q, k, v at slices 0, 1, 2 of one buffer with token stride 3*heads*head_dim. */
+typedef struct {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  fa_dtype qkv_dtype, o_dtype;
+  int32_t batch, seqlen_q, seqlen_k, heads, head_dim;
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];
+  float softmax_scale;
+  int32_t causal;  /* 0 or 1 */
+  int32_t window;  /* 0 = unlimited, W > 0 = sliding window of W keys */
+  float q_descale, k_descale, v_descale;
+} fa_fwd_params;
+
+/* Packed variable-length forward (self-attention within each sequence).
+ *   q, k, v, o [total_tokens, heads, head_dim]; x_stride = {token, head}.
+ *   Sequence s occupies tokens cu_seqlens[s] .. cu_seqlens[s+1]-1 and attends
+ *   only to itself (its own positions start at 0 for the masks).
+ *   cu_seqlens: DEVICE int32 [num_seqs + 1], cu_seqlens[0] = 0,
+ *   non-decreasing, cu_seqlens[num_seqs] = total_tokens.  Every length must be
+ *   <= max_seqlen, which sizes the launch grid.  These device-side contracts
+ *   are not checked: violating them reads or writes out of bounds.
+ *   lse [heads, total_tokens] fp32 contiguous, or NULL. */
+typedef struct {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  const int32_t *cu_seqlens;
+  fa_dtype qkv_dtype, o_dtype;
+  int32_t num_seqs, total_tokens, max_seqlen, heads, head_dim;
+  int64_t q_stride[2], k_stride[2], v_stride[2], o_stride[2];
+  float softmax_scale;
+  int32_t causal, window;
+  float q_descale, k_descale, v_descale;
+} fa_varlen_fwd_params;
+
+/* Dense backward (recomputation from the saved LSE).
+ *   q, k, v, o, dout: as in the forward (qkv_dtype BF16: all five bf16);
+ *   lse [batch, heads, seqlen_q] fp32 from the forward of the same inputs.
+ *   dq [batch, seqlen_q, heads, head_dim], dk, dv [batch, seqlen_k, heads,
+ *   head_dim] in grad_dtype (FA_F32, the default of the Python layer, or
+ *   FA_BF16).  deterministic = 1 computes dQ without atomics, so repeated
+ *   calls give bitwise identical gradients; 0 allows a faster atomic dQ
+ *   reduction whose rounding may vary from call to call.
+ *   workspace: device memory of fa_bwd_workspace_bytes(p) bytes, 256-byte
+ *   aligned, owned by the caller; its contents on entry are ignored. */
+typedef struct {
+  const void *q, *k, *v, *o, *dout;
+  const float *lse;
+  void *dq, *dk, *dv;
+  fa_dtype qkv_dtype, grad_dtype;
+  int32_t batch, seqlen_q, seqlen_k, heads, head_dim;
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3], do_stride[3];
+  int64_t dq_stride[3], dk_stride[3], dv_stride[3];
+  float softmax_scale;
+  int32_t causal, window, deterministic;
+} fa_bwd_params;
+
+/* Host-only validation: never touches a device.  Returns the status the
+ * corresponding entry point would return before launching anything. */
+fa_status fa_check_fwd(const fa_fwd_params *p);
+fa_status fa_check_varlen_fwd(const fa_varlen_fwd_params *p);
+fa_status fa_check_bwd(const fa_bwd_params *p);
+
+/* Enqueue the forward: writes o (and lse when non-NULL). */
+fa_status fa_fwd(const fa_fwd_params *p, void *stream);
+
+/* Enqueue the packed variable-length forward. */
+fa_status fa_varlen_fwd(const fa_varlen_fwd_params *p, void *stream);
+
+/* Bytes of device workspace fa_bwd needs for these parameters (0 on invalid
+ * parameters; see fa_last_error). */
+size_t fa_bwd_workspace_bytes(const fa_bwd_params *p);
+
+/* Enqueue the backward: writes dq, dk, dv. */
+fa_status fa_bwd(const fa_bwd_params *p, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Thread-local description of the last non-FA_OK status ("" if none). */
+const char *fa_last_error(void);
+
+/* FA_ABI_VERSION of the loaded library. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

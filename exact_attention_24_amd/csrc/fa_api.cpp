@@ -80,12 +80,21 @@ fa_status check_fwd_common(fa_dtype qkv, fa_dtype o, int32_t heads, int32_t head
 // Row alignment: every row the kernels load with 16-byte accesses must start
 // 16-byte aligned, i.e. pointer and all token/head/batch strides.
 fa_status check_tensor(const char *name, const void *ptr, const int64_t *stride, int nstride,
-                       int elem_bytes, bool empty) {
+                       int elem_bytes, bool empty, int64_t rows = 0, int head_dim = 0) {
   if (empty) return FA_OK;
   if (!ptr) return fail(FA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
   for (int i = 0; i < nstride; ++i)
     if (stride[i] < 0) return fail(FA_ERR_INVALID_ARGUMENT, "%s stride[%d] must be >= 0 (got %lld)",
                                    name, i, (long long)stride[i]);
+  // rows are addressed with 32-bit byte offsets from the start of each
+  // (batch, head) slice, and rows past the end read as zeros only if rows do
+  // not overlap: token stride >= head_dim whenever there is more than one row
+  const int64_t tok = stride[nstride == 3 ? 1 : 0];
+  if (rows > 1 && tok < head_dim)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s token stride (%lld) must be >= head_dim (%d)", name,
+                (long long)tok, head_dim);
+  if ((rows + 256) * tok * elem_bytes >= (int64_t)1 << 31)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: one (batch, head) slice spans more than 2 GiB", name);
   if (elem_bytes < 4) {
     const int64_t a = 16 / elem_bytes;
     if (reinterpret_cast<uintptr_t>(ptr) % 16)
@@ -147,10 +156,11 @@ fa_status fa_check_fwd(const fa_fwd_params *p) {
   const bool q_empty = (int64_t)p->batch * p->seqlen_q * p->heads == 0;
   const bool k_empty = (int64_t)p->batch * p->seqlen_k * p->heads == 0;
   const int eb = dtype_bytes(p->qkv_dtype), ob = dtype_bytes(p->o_dtype);
-  if ((st = check_tensor("q", p->q, p->q_stride, 3, eb, q_empty)) != FA_OK) return st;
-  if ((st = check_tensor("k", p->k, p->k_stride, 3, eb, k_empty)) != FA_OK) return st;
-  if ((st = check_tensor("v", p->v, p->v_stride, 3, eb, k_empty)) != FA_OK) return st;
-  if ((st = check_tensor("o", p->o, p->o_stride, 3, ob, q_empty)) != FA_OK) return st;
+  const int hd = p->head_dim;
+  if ((st = check_tensor("q", p->q, p->q_stride, 3, eb, q_empty, p->seqlen_q, hd)) != FA_OK) return st;
+  if ((st = check_tensor("k", p->k, p->k_stride, 3, eb, k_empty, p->seqlen_k, hd)) != FA_OK) return st;
+  if ((st = check_tensor("v", p->v, p->v_stride, 3, eb, k_empty, p->seqlen_k, hd)) != FA_OK) return st;
+  if ((st = check_tensor("o", p->o, p->o_stride, 3, ob, q_empty, p->seqlen_q, hd)) != FA_OK) return st;
   const int64_t items = ceil_div(p->seqlen_q, fa::fwd_block_rows(p->qkv_dtype, p->head_dim)) *
                         (int64_t)p->heads * p->batch;
   if (items > INT32_MAX) return fail(FA_ERR_INVALID_ARGUMENT, "problem too large for one launch");
@@ -171,10 +181,11 @@ fa_status fa_check_varlen_fwd(const fa_varlen_fwd_params *p) {
   const bool empty = (int64_t)p->total_tokens * p->heads == 0 || p->num_seqs == 0;
   if (!empty && !p->cu_seqlens) return fail(FA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
   const int eb = dtype_bytes(p->qkv_dtype), ob = dtype_bytes(p->o_dtype);
-  if ((st = check_tensor("q", p->q, p->q_stride, 2, eb, empty)) != FA_OK) return st;
-  if ((st = check_tensor("k", p->k, p->k_stride, 2, eb, empty)) != FA_OK) return st;
-  if ((st = check_tensor("v", p->v, p->v_stride, 2, eb, empty)) != FA_OK) return st;
-  if ((st = check_tensor("o", p->o, p->o_stride, 2, ob, empty)) != FA_OK) return st;
+  const int hd = p->head_dim, tt = p->total_tokens;
+  if ((st = check_tensor("q", p->q, p->q_stride, 2, eb, empty, tt, hd)) != FA_OK) return st;
+  if ((st = check_tensor("k", p->k, p->k_stride, 2, eb, empty, tt, hd)) != FA_OK) return st;
+  if ((st = check_tensor("v", p->v, p->v_stride, 2, eb, empty, tt, hd)) != FA_OK) return st;
+  if ((st = check_tensor("o", p->o, p->o_stride, 2, ob, empty, tt, hd)) != FA_OK) return st;
   const int64_t items = ceil_div(p->max_seqlen, fa::fwd_block_rows(p->qkv_dtype, p->head_dim)) *
                         (int64_t)p->heads * p->num_seqs;
   if (items > INT32_MAX) return fail(FA_ERR_INVALID_ARGUMENT, "problem too large for one launch");
@@ -209,14 +220,15 @@ fa_status fa_check_bwd(const fa_bwd_params *p) {
   const bool k_empty = (int64_t)p->batch * p->seqlen_k * p->heads == 0;
   const int gb = dtype_bytes(p->grad_dtype);
   fa_status st;
-  if ((st = check_tensor("q", p->q, p->q_stride, 3, 2, q_empty)) != FA_OK) return st;
-  if ((st = check_tensor("k", p->k, p->k_stride, 3, 2, k_empty)) != FA_OK) return st;
-  if ((st = check_tensor("v", p->v, p->v_stride, 3, 2, k_empty)) != FA_OK) return st;
-  if ((st = check_tensor("o", p->o, p->o_stride, 3, 2, q_empty)) != FA_OK) return st;
-  if ((st = check_tensor("dout", p->dout, p->do_stride, 3, 2, q_empty)) != FA_OK) return st;
-  if ((st = check_tensor("dq", p->dq, p->dq_stride, 3, gb, q_empty)) != FA_OK) return st;
-  if ((st = check_tensor("dk", p->dk, p->dk_stride, 3, gb, k_empty)) != FA_OK) return st;
-  if ((st = check_tensor("dv", p->dv, p->dv_stride, 3, gb, k_empty)) != FA_OK) return st;
+  const int hd = p->head_dim, nq = p->seqlen_q, nk = p->seqlen_k;
+  if ((st = check_tensor("q", p->q, p->q_stride, 3, 2, q_empty, nq, hd)) != FA_OK) return st;
+  if ((st = check_tensor("k", p->k, p->k_stride, 3, 2, k_empty, nk, hd)) != FA_OK) return st;
+  if ((st = check_tensor("v", p->v, p->v_stride, 3, 2, k_empty, nk, hd)) != FA_OK) return st;
+  if ((st = check_tensor("o", p->o, p->o_stride, 3, 2, q_empty, nq, hd)) != FA_OK) return st;
+  if ((st = check_tensor("dout", p->dout, p->do_stride, 3, 2, q_empty, nq, hd)) != FA_OK) return st;
+  if ((st = check_tensor("dq", p->dq, p->dq_stride, 3, gb, q_empty, nq, hd)) != FA_OK) return st;
+  if ((st = check_tensor("dk", p->dk, p->dk_stride, 3, gb, k_empty, nk, hd)) != FA_OK) return st;
+  if ((st = check_tensor("dv", p->dv, p->dv_stride, 3, gb, k_empty, nk, hd)) != FA_OK) return st;
   if (!q_empty && !p->lse) return fail(FA_ERR_INVALID_ARGUMENT, "lse is NULL");
   return ok();
 }

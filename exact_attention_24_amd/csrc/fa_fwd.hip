@@ -33,6 +33,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "fa_internal.h"
 
@@ -51,6 +52,22 @@ __device__ __forceinline__ f32x16 mfma_bf16(uint4 a, uint4 b, f32x16 c) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Raw buffer resource over one (batch, head) slice.  Loads whose byte offset
+// lies at or beyond `bytes` return zeros, which is how rows past the end of a
+// sequence are zero-filled without any predication.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Bytes spanned by rows 0..n-1 of width w elements at row stride st.
+__device__ __forceinline__ uint32_t slice_bytes(int n, int64_t st, int w, int elem) {
+  return n > 0 ? (uint32_t)(((int64_t)(n - 1) * st + w) * elem) : 0u;
+}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -87,20 +104,77 @@ __device__ __forceinline__ int vt_group_pos(int g) {
   return (g >> 2) * 16 + sw * 4;
 }
 
+// K/V tile staging for the bf16 kernel: global -> VGPR (buffer loads, rows
+// past the slice come back as zeros) and VGPR -> LDS (K row-major, V
+// transposed with the accumulator's key order).
+template <int D, int T>
+struct KvStage {
+  static constexpr int BC = 64;
+  static constexpr int DCH = D / 8;                  // 16-byte chunks per row
+  static constexpr int KCH = (BC * DCH + T - 1) / T; // K chunks per thread
+  static constexpr int VUNITS = (BC / 4) * DCH;      // (4 keys x 8 dims) units per V tile
+  static constexpr int VCH = (VUNITS + T - 1) / T;
+  static constexpr int KP = D + 8;                   // K tile row pitch (bf16), +16 B vs bank conflicts
+  static constexpr int VP = BC + 8;                  // V^T tile row pitch (bf16)
+  static constexpr int KS = BC * KP;
+  static constexpr int VS = D * VP;
+  static constexpr int STAGE = KS + VS;
+
+  uint4 kreg[KCH];
+  uint4 vreg[VCH][4];
+
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, int k0,
+                                       int tid, uint32_t kst2, uint32_t vst2) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + i * T;
+      const int row = c / DCH, col = (c % DCH) * 8;
+      kreg[i] = bload16(krs, (uint32_t)(k0 + row) * kst2 + col * 2);
+    }
+#pragma unroll
+    for (int u = 0; u < VCH; ++u) {
+      const int unit = tid + u * T;
+      const int g = unit / DCH, dc = unit % DCH;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vreg[u][i] = bload16(vrs, (uint32_t)(k0 + 4 * g + i) * vst2 + dc * 16);
+    }
+  }
+
+  __device__ __forceinline__ void store(uint16_t *ks, int tid) const {
+    uint16_t *vt = ks + KS;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + i * T;
+      if (KCH * T == BC * DCH || c < BC * DCH) {
+        const int row = c / DCH, col = (c % DCH) * 8;
+        *(uint4 *)(ks + row * KP + col) = kreg[i];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < VCH; ++u) {
+      const int unit = tid + u * T;
+      if (VCH * T == VUNITS || unit < VUNITS) {
+        const int g = unit / DCH, dc = unit % DCH;
+        const int pos = vt_group_pos(g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          uint2 w;
+          w.x = u16_at(vreg[u][0], e) | (u16_at(vreg[u][1], e) << 16);
+          w.y = u16_at(vreg[u][2], e) | (u16_at(vreg[u][3], e) << 16);
+          *(uint2 *)(vt + (dc * 8 + e) * VP + pos) = w;
+        }
+      }
+    }
+  }
+};
+
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
-  constexpr int BC = 64;            // keys per tile
+  using St = KvStage<D, NW * 64>;
+  constexpr int BC = St::BC;        // keys per tile
   constexpr int BR = 32 * NW;       // query rows per work-group
   constexpr int T = NW * 64;        // threads
-  constexpr int KP = D + 8;         // K tile row pitch (bf16), +16 B against bank conflicts
-  constexpr int VP = BC + 8;        // V^T tile row pitch (bf16)
-  constexpr int KS = BC * KP;
-  constexpr int VS = D * VP;
-  constexpr int STAGE = KS + VS;
-  constexpr int DCH = D / 8;                       // 16-byte chunks per row
-  constexpr int KCH = (BC * DCH + T - 1) / T;      // K chunks per thread
-  constexpr int VUNITS = (BC / 4) * DCH;           // (4 keys x 8 dims) units per V tile
-  constexpr int VCH = (VUNITS + T - 1) / T;
+  constexpr int KP = St::KP, VP = St::VP, KS = St::KS, STAGE = St::STAGE;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -121,6 +195,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
   const uint16_t *qbase = (const uint16_t *)a.q + b * a.q_sb + (int64_t)seq0 * a.q_st + h * a.q_sh;
   const uint16_t *kbase = (const uint16_t *)a.k + b * a.k_sb + (int64_t)seq0 * a.k_st + h * a.k_sh;
   const uint16_t *vbase = (const uint16_t *)a.v + b * a.v_sb + (int64_t)seq0 * a.v_st + h * a.v_sh;
+  const __amdgpu_buffer_rsrc_t qrs = slice_rsrc(qbase, slice_bytes(nq, a.q_st, D, 2));
+  const __amdgpu_buffer_rsrc_t krs = slice_rsrc(kbase, slice_bytes(nk, a.k_st, D, 2));
+  const __amdgpu_buffer_rsrc_t vrs = slice_rsrc(vbase, slice_bytes(nk, a.v_st, D, 2));
+  const uint32_t kst2 = (uint32_t)a.k_st * 2, vst2 = (uint32_t)a.v_st * 2;
 
   // key range the whole work-group needs
   const int p_lo = q0 + off, p_hi = min(q0 + BR, nq) - 1 + off;
@@ -139,64 +217,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
 
   uint4 qreg[D / 16];
   {
-    const uint4 z = {0u, 0u, 0u, 0u};
-    const uint16_t *qrow = qbase + (int64_t)my_q * a.q_st + hf * 8;
+    const uint32_t qoff = (uint32_t)my_q * (uint32_t)a.q_st * 2 + hf * 16;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-      qreg[kk] = my_q < nq ? *(const uint4 *)(qrow + kk * 16) : z;
+    for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = bload16(qrs, qoff + kk * 32);
   }
 
-  uint4 kreg[KCH];
-  uint4 vreg[VCH][4];
-  auto load_tile = [&](int k0) {
-    const uint4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * T;
-      const int row = c / DCH, col = (c % DCH) * 8;
-      const int key = k0 + row;
-      kreg[i] = (c < BC * DCH && key < nk) ? *(const uint4 *)(kbase + (int64_t)key * a.k_st + col) : z;
-    }
-#pragma unroll
-    for (int u = 0; u < VCH; ++u) {
-      const int unit = tid + u * T;
-      const int g = unit / DCH, dc = unit % DCH;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = k0 + 4 * g + i;
-        vreg[u][i] = (unit < VUNITS && key < nk)
-                         ? *(const uint4 *)(vbase + (int64_t)key * a.v_st + dc * 8) : z;
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint16_t *ks = smem + buf * STAGE;
-    uint16_t *vt = ks + KS;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * T;
-      if (c < BC * DCH) {
-        const int row = c / DCH, col = (c % DCH) * 8;
-        *(uint4 *)(ks + row * KP + col) = kreg[i];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < VCH; ++u) {
-      const int unit = tid + u * T;
-      if (unit < VUNITS) {
-        const int g = unit / DCH, dc = unit % DCH;
-        const int pos = vt_group_pos(g);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          uint2 w;
-          w.x = u16_at(vreg[u][0], e) | (u16_at(vreg[u][1], e) << 16);
-          w.y = u16_at(vreg[u][2], e) | (u16_at(vreg[u][3], e) << 16);
-          *(uint2 *)(vt + (dc * 8 + e) * VP + pos) = w;
-        }
-      }
-    }
-  };
-
+  St st;
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
@@ -204,8 +230,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
   const float c = a.scale_log2;
 
   if (jt0 < jt1) {
-    load_tile(jt0 * BC);
-    store_tile(0);
+    st.load(krs, vrs, jt0 * BC, tid, kst2, vst2);
+    st.store(smem, tid);
   }
   __syncthreads();
 
@@ -213,7 +239,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
     const int buf = (jt - jt0) & 1;
     const int k0 = jt * BC;
     const bool more = jt + 1 < jt1;
-    if (more) load_tile(k0 + BC);
+    if (more) st.load(krs, vrs, k0 + BC, tid, kst2, vst2);
     const uint16_t *ks = smem + buf * STAGE;
     const uint16_t *vt = ks + KS;
 
@@ -262,8 +288,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
           rs += p;
         }
       l = l * alpha + rs;
+      // the running max of most rows stops changing after a few tiles: skip
+      // the accumulator rescale when it is 1 for every row of the wave
+      if (__ballot(alpha != 1.f)) {
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+        for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+      }
       uint4 pb[4];
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
@@ -281,7 +311,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
           acc[db] = mfma_bf16(*(const uint4 *)(vrow + cc * 16), pb[cc], acc[db]);
       }
     }
-    if (more) store_tile(buf ^ 1);
+    if (more) st.store(smem + (buf ^ 1) * STAGE, tid);
     __syncthreads();
   }
 
@@ -401,17 +431,36 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
 
 }  // namespace
 
+// Waves per work-group of the bf16 forward (32 query rows each).  8 by
+// default; FA_FWD_WAVES=4 selects the 4-wave variant (for tuning runs).
+static int bf16_waves() {
+  static const int w = [] {
+    const char *e = getenv("FA_FWD_WAVES");
+    return (e && atoi(e) == 4) ? 4 : 8;
+  }();
+  return w;
+}
+
 int fwd_block_rows(int qkv_dtype, int head_dim) {
   (void)head_dim;
-  return qkv_dtype == 0 ? 64 : 128;
+  if (qkv_dtype == 0) return 64;
+  return 32 * bf16_waves();
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, int head_dim, hipStream_t s) {
   const dim3 grid((unsigned)(a.nqt * a.heads * a.batch));
-  if (head_dim == 128)
-    hipLaunchKernelGGL((fwd_bf16_kernel<128, 4>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((fwd_bf16_kernel<64, 4>), grid, dim3(256), 0, s, a);
+  const int nw = bf16_waves();
+  if (head_dim == 128) {
+    if (nw == 8)
+      hipLaunchKernelGGL((fwd_bf16_kernel<128, 8>), grid, dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<128, 4>), grid, dim3(256), 0, s, a);
+  } else {
+    if (nw == 8)
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, 8>), grid, dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, 4>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -95,15 +95,13 @@ fa_status check_tensor(const char *name, const void *ptr, const int64_t *stride,
                 (long long)tok, head_dim);
   if ((rows + 256) * tok * elem_bytes >= (int64_t)1 << 31)
     return fail(FA_ERR_INVALID_ARGUMENT, "%s: one (batch, head) slice spans more than 2 GiB", name);
-  if (elem_bytes < 4) {
-    const int64_t a = 16 / elem_bytes;
-    if (reinterpret_cast<uintptr_t>(ptr) % 16)
-      return fail(FA_ERR_INVALID_ARGUMENT, "%s must be 16-byte aligned", name);
-    for (int i = 0; i < nstride; ++i)
-      if (stride[i] % a)
-        return fail(FA_ERR_INVALID_ARGUMENT, "%s stride[%d] must be a multiple of %lld elements (got %lld)",
-                    name, i, (long long)a, (long long)stride[i]);
-  }
+  const int64_t a = 16 / elem_bytes;
+  if (reinterpret_cast<uintptr_t>(ptr) % 16)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s must be 16-byte aligned", name);
+  for (int i = 0; i < nstride; ++i)
+    if (stride[i] % a)
+      return fail(FA_ERR_INVALID_ARGUMENT, "%s stride[%d] must be a multiple of %lld elements (got %lld)",
+                  name, i, (long long)a, (long long)stride[i]);
   return FA_OK;
 }
 

@@ -35,73 +35,22 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+using namespace dev;
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-__device__ __forceinline__ f32x16 mfma_bf16(uint4 a, uint4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Raw buffer resource over one (batch, head) slice.  Loads whose byte offset
-// lies at or beyond `bytes` return zeros, which is how rows past the end of a
-// sequence are zero-filled without any predication.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
-// Bytes spanned by rows 0..n-1 of width w elements at row stride st.
-__device__ __forceinline__ uint32_t slice_bytes(int n, int64_t st, int w, int elem) {
-  return n > 0 ? (uint32_t)(((int64_t)(n - 1) * st + w) * elem) : 0u;
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  bf16x2 v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ uint32_t u16_at(const uint4 &v, int e) {
-  const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
-  return (e & 1) ? (w >> 16) : (w & 0xffffu);
-}
-
-// Renumber the linear block id so that XCD x (blocks x, x+8, x+16, ...) gets
-// one contiguous range of logical items; then split the item into
-// (batch, head, query tile), heaviest causal tiles first.
+// Split the (XCD-renumbered) block id into (batch, head, query tile),
+// heaviest causal tiles first.
 __device__ __forceinline__ void decode_item(const FwdArgs &a, int &b, int &h, int &qt) {
-  const int total = a.nqt * a.heads * a.batch;
-  const int bid = blockIdx.x;
-  const int per = total / 8, rem = total % 8;
-  const int xcd = bid % 8, idx = bid / 8;
-  const int item = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+  const int item = xcd_item(blockIdx.x, a.nqt * a.heads * a.batch);
   const int bh = item / a.nqt, t = item % a.nqt;
   qt = a.causal ? a.nqt - 1 - t : t;
   b = bh / a.heads;
   h = bh % a.heads;
-}
-
-// Position of key group g (4 keys) inside the transposed V tile: within each
-// group of 16 keys the 32x32 MFMA accumulator lists keys 0-3, 8-11 for lanes
-// 0-31 and 4-7, 12-15 for lanes 32-63, so groups 1 and 2 trade places.
-__device__ __forceinline__ int vt_group_pos(int g) {
-  const int gi = g & 3;
-  const int sw = gi == 1 ? 2 : gi == 2 ? 1 : gi;
-  return (g >> 2) * 16 + sw * 4;
 }
 
 // K/V tile staging for the bf16 kernel: global -> VGPR (buffer loads, rows
@@ -155,14 +104,7 @@ struct KvStage {
       const int unit = tid + u * T;
       if (VCH * T == VUNITS || unit < VUNITS) {
         const int g = unit / DCH, dc = unit % DCH;
-        const int pos = vt_group_pos(g);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          uint2 w;
-          w.x = u16_at(vreg[u][0], e) | (u16_at(vreg[u][1], e) << 16);
-          w.y = u16_at(vreg[u][2], e) | (u16_at(vreg[u][3], e) << 16);
-          *(uint2 *)(vt + (dc * 8 + e) * VP + pos) = w;
-        }
+        store_transposed_4x8(vt, VP, dc * 8, vt_group_pos(g), vreg[u]);
       }
     }
   }

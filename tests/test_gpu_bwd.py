@@ -1,0 +1,96 @@
+"""GPU parity of the recomputing backward against the fp64 oracle (through the C ABI)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_24_amd import fa_bwd, fa_fwd
+from exact_attention_24_amd.inputs import WORKLOADS, dense_inputs, workload_inputs
+from tests.parity import BF16_MAX_ABS, assert_close, f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _fwd_bwd(q, k, v, do, causal, window, grad_dtype=torch.float32, deterministic=True):
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    o, lse = fa_fwd(qd, kd, vd, causal=causal, window=window)
+    dq, dk, dv = fa_bwd(dod, qd, kd, vd, o, lse, causal=causal, window=window, grad_dtype=grad_dtype,
+                        deterministic=deterministic)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+SMALL = [
+    # (batch, nq, nk, heads, d, causal, window)
+    (1, 1, 1, 1, 64, False, 0),
+    (1, 37, 37, 2, 64, True, 0),
+    (2, 300, 300, 2, 128, True, 0),
+    (1, 300, 300, 2, 128, False, 0),
+    (1, 257, 257, 3, 64, False, 0),
+    (1, 520, 520, 2, 128, True, 130),
+    (1, 200, 200, 2, 64, False, 50),
+    (1, 150, 400, 2, 128, True, 0),   # Nq < Nk, bottom-right causal
+    (1, 400, 150, 2, 128, True, 0),   # Nq > Nk: early rows see no key
+]
+
+
+@pytest.mark.parametrize("b,nq,nk,h,d,causal,window", SMALL)
+def test_bwd_small_elementwise(b, nq, nk, h, d, causal, window):
+    print(f"[bwd] b={b} nq={nq} nk={nk} h={h} d={d} causal={causal} window={window}", flush=True)
+    q, _, _, do = dense_inputs(b, nq, h, d, "bf16", seed=nq * 13 + nk, with_dout=True)
+    _, k, v = dense_inputs(b, nk, h, d, "bf16", seed=nq * 13 + nk + 1)
+    dq, dk, dv = _fwd_bwd(q, k, v, do, causal, window)
+    rq, rk, rv = oracle.mha_bwd(f64(q), f64(k), f64(v), f64(do), 1 / np.sqrt(d), causal, window)
+    assert_close(f64(dq), rq, what="dQ")
+    assert_close(f64(dk), rk, what="dK")
+    assert_close(f64(dv), rv, what="dV")
+
+
+def test_bwd_n8192_full_size():
+    """B1 H32 N8192 d128 bf16 causal: two whole heads element by element, and
+    on every head the identities sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i."""
+    w = WORKLOADS["bwd_n8192"]
+    t = workload_inputs("bwd_n8192")
+    print("[bwd n8192] launching", flush=True)
+    dq, dk, dv = _fwd_bwd(t["q"], t["k"], t["v"], t["dout"], w.causal, w.window)
+    q, k, v, do = (f64(t[x]) for x in ("q", "k", "v", "dout"))
+    dq64, dk64, dv64 = f64(dq), f64(dk), f64(dv)
+    for h in (0, w.heads - 1):
+        rq, rk, rv = oracle.attention_bwd(q[0, :, h], k[0, :, h], v[0, :, h], do[0, :, h], w.scale, True, 0)
+        assert_close(dq64[0, :, h], rq, what=f"dQ head {h}")
+        assert_close(dk64[0, :, h], rk, what=f"dK head {h}")
+        assert_close(dv64[0, :, h], rv, what=f"dV head {h}")
+    # properties at full size on every head
+    assert np.abs(dk64.sum(axis=1)).max() < 0.05
+    assert np.abs(dv64.sum(axis=1) - do.sum(axis=1)).max() < 0.05
+
+
+def test_bwd_deterministic_bitwise():
+    q, k, v, do = dense_inputs(1, 700, 4, 128, "bf16", seed=21, with_dout=True)
+    g1 = _fwd_bwd(q, k, v, do, True, 0)
+    g2 = _fwd_bwd(q, k, v, do, True, 0)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_bwd_bf16_gradients():
+    q, k, v, do = dense_inputs(1, 333, 2, 128, "bf16", seed=22, with_dout=True)
+    dq, dk, dv = _fwd_bwd(q, k, v, do, True, 0, grad_dtype=torch.bfloat16)
+    rq, rk, rv = oracle.mha_bwd(f64(q), f64(k), f64(v), f64(do), 1 / np.sqrt(128), True, 0)
+    for g, r, n in ((dq, rq, "dQ"), (dk, rk, "dK"), (dv, rv, "dV")):
+        assert g.dtype == torch.bfloat16
+        # bf16 output rounding (half an ulp of |r|) on top of the fp32 tolerance
+        err = np.abs(f64(g) - r)
+        bound = BF16_MAX_ABS + np.abs(r) * 2.0 ** -8
+        assert (err <= bound).all(), f"{n}: max excess {(err - bound).max():.3e}"
+
+
+def test_bwd_empty_and_no_keys():
+    q = torch.randn(1, 9, 2, 64, device=DEV).to(torch.bfloat16)
+    kv = torch.empty(1, 0, 2, 64, dtype=torch.bfloat16, device=DEV)
+    o, lse = fa_fwd(q, kv, kv)
+    dq, dk, dv = fa_bwd(torch.ones_like(q), q, kv, kv, o, lse)
+    torch.cuda.synchronize()
+    assert (dq == 0).all() and dk.numel() == 0

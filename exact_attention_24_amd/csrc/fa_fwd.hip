@@ -385,7 +385,8 @@ static int bf16_waves() {
 
 int fwd_block_rows(int qkv_dtype, int head_dim) {
   (void)head_dim;
-  if (qkv_dtype == 0) return 64;
+  if (qkv_dtype == 0) return 64;   // fp32 kernel
+  if (qkv_dtype == 2) return 256;  // fp8 kernel: 8 waves
   return 32 * bf16_waves();
 }
 

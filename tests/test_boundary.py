@@ -1,0 +1,165 @@
+"""The C-ABI boundary on the CPU: libfa.so loads, exports every function
+include/fa.h declares, and its host-side validation (which never touches a
+device) returns the documented status for each class of bad argument."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from exact_attention_24_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):  # build only when nothing is built
+        from exact_attention_24_amd import build
+        build.build()
+    return B.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("fa_fwd", "fa_varlen_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_check_fwd",
+              "fa_check_varlen_fwd", "fa_check_bwd", "fa_last_error", "fa_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (fa_\w+)", out))
+    for n in declared_functions():
+        assert n in exported, f"{n} declared in fa.h but not exported"
+        getattr(lib, n)  # resolvable through the dynamic loader
+    assert lib.fa_abi_version() == B.ABI_VERSION
+
+
+def test_struct_sizes_match_c_layout():
+    # offsets follow the C rules for these field lists (pointers 8, enums/int32 4, int64 8)
+    assert ctypes.sizeof(B.FwdParams) == 5 * 8 + 7 * 4 + 4 + 12 * 8 + 6 * 4
+    assert B.FwdParams.q_stride.offset == 5 * 8 + 7 * 4 + 4
+
+
+def _fwd_params(dtype=torch.bfloat16, b=1, n=16, h=2, d=64, causal=True, window=0):
+    q = torch.zeros(b, n, h, d, dtype=dtype)
+    o = torch.zeros(b, n, h, d, dtype=torch.bfloat16 if dtype == torch.float8_e4m3fn else dtype)
+    lse = torch.zeros(b, h, n, dtype=torch.float32)
+    return B.make_fwd_params(q, q, q, o, lse, causal=causal, window=window), (q, o, lse)
+
+
+def _status(lib, p):
+    st = lib.fa_check_fwd(ctypes.byref(p))
+    return st, lib.fa_last_error().decode()
+
+
+def test_valid_params_pass(lib):
+    for dt in (torch.float32, torch.bfloat16, torch.float8_e4m3fn):
+        p, keep = _fwd_params(dt)
+        if dt == torch.float8_e4m3fn:
+            p.q_descale = p.k_descale = p.v_descale = 0.5
+        assert _status(lib, p) == (B.FA_OK, "")
+
+
+@pytest.mark.parametrize("field,value,code,msg", [
+    ("window", -3, B.FA_ERR_INVALID_ARGUMENT, "window must be >= 0 (got -3)"),
+    ("causal", 2, B.FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got 2)"),
+    ("head_dim", 96, B.FA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got 96)"),
+    ("softmax_scale", 0.0, B.FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0"),
+    ("softmax_scale", float("nan"), B.FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0"),
+    ("seqlen_q", -1, B.FA_ERR_INVALID_ARGUMENT, "sizes must be >= 0"),
+    ("q_descale", 2.0, B.FA_ERR_INVALID_ARGUMENT, "descales must be 1 for non-fp8 inputs"),
+    ("o_dtype", B.FA_F32, B.FA_ERR_DTYPE_MISMATCH, "Input and output tensors must have the same dtype"),
+    ("qkv_dtype", 7, B.FA_ERR_INVALID_ARGUMENT, "unknown dtype code"),
+    ("k", None, B.FA_ERR_INVALID_ARGUMENT, "k is NULL"),
+])
+def test_fwd_rejects(lib, field, value, code, msg):
+    p, keep = _fwd_params()
+    setattr(p, field, value)
+    st, err = _status(lib, p)
+    assert st == code and msg in err, (st, err)
+
+
+def test_fwd_rejects_bad_strides(lib):
+    p, keep = _fwd_params()
+    p.k_stride[1] = 100  # not a multiple of 8 bf16 elements: rows not 16-byte aligned
+    st, err = _status(lib, p)
+    assert st == B.FA_ERR_INVALID_ARGUMENT and "multiple of 8" in err
+    p, keep = _fwd_params()
+    p.v_stride[1] = 8  # token stride below head_dim: rows overlap
+    st, err = _status(lib, p)
+    assert st == B.FA_ERR_INVALID_ARGUMENT and "token stride" in err
+
+
+def test_fp8_rules(lib):
+    p, keep = _fwd_params(torch.float8_e4m3fn)
+    st, err = _status(lib, p)  # descales left at 1.0 are valid for fp8
+    assert st == B.FA_OK
+    p.v_descale = -1.0
+    assert _status(lib, p)[0] == B.FA_ERR_INVALID_ARGUMENT
+    p, keep = _fwd_params(torch.float8_e4m3fn)
+    p.o_dtype = B.FA_FP8_E4M3  # fp8 in -> bf16 out only
+    assert _status(lib, p)[0] == B.FA_ERR_DTYPE_MISMATCH
+
+
+def test_empty_problem_is_valid(lib):
+    q = torch.empty(0, 16, 2, 64, dtype=torch.bfloat16)
+    p = B.make_fwd_params(q, q, q, q, None)
+    assert _status(lib, p) == (B.FA_OK, "")
+
+
+def test_varlen_checks(lib):
+    q = torch.zeros(40, 2, 128, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 10, 40], dtype=torch.int32)
+    p = B.make_varlen_params(q, q, q, q, None, cu, 30)
+    assert lib.fa_check_varlen_fwd(ctypes.byref(p)) == B.FA_OK
+    p.max_seqlen = 41
+    assert lib.fa_check_varlen_fwd(ctypes.byref(p)) == B.FA_ERR_INVALID_ARGUMENT
+    assert b"exceeds total_tokens" in lib.fa_last_error()
+    p = B.make_varlen_params(q, q, q, q, None, cu, 30)
+    p.cu_seqlens = None
+    assert lib.fa_check_varlen_fwd(ctypes.byref(p)) == B.FA_ERR_INVALID_ARGUMENT
+
+
+def test_bwd_checks(lib):
+    q = torch.zeros(1, 16, 2, 128, dtype=torch.bfloat16)
+    g = torch.zeros(1, 16, 2, 128, dtype=torch.float32)
+    lse = torch.zeros(1, 2, 16, dtype=torch.float32)
+    p = B.make_bwd_params(q, q, q, q, q, lse, g, g, g, causal=True)
+    assert lib.fa_check_bwd(ctypes.byref(p)) == B.FA_OK
+    assert lib.fa_bwd_workspace_bytes(ctypes.byref(p)) == 256  # D: 1*2*16 fp32, rounded to 256 bytes
+    p.qkv_dtype = B.FA_FP8_E4M3
+    assert lib.fa_check_bwd(ctypes.byref(p)) == B.FA_ERR_UNSUPPORTED
+    p = B.make_bwd_params(q, q, q, q, q, lse, g, g, g)
+    p.lse = None
+    assert lib.fa_check_bwd(ctypes.byref(p)) == B.FA_ERR_INVALID_ARGUMENT
+    p = B.make_bwd_params(q, q, q, q, q, lse, g, g, g)
+    p.deterministic = 5
+    assert lib.fa_check_bwd(ctypes.byref(p)) == B.FA_ERR_INVALID_ARGUMENT
+
+
+def test_python_layer_error_mapping(lib):
+    q = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="same dtype"):
+        B.fa_fwd(q, q.float(), q)
+    with pytest.raises(ValueError, match="head_dim|shape"):
+        B.fa_fwd(q, q[..., :32], q)
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU behaviour")
+def test_launch_without_gpu_fails_loudly(lib):
+    q = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    p = B.make_fwd_params(q, q, q, q, None)
+    st = lib.fa_fwd(ctypes.byref(p), None)
+    assert st == B.FA_ERR_HIP
+    assert lib.fa_last_error()

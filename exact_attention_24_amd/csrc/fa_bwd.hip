@@ -96,7 +96,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int STAGE_BYTES = STAGE_H * 2 + 2 * BR * 4;  // + lse2[BR], dsum[BR] (fp32)
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE_BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int ql = lane & 31, hf = lane >> 5;
   const int nq = a.nq, nk = a.nk, off = nk - nq;
   const int causal = a.causal, window = a.window;
@@ -317,7 +318,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr int VCH = (BC * DCH + T - 1) / T;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int ql = lane & 31, hf = lane >> 5;
   const int nq = a.nq, nk = a.nk, off = nk - nq;
   const int causal = a.causal, window = a.window;

@@ -58,6 +58,28 @@ __device__ __forceinline__ int vt_group_pos(int g) {
   return (g >> 2) * 16 + sw * 4;
 }
 
+// Combine a per-lane value with the one in lane l ^ 32 (the other half of a
+// 32x32 accumulator column): v_permlane32_swap exchanges the halves, and the
+// pair {own, other} comes back in some order, which max and + ignore.
+__device__ __forceinline__ float half_swap_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, the four 16-bit values
+// lane l receives are element (l % 4) of the 8-byte chunks addressed by
+// lanes (l % 16) / 4 + 4 j of its group, j = 0..3 (measured on gfx950).
+// Used to read MFMA operands "down the columns" of a row-major LDS tile.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t *p) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
 // XCD-aware renumbering of the linear block id: the hardware hands
 // consecutive block ids to the 8 XCDs in turn, so XCD x sees ids x, x+8, ...;
 // map them to one contiguous range of logical items per XCD so that items

@@ -68,7 +68,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdArgs a) {
   constexpr int VCH = (VUNITS + T - 1) / T;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int ql = lane & 31, hf = lane >> 5;
 
   const int item = xcd_item(blockIdx.x, a.nqt * a.heads * a.batch);

@@ -35,6 +35,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -54,57 +56,41 @@ __device__ __forceinline__ void decode_item(const FwdArgs &a, int &b, int &h, in
 }
 
 // K/V tile staging for the bf16 kernel: global -> VGPR (buffer loads, rows
-// past the slice come back as zeros) and VGPR -> LDS (K row-major, V
-// transposed with the accumulator's key order).
+// past the slice come back as zeros) -> LDS, both tiles row-major.
 template <int D, int T>
 struct KvStage {
   static constexpr int BC = 64;
   static constexpr int DCH = D / 8;                  // 16-byte chunks per row
-  static constexpr int KCH = (BC * DCH + T - 1) / T; // K chunks per thread
-  static constexpr int VUNITS = (BC / 4) * DCH;      // (4 keys x 8 dims) units per V tile
-  static constexpr int VCH = (VUNITS + T - 1) / T;
-  static constexpr int KP = D + 8;                   // K tile row pitch (bf16), +16 B vs bank conflicts
-  static constexpr int VP = BC + 8;                  // V^T tile row pitch (bf16)
+  static constexpr int NCH = (BC * DCH + T - 1) / T; // chunks per thread and tile
+  static constexpr int KP = D + 8;   // K row pitch (bf16): 16-lane b128 reads of 16 rows hit distinct banks
+  static constexpr int VP = D + 32;  // V row pitch (bf16): the 4 rows of a 32-lane transposed read start
+                                     // 16 banks apart
   static constexpr int KS = BC * KP;
-  static constexpr int VS = D * VP;
+  static constexpr int VS = BC * VP;
   static constexpr int STAGE = KS + VS;
 
-  uint4 kreg[KCH];
-  uint4 vreg[VCH][4];
+  uint4 kreg[NCH], vreg[NCH];
 
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, int k0,
                                        int tid, uint32_t kst2, uint32_t vst2) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
+    for (int i = 0; i < NCH; ++i) {
       const int c = tid + i * T;
       const int row = c / DCH, col = (c % DCH) * 8;
       kreg[i] = bload16(krs, (uint32_t)(k0 + row) * kst2 + col * 2);
-    }
-#pragma unroll
-    for (int u = 0; u < VCH; ++u) {
-      const int unit = tid + u * T;
-      const int g = unit / DCH, dc = unit % DCH;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vreg[u][i] = bload16(vrs, (uint32_t)(k0 + 4 * g + i) * vst2 + dc * 16);
+      vreg[i] = bload16(vrs, (uint32_t)(k0 + row) * vst2 + col * 2);
     }
   }
 
   __device__ __forceinline__ void store(uint16_t *ks, int tid) const {
-    uint16_t *vt = ks + KS;
+    uint16_t *vs = ks + KS;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
+    for (int i = 0; i < NCH; ++i) {
       const int c = tid + i * T;
-      if (KCH * T == BC * DCH || c < BC * DCH) {
+      if (NCH * T == BC * DCH || c < BC * DCH) {
         const int row = c / DCH, col = (c % DCH) * 8;
         *(uint4 *)(ks + row * KP + col) = kreg[i];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < VCH; ++u) {
-      const int unit = tid + u * T;
-      if (VCH * T == VUNITS || unit < VUNITS) {
-        const int g = unit / DCH, dc = unit % DCH;
-        store_transposed_4x8(vt, VP, dc * 8, vt_group_pos(g), vreg[u]);
+        *(uint4 *)(vs + row * VP + col) = vreg[i];
       }
     }
   }
@@ -117,10 +103,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int BR = 32 * NW;       // query rows per work-group
   constexpr int T = NW * 64;        // threads
   constexpr int KP = St::KP, VP = St::VP, KS = St::KS, STAGE = St::STAGE;
+  static_assert(VP % 4 == 0, "8-byte aligned transposed reads");
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int ql = lane & 31, hf = lane >> 5;
+  // this lane's source address (in V-tile elements) for the transposed reads
+  const int vtr_off = (4 * hf + (lane & 15) / 4) * St::VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   int b, h, qt;
   decode_item(a, b, h, qt);
@@ -171,22 +161,19 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
   float m = -INFINITY, l = 0.f;
   const float c = a.scale_log2;
 
-  if (jt0 < jt1) {
-    st.load(krs, vrs, jt0 * BC, tid, kst2, vst2);
-    st.store(smem, tid);
-  }
-  __syncthreads();
-
-  for (int jt = jt0; jt < jt1; ++jt) {
+  // One key tile: S^T = K Q^T, (mask), online softmax, O^T += V^T P^T.
+  // MASK = false is only used for tiles that no row of the work-group sees
+  // partially, so that path carries no compare or select at all.
+  auto tile = [&](auto mask_tag, int jt) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int buf = (jt - jt0) & 1;
     const int k0 = jt * BC;
     const bool more = jt + 1 < jt1;
     if (more) st.load(krs, vrs, k0 + BC, tid, kst2, vst2);
     const uint16_t *ks = smem + buf * STAGE;
     const uint16_t *vt = ks + KS;
-
-    const bool active = wave_rows && (!causal || k0 <= wp_hi) &&
-                        (window <= 0 || k0 + BC - 1 > wp_lo - window);
+    const bool active = !MASK || (wave_rows && (!causal || k0 <= wp_hi) &&
+                                  (window <= 0 || k0 + BC - 1 > wp_lo - window));
     if (active) {
       f32x16 s[2];
 #pragma unroll
@@ -197,9 +184,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
         for (int kk = 0; kk < D / 16; ++kk)
           s[kb] = mfma_bf16(*(const uint4 *)(krow + kk * 16), qreg[kk], s[kb]);
       }
-      const bool need_mask = (causal && k0 + BC - 1 > wp_lo) ||
-                             (window > 0 && k0 <= wp_hi - window) || (k0 + BC > nk);
-      if (need_mask) {
+      if (MASK) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -215,7 +200,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = half_swap_max(mx);
       const float m_new = fmaxf(m, mx * c);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = fast_exp2(m - m_use);
@@ -231,10 +216,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
         }
       l = l * alpha + rs;
       // the running max of most rows stops changing after a few tiles: skip
-      // the accumulator rescale when it is 1 for every row of the wave
+      // the accumulator rescale when it is 1 for every row of the wave.
+      // Passing alpha through an empty asm inside the branch stops the
+      // compiler from hoisting the 64 multiplies out of it.
       if (__ballot(alpha != 1.f)) {
+        float a_r = alpha;
+        asm volatile("" : "+v"(a_r));
 #pragma unroll
-        for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+        for (int i = 0; i < D / 32; ++i) acc[i] *= a_r;
       }
       uint4 pb[4];
 #pragma unroll
@@ -245,20 +234,53 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
         pb[cc].z = pack_bf16x2(s[kb][r0 + 4], s[kb][r0 + 5]);
         pb[cc].w = pack_bf16x2(s[kb][r0 + 6], s[kb][r0 + 7]);
       }
+      // A = V^T (32 dims x 16 keys) straight from the row-major V tile:
+      // two transposed reads give lane (d = lane % 32, half hf) the keys
+      // 16 cc + 4 hf + 0..3 and 16 cc + 8 + 4 hf + 0..3, the order in which
+      // the accumulator lists P~ for that lane half.
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const uint16_t *vrow = vt + (db * 32 + ql) * VP + hf * 8;
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-          acc[db] = mfma_bf16(*(const uint4 *)(vrow + cc * 16), pb[cc], acc[db]);
+        for (int cc = 0; cc < 4; ++cc) {
+          const uint16_t *vp = vt + vtr_off + cc * 16 * VP + db * 32;
+          const uint2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 8 * VP);
+          const uint4 va = {lo.x, lo.y, hi.x, hi.y};
+          acc[db] = mfma_bf16(va, pb[cc], acc[db]);
+        }
       }
     }
     if (more) st.store(smem + (buf ^ 1) * STAGE, tid);
     __syncthreads();
+  };
+
+  // Tiles [jt0, ja) may be cut by the window, [jb, jt1) by the diagonal or
+  // the end of the keys; [ja, jb) is seen whole by every row.
+  int ja = jt0, jb = jt1;
+  if (window > 0) {
+    // tile jt needs the mask while its first key is <= p_hi - window
+    const int lim = p_hi - window;
+    ja = lim >= 0 ? min(jt1, max(jt0, lim / BC + 1)) : jt0;
   }
+  if (causal) {
+    // tile jt needs the mask once its last key exceeds p_lo
+    const int lim = p_lo - (BC - 1);
+    jb = lim >= 0 ? max(ja, min(jt1, lim / BC + 1)) : ja;
+  }
+  if (jt1 > jt0 && jt1 * BC > nk) jb = max(ja, min(jb, jt1 - 1));
+
+  if (jt0 < jt1) {
+    st.load(krs, vrs, jt0 * BC, tid, kst2, vst2);
+    st.store(smem, tid);
+  }
+  __syncthreads();
+  const std::true_type masked;
+  const std::false_type whole;
+  for (int jt = jt0; jt < ja; ++jt) tile(masked, jt);
+  for (int jt = ja; jt < jb; ++jt) tile(whole, jt);
+  for (int jt = jb; jt < jt1; ++jt) tile(masked, jt);
 
   // epilogue: O = acc / l (bf16, round to nearest even), LSE = (m + log2 l) ln 2
-  const float lt = l + __shfl_xor(l, 32);
+  const float lt = half_swap_sum(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (my_q < nq) {
     uint16_t *orow = (uint16_t *)a.o + b * a.o_sb + (int64_t)(seq0 + my_q) * a.o_st + h * a.o_sh;
@@ -286,7 +308,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
   constexpr int BC = 32, BR = 64, DQ = D / 4, KP = D + 4;
   __shared__ float ks[BC * KP];
   __shared__ float vs[BC * KP];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int qr = lane & 15, quarter = lane >> 4;
 
   int b, h, qt;

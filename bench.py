@@ -177,6 +177,45 @@ def extra_rows(torch, fa, steps):
     return rows
 
 
+WORKLOAD_CHOICES = ("fwd_causal", "fwd_noncausal", "bwd", "varlen", "fp8")
+
+
+def make_step(name, torch, fa):
+    """(step fn, FLOPs per step, description, dtype, peak TFLOP/s, kernel source) of a workload,
+    inputs generated and moved to HBM before timing."""
+    from exact_attention_24_amd.inputs import WORKLOADS, workload_inputs
+    if name in ("fwd_causal", "fwd_noncausal"):
+        causal = name == "fwd_causal"
+        w = WORKLOADS["llama_n8192"]
+        t = workload_inputs("llama_n8192")
+        q, k, v = (t[x].cuda() for x in ("q", "k", "v"))
+        o = torch.empty_like(q)
+        lse = torch.empty((1, w.heads, w.seqlen), dtype=torch.float32, device="cuda")
+        desc = f"fwd B1 H32 N8192 d128 bf16 {'causal' if causal else 'non-causal'} (Llama-7B attention shape)"
+        return (lambda: fa.fa_fwd(q, k, v, causal=causal, out=o, lse=lse),
+                fwd_flops(1, 32, 8192, 128, causal), desc, "bf16", PEAK_BF16_TFLOPS, "fa_fwd.hip")
+    if name == "bwd":
+        t = {k_: v_.cuda() for k_, v_ in workload_inputs("bwd_n8192").items()}
+        o, lse = fa.fa_fwd(t["q"], t["k"], t["v"], causal=True)
+        dq, dk, dv = (torch.empty(t[x].shape, dtype=torch.float32, device="cuda") for x in ("q", "k", "v"))
+        return (lambda: fa.fa_bwd(t["dout"], t["q"], t["k"], t["v"], o, lse, causal=True, dq=dq, dk=dk, dv=dv),
+                2.5 * fwd_flops(1, 32, 8192, 128, True), "bwd B1 H32 N8192 d128 bf16 causal, fp32 gradients",
+                "bf16", PEAK_BF16_TFLOPS, "fa_bwd.hip")
+    if name == "varlen":
+        w = WORKLOADS["varlen_32k"]
+        t = workload_inputs("varlen_32k")
+        q, k, v, cu = (t[x].cuda() for x in ("q", "k", "v", "cu_seqlens"))
+        mx = max(t["lengths"])
+        f = 4.0 * w.head_dim * w.heads * visible_pairs_varlen(t["lengths"], True, w.window)
+        return (lambda: fa.fa_varlen_fwd(q, k, v, cu, mx, causal=True, window=w.window), f,
+                "varlen fwd 32768 tokens H28 d128 bf16 causal window 4096", "bf16", PEAK_BF16_TFLOPS, "fa_fwd.hip")
+    t = workload_inputs("fp8_n8192")
+    q8, k8, v8 = (t[x].cuda() for x in ("q8", "k8", "v8"))
+    ds = (t["q_scale"], t["k_scale"], t["v_scale"])
+    return (lambda: fa.fa_fwd(q8, k8, v8, causal=True, descale=ds), fwd_flops(1, 32, 8192, 128, True),
+            "fwd B1 H32 N8192 d128 fp8-e4m3 causal", "fp8_e4m3", PEAK_FP8_TFLOPS, "fa_fp8.hip")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -187,8 +226,13 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run one plain 1 GiB device copy (HBM-counter calibration)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--workload", default="fwd_causal",
+                    help="what one step runs: " + ", ".join(WORKLOAD_CHOICES) +
+                         " (default fwd_causal, the headline; the others are for profiling runs)")
     args = ap.parse_args()
 
+    if args.workload not in WORKLOAD_CHOICES:
+        ap.error(f"--workload must be one of {WORKLOAD_CHOICES}")
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this library has no multi-GPU path",
               file=sys.stderr)
@@ -202,37 +246,30 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     fa.lib()  # fail loudly if the HIP library is missing
-    w = WORKLOADS["llama_n8192"]
-    log(f"[bench] {torch.cuda.get_device_name(0)}; workload {w.name}")
-    t = workload_inputs("llama_n8192")
-    q, k, v = (t[x].cuda() for x in ("q", "k", "v"))
-    o = torch.empty_like(q)
-    lse = torch.empty((1, w.heads, w.seqlen), dtype=torch.float32, device="cuda")
-
-    def step():
-        fa.fa_fwd(q, k, v, causal=True, out=o, lse=lse)
+    step, flops, desc, dtype, peak, src = make_step(args.workload, torch, fa)
+    log(f"[bench] {torch.cuda.get_device_name(0)}; workload {desc}")
 
     wall_ms, per_call = time_calls(step, args.warmup, args.steps, torch)
-    flops = fwd_flops(w.batch, w.heads, w.seqlen, w.head_dim, True)
     ms_per_step = wall_ms / args.steps
     kernel_ms = sum(per_call) / len(per_call)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kernel_ms * 1e-3) / 1e12
-    log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step (wall), kernel avg {kernel_ms:.4f} ms, "
+    log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step (wall), per-call avg {kernel_ms:.4f} ms, "
         f"{achieved:.1f} TFLOP/s")
 
     if args.calib_copy:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
+        src_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst_buf = torch.empty_like(src_buf)
+        dst_buf.copy_(src_buf)
         torch.cuda.synchronize()
         log("[bench] calibration copy of 1 GiB done")
 
-    sha = src_hash("fa_fwd.hip")
-    rows = {} if args.no_rows else extra_rows(torch, fa, max(5, min(args.steps, 20)))
+    sha = src_hash(src)
+    headline = args.workload == "fwd_causal"
+    rows = {} if (args.no_rows or not headline) else extra_rows(torch, fa, max(5, min(args.steps, 20)))
     if rows:
         log(f"[bench] rows: {json.dumps(rows)}")
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_budget)
+    cpu = None if (args.no_cpu_baseline or not headline) else cpu_baseline(args.cpu_budget)
 
     out = {
         "metric": "attention fwd TFLOP/s + % MFMA peak, bf16 causal N=8192 d=128, 1 GPU",
@@ -245,15 +282,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic: seeded i.i.d. N(0,1) Q/K/V cast to bf16",
-        "config": {"workload": "fwd B1 H32 N8192 d128 bf16 causal (Llama-7B attention shape)",
-                   "batch": 1, "heads": 32, "seq_len": 8192, "head_dim": 128, "causal": True,
-                   "parallelism": "none (1 GPU)"},
-        "pct_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_from_profile(sha), "kernel_src_sha": sha},
+        "dtype": dtype,
+        "data": "synthetic: seeded i.i.d. N(0,1) inputs (see exact_attention_24_amd/inputs.py)",
+        "config": {"workload": desc, "parallelism": "none (1 GPU)"},
+        "pct_mfma_peak": round(100 * value / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic_from_profile(sha) if headline else None, "kernel_src_sha": sha},
         "cpu_baseline": cpu,
         "rows": rows,
     }

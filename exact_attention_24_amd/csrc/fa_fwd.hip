@@ -12,28 +12,35 @@
 // tiles that the mask hides entirely are skipped (FA-3 paragraph of the
 // ms-swift integration page).
 //
-// gfx950 mapping of the bf16 kernel (one work-group = NW waves, 32 query rows
-// per wave, key tiles of 64):
+// gfx950 mapping of the bf16 kernel (work-group = 8 waves x 32 query rows,
+// key tiles of 64, two waves per SIMD):
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims read as
 //     16-byte rows of the K tile in LDS, B = Q^T held in VGPRs for the whole
-//     loop.  The 32x32 accumulator then gives every lane ONE query (lane % 32)
-//     and 16 keys, so the row max / row sum need only in-lane work plus one
-//     exchange with lane ^ 32.
-//   * O^T += V^T P^T on the same MFMA: B = P^T comes straight from the S^T
-//     accumulator registers (converted to bf16), A = V^T read from a
-//     transposed copy of the V tile in LDS whose key order inside each group
-//     of 16 keys matches the accumulator's layout, so no register shuffles are
-//     needed.  O^T again gives each lane one query, so the rescale by
-//     alpha = 2^(m_old - m_new) is a per-lane scalar.
-//   * K/V tiles stream global -> VGPR -> LDS with 16-byte coalesced loads,
-//     issued one tile ahead and double-buffered in LDS (one barrier per tile).
+//     loop.  The 32x32 accumulator gives every lane ONE query (lane % 32) and
+//     16 keys, so the row max / row sum need only in-lane work plus one
+//     v_permlane32_swap with the other half of the wave.
+//   * O^T += V^T P~^T on the same MFMA: B = P~^T straight from the S^T
+//     accumulator (converted to bf16), A = V^T read with ds_read_b64_tr_b16
+//     from the row-major V tile, addressed so that its key order matches the
+//     accumulator's; O^T again gives each lane one query, so the rescale by
+//     alpha = 2^(m_old - m_new) is a per-lane scalar (and is skipped when no
+//     row max of the wave changed).
+//   * The product of tile j-1 is deferred into tile j: the softmax stages of
+//     S(j) are issued between the MFMAs of O += V(j-1)^T P~(j-1)^T, so each
+//     wave keeps the VALU and the matrix cores busy at once.
+//   * K/V tiles stream global -> VGPR -> LDS with 16-byte buffer loads (rows
+//     past the end read as zeros), K one tile ahead of V, rings of two LDS
+//     buffers, one barrier per tile; row pitches chosen so every LDS access
+//     pattern is bank-conflict free.
+//   * Key tiles that no row sees partially run without any mask code; the
+//     edge tiles of the causal diagonal, the window and the key tail take a
+//     masked path.
 //   * Work-group ids are renumbered so each XCD (own L2) processes a
 //     contiguous range of (head, query-tile) items, keeping a head's K/V in one
 //     L2; causal items run heaviest first.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <stdlib.h>
 
 #include <type_traits>
 
@@ -55,62 +62,71 @@ __device__ __forceinline__ void decode_item(const FwdArgs &a, int &b, int &h, in
   h = bh % a.heads;
 }
 
-// K/V tile staging for the bf16 kernel: global -> VGPR (buffer loads, rows
-// past the slice come back as zeros) -> LDS, both tiles row-major.
+// K/V staging with K and V of different tiles (K runs one tile ahead).
 template <int D, int T>
 struct KvStage {
   static constexpr int BC = 64;
-  static constexpr int DCH = D / 8;                  // 16-byte chunks per row
-  static constexpr int NCH = (BC * DCH + T - 1) / T; // chunks per thread and tile
+  static constexpr int DCH = D / 8;
+  static constexpr int NCH = (BC * DCH + T - 1) / T;
   static constexpr int KP = D + 8;   // K row pitch (bf16): 16-lane b128 reads of 16 rows hit distinct banks
   static constexpr int VP = D + 32;  // V row pitch (bf16): the 4 rows of a 32-lane transposed read start
                                      // 16 banks apart
   static constexpr int KS = BC * KP;
   static constexpr int VS = BC * VP;
-  static constexpr int STAGE = KS + VS;
 
   uint4 kreg[NCH], vreg[NCH];
 
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, int k0,
-                                       int tid, uint32_t kst2, uint32_t vst2) {
+  __device__ __forceinline__ void load_k(__amdgpu_buffer_rsrc_t krs, int k0, int tid, uint32_t kst2) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = tid + i * T;
-      const int row = c / DCH, col = (c % DCH) * 8;
-      kreg[i] = bload16(krs, (uint32_t)(k0 + row) * kst2 + col * 2);
-      vreg[i] = bload16(vrs, (uint32_t)(k0 + row) * vst2 + col * 2);
+      kreg[i] = bload16(krs, (uint32_t)(k0 + c / DCH) * kst2 + (c % DCH) * 16);
     }
   }
-
-  __device__ __forceinline__ void store(uint16_t *ks, int tid) const {
-    uint16_t *vs = ks + KS;
+  __device__ __forceinline__ void load_v(__amdgpu_buffer_rsrc_t vrs, int k0, int tid, uint32_t vst2) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = tid + i * T;
-      if (NCH * T == BC * DCH || c < BC * DCH) {
-        const int row = c / DCH, col = (c % DCH) * 8;
-        *(uint4 *)(ks + row * KP + col) = kreg[i];
-        *(uint4 *)(vs + row * VP + col) = vreg[i];
-      }
+      vreg[i] = bload16(vrs, (uint32_t)(k0 + c / DCH) * vst2 + (c % DCH) * 16);
+    }
+  }
+  __device__ __forceinline__ void store_k(uint16_t *ks, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + i * T;
+      if (NCH * T == BC * DCH || c < BC * DCH) *(uint4 *)(ks + (c / DCH) * KP + (c % DCH) * 8) = kreg[i];
+    }
+  }
+  __device__ __forceinline__ void store_v(uint16_t *vs, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + i * T;
+      if (NCH * T == BC * DCH || c < BC * DCH) *(uint4 *)(vs + (c / DCH) * VP + (c % DCH) * 8) = vreg[i];
     }
   }
 };
 
+// ---------------------------------------------------------------------------
+// bf16 forward with the P.V product deferred by one key tile.  8 waves of 32
+// query rows (256 rows per work-group), two waves per SIMD.  For key tile j
+// each wave computes S(j) = K(j) Q^T, then runs the online softmax of S(j)
+// on the VALU while the matrix cores accumulate O += V(j-1)^T P~(j-1)^T of
+// the previous tile: the softmax overlaps matrix work inside every wave,
+// and both waves of a SIMD keep feeding the matrix cores from LDS.  K is
+// staged one tile ahead of V (LDS rings of two for each).
+// ---------------------------------------------------------------------------
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
-  using St = KvStage<D, NW * 64>;
-  constexpr int BC = St::BC;        // keys per tile
-  constexpr int BR = 32 * NW;       // query rows per work-group
-  constexpr int T = NW * 64;        // threads
-  constexpr int KP = St::KP, VP = St::VP, KS = St::KS, STAGE = St::STAGE;
+  constexpr int T = NW * 64, BR = NW * 32;
+  using St = KvStage<D, T>;
+  constexpr int BC = St::BC, KP = St::KP, VP = St::VP, KS = St::KS, VS = St::VS;
   static_assert(VP % 4 == 0, "8-byte aligned transposed reads");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * KS + 2 * VS];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int ql = lane & 31, hf = lane >> 5;
-  // this lane's source address (in V-tile elements) for the transposed reads
-  const int vtr_off = (4 * hf + (lane & 15) / 4) * St::VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int vtr_off = (4 * hf + (lane & 15) / 4) * VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   int b, h, qt;
   decode_item(a, b, h, qt);
@@ -132,7 +148,6 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
   const __amdgpu_buffer_rsrc_t vrs = slice_rsrc(vbase, slice_bytes(nk, a.v_st, D, 2));
   const uint32_t kst2 = (uint32_t)a.k_st * 2, vst2 = (uint32_t)a.v_st * 2;
 
-  // key range the whole work-group needs
   const int p_lo = q0 + off, p_hi = min(q0 + BR, nq) - 1 + off;
   int kv_lo = 0, kv_hi = nk;
   if (causal) kv_hi = min(nk, p_hi + 1);
@@ -140,12 +155,17 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int jt0 = kv_lo / BC;
   const int jt1 = kv_hi > kv_lo ? (kv_hi + BC - 1) / BC : jt0;
 
-  // this wave's rows
   const int wq0 = q0 + 32 * wave;
   const bool wave_rows = wq0 < nq;
   const int wp_lo = wq0 + off, wp_hi = min(wq0 + 31, nq - 1) + off;
   const int my_q = wq0 + ql;
   const int my_p = my_q + off;
+  auto active = [&](int jt) __attribute__((always_inline)) {
+    const int k0 = jt * BC;
+    return wave_rows && (!causal || k0 <= wp_hi) && (window <= 0 || k0 + BC - 1 > wp_lo - window);
+  };
+  auto kbuf = [&](int jt) __attribute__((always_inline)) { return smem + ((jt - jt0) & 1) * KS; };
+  auto vbuf = [&](int jt) __attribute__((always_inline)) { return smem + 2 * KS + ((jt - jt0) & 1) * VS; };
 
   uint4 qreg[D / 16];
   {
@@ -160,124 +180,199 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
   for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
   float m = -INFINITY, l = 0.f;
   const float c = a.scale_log2;
+  f32x16 s[2];
+  uint4 pb_prev[4];        // P~ of the previous tile (B operands)
+  float alpha_prev = 1.f;  // accumulator rescale that goes with it
+  bool has_prev = false;
 
-  // One key tile: S^T = K Q^T, (mask), online softmax, O^T += V^T P^T.
-  // MASK = false is only used for tiles that no row of the work-group sees
-  // partially, so that path carries no compare or select at all.
-  auto tile = [&](auto mask_tag, int jt) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const int buf = (jt - jt0) & 1;
-    const int k0 = jt * BC;
-    const bool more = jt + 1 < jt1;
-    if (more) st.load(krs, vrs, k0 + BC, tid, kst2, vst2);
-    const uint16_t *ks = smem + buf * STAGE;
-    const uint16_t *vt = ks + KS;
-    const bool active = !MASK || (wave_rows && (!causal || k0 <= wp_hi) &&
-                                  (window <= 0 || k0 + BC - 1 > wp_lo - window));
-    if (active) {
-      f32x16 s[2];
+  auto qk = [&](const uint16_t *ks) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = (f32x16){};
-        const uint16_t *krow = ks + (kb * 32 + ql) * KP + hf * 8;
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = (f32x16){};
+      const uint16_t *krow = ks + (kb * 32 + ql) * KP + hf * 8;
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-          s[kb] = mfma_bf16(*(const uint4 *)(krow + kk * 16), qreg[kk], s[kb]);
-      }
-      if (MASK) {
+      for (int kk = 0; kk < D / 16; ++kk) s[kb] = mfma_bf16(*(const uint4 *)(krow + kk * 16), qreg[kk], s[kb]);
+    }
+  };
+  auto rescale_prev = [&]() __attribute__((always_inline)) {
+    if (__ballot(alpha_prev != 1.f)) {  // rarely taken once the row maxima settle
+      float a_r = alpha_prev;
+      asm volatile("" : "+v"(a_r));  // keep the multiplies inside this branch
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int i = 0; i < D / 32; ++i) acc[i] *= a_r;
+    }
+  };
+  auto pv_prev = [&](const uint16_t *vs) __attribute__((always_inline)) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            const bool ok = key < nk && (!causal || key <= my_p) &&
-                            (window <= 0 || key > my_p - window);
-            if (!ok) s[kb][r] = -INFINITY;
-          }
-      }
-      float mx = s[0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = half_swap_max(mx);
-      const float m_new = fmaxf(m, mx * c);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_use);
-      m = m_new;
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
-          s[kb][r] = p;
-          rs += p;
-        }
-      l = l * alpha + rs;
-      // the running max of most rows stops changing after a few tiles: skip
-      // the accumulator rescale when it is 1 for every row of the wave.
-      // Passing alpha through an empty asm inside the branch stops the
-      // compiler from hoisting the 64 multiplies out of it.
-      if (__ballot(alpha != 1.f)) {
-        float a_r = alpha;
-        asm volatile("" : "+v"(a_r));
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) acc[i] *= a_r;
-      }
-      uint4 pb[4];
+    for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
-        const int kb = cc >> 1, r0 = (cc & 1) * 8;
-        pb[cc].x = pack_bf16x2(s[kb][r0 + 0], s[kb][r0 + 1]);
-        pb[cc].y = pack_bf16x2(s[kb][r0 + 2], s[kb][r0 + 3]);
-        pb[cc].z = pack_bf16x2(s[kb][r0 + 4], s[kb][r0 + 5]);
-        pb[cc].w = pack_bf16x2(s[kb][r0 + 6], s[kb][r0 + 7]);
-      }
-      // A = V^T (32 dims x 16 keys) straight from the row-major V tile:
-      // two transposed reads give lane (d = lane % 32, half hf) the keys
-      // 16 cc + 4 hf + 0..3 and 16 cc + 8 + 4 hf + 0..3, the order in which
-      // the accumulator lists P~ for that lane half.
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const uint16_t *vp = vt + vtr_off + cc * 16 * VP + db * 32;
-          const uint2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 8 * VP);
-          const uint4 va = {lo.x, lo.y, hi.x, hi.y};
-          acc[db] = mfma_bf16(va, pb[cc], acc[db]);
-        }
+        const uint16_t *vp = vs + vtr_off + cc * 16 * VP + db * 32;
+        const uint2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 8 * VP);
+        const uint4 va = {lo.x, lo.y, hi.x, hi.y};
+        acc[db] = mfma_bf16(va, pb_prev[cc], acc[db]);
       }
     }
-    if (more) st.store(smem + (buf ^ 1) * STAGE, tid);
-    __syncthreads();
+  };
+  auto softmax = [&](auto mask_tag, int k0, uint4 (&pb)[4]) __attribute__((always_inline)) -> float {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    if (MASK) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
+          const bool ok = key < nk && (!causal || key <= my_p) && (window <= 0 || key > my_p - window);
+          if (!ok) s[kb][e] = -INFINITY;
+        }
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
+    mx = half_swap_max(mx);
+    const float m_new = fmaxf(m, mx * c);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    m = m_new;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = fast_exp2(__builtin_fmaf(s[kb][e], c, -m_use));
+        s[kb][e] = p;
+        rs += p;
+      }
+    l = l * alpha + rs;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const int kb = cc >> 1, r0 = (cc & 1) * 8;
+      pb[cc].x = pack_bf16x2(s[kb][r0 + 0], s[kb][r0 + 1]);
+      pb[cc].y = pack_bf16x2(s[kb][r0 + 2], s[kb][r0 + 3]);
+      pb[cc].z = pack_bf16x2(s[kb][r0 + 4], s[kb][r0 + 5]);
+      pb[cc].w = pack_bf16x2(s[kb][r0 + 6], s[kb][r0 + 7]);
+    }
+    return alpha;
   };
 
-  // Tiles [jt0, ja) may be cut by the window, [jb, jt1) by the diagonal or
-  // the end of the keys; [ja, jb) is seen whole by every row.
+  // one key tile: K(jt+1) and V(jt) are fetched into registers meanwhile
+  auto step = [&](auto mask_tag, int jt) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int k0 = jt * BC;
+    const bool more_k = jt + 1 < jt1;
+    if (!MASK || more_k) st.load_k(krs, k0 + BC, tid, kst2);
+    st.load_v(vrs, k0, tid, vst2);
+    uint4 pb[4];
+    float alpha = 1.f;
+    if (!MASK) {
+      // interior tile: the wave sees the whole tile and the previous one.
+      // The softmax of S(jt) is cut into 16 stages, each issued next to one
+      // MFMA of the previous tile's O += V^T P~^T (whose transposed operand
+      // reads run two MFMAs ahead); the scheduling fences keep the compiler
+      // from regrouping them, so the VALU and the matrix cores work at once.
+      qk(kbuf(jt));
+      rescale_prev();
+      const uint16_t *vs = vbuf(jt - 1) + vtr_off;
+      auto vread = [&](int i) __attribute__((always_inline)) {
+        const uint16_t *vp = vs + (i % 4) * 16 * VP + (i / 4) * 32;
+        const uint2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 8 * VP);
+        return (uint4){lo.x, lo.y, hi.x, hi.y};
+      };
+      constexpr int NOP = (D / 32) * 4;  // MFMAs of the product
+      uint4 va[NOP];
+      va[0] = vread(0);
+      va[1] = vread(1);
+      float mx = 0.f, m_use = 0.f, rs = 0.f;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i + 2 < NOP) va[i + 2] = vread(i + 2);
+        if (i < NOP) acc[i / 4] = mfma_bf16(va[i], pb_prev[i % 4], acc[i / 4]);
+        // softmax stage i
+        if (i == 0) {
+          mx = s[0][0];
+#pragma unroll
+          for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[0][e]);
+        } else if (i == 1) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[1][e]);
+          mx = half_swap_max(mx);
+          const float m_new = fmaxf(m, mx * c);
+          m_use = m_new == -INFINITY ? 0.f : m_new;
+          alpha = fast_exp2(m - m_use);
+          m = m_new;
+        } else if (i < 10) {
+          const int kb = (i - 2) >> 2, e0 = ((i - 2) & 3) * 4;
+#pragma unroll
+          for (int e = e0; e < e0 + 4; ++e) {
+            const float p = fast_exp2(__builtin_fmaf(s[kb][e], c, -m_use));
+            s[kb][e] = p;
+            rs += p;
+          }
+          if (i == 9) l = l * alpha + rs;
+        } else if (i < 14) {
+          const int cc = i - 10, kb = cc >> 1, r0 = (cc & 1) * 8;
+          pb[cc].x = pack_bf16x2(s[kb][r0 + 0], s[kb][r0 + 1]);
+          pb[cc].y = pack_bf16x2(s[kb][r0 + 2], s[kb][r0 + 3]);
+          pb[cc].z = pack_bf16x2(s[kb][r0 + 4], s[kb][r0 + 5]);
+          pb[cc].w = pack_bf16x2(s[kb][r0 + 6], s[kb][r0 + 7]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      has_prev = true;
+    } else {
+      const bool act = active(jt);
+      if (act) qk(kbuf(jt));
+      if (has_prev) {
+        rescale_prev();
+        pv_prev(vbuf(jt - 1));
+      }
+      if (act) alpha = softmax(std::true_type(), k0, pb);
+      has_prev = act;
+    }
+    // interior tiles always have a next tile (the last tile takes the masked
+    // path), so their K store is unconditional and no branch splits the
+    // scheduled region above
+    if (!MASK || more_k) st.store_k(kbuf(jt + 1), tid);
+    st.store_v(vbuf(jt), tid);
+    __syncthreads();
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) pb_prev[cc] = pb[cc];
+    alpha_prev = alpha;
+  };
+
+  // tiles [jt0, ja) may be cut by the window, [jb, jt1) by the diagonal or
+  // the end of the keys; the first tile always takes the masked path (no
+  // previous product yet)
   int ja = jt0, jb = jt1;
   if (window > 0) {
-    // tile jt needs the mask while its first key is <= p_hi - window
     const int lim = p_hi - window;
     ja = lim >= 0 ? min(jt1, max(jt0, lim / BC + 1)) : jt0;
   }
   if (causal) {
-    // tile jt needs the mask once its last key exceeds p_lo
     const int lim = p_lo - (BC - 1);
     jb = lim >= 0 ? max(ja, min(jt1, lim / BC + 1)) : ja;
   }
   if (jt1 > jt0 && jt1 * BC > nk) jb = max(ja, min(jb, jt1 - 1));
+  ja = min(max(ja, jt0 + 1), jt1);
+  jb = max(min(jb, jt1 - 1), ja);
 
   if (jt0 < jt1) {
-    st.load(krs, vrs, jt0 * BC, tid, kst2, vst2);
-    st.store(smem, tid);
+    st.load_k(krs, jt0 * BC, tid, kst2);
+    st.store_k(kbuf(jt0), tid);
   }
   __syncthreads();
   const std::true_type masked;
   const std::false_type whole;
-  for (int jt = jt0; jt < ja; ++jt) tile(masked, jt);
-  for (int jt = ja; jt < jb; ++jt) tile(whole, jt);
-  for (int jt = jb; jt < jt1; ++jt) tile(masked, jt);
+  for (int jt = jt0; jt < ja; ++jt) step(masked, jt);
+  for (int jt = ja; jt < jb; ++jt) step(whole, jt);
+  for (int jt = jb; jt < jt1; ++jt) step(masked, jt);
+  if (has_prev) {
+    rescale_prev();
+    pv_prev(vbuf(jt1 - 1));
+  }
 
   // epilogue: O = acc / l (bf16, round to nearest even), LSE = (m + log2 l) ln 2
   const float lt = half_swap_sum(l);
@@ -294,8 +389,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
         *(uint2 *)(orow + db * 32 + 8 * rb + 4 * hf) = w;
       }
     if (hf == 0 && a.lse)
-      a.lse[b * a.lse_sb + h * a.lse_sh + seq0 + my_q] =
-          lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+      a.lse[b * a.lse_sb + h * a.lse_sh + seq0 + my_q] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
   }
 }
 
@@ -396,37 +490,18 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
 
 }  // namespace
 
-// Waves per work-group of the bf16 forward (32 query rows each).  8 by
-// default; FA_FWD_WAVES=4 selects the 4-wave variant (for tuning runs).
-static int bf16_waves() {
-  static const int w = [] {
-    const char *e = getenv("FA_FWD_WAVES");
-    return (e && atoi(e) == 4) ? 4 : 8;
-  }();
-  return w;
-}
-
 int fwd_block_rows(int qkv_dtype, int head_dim) {
   (void)head_dim;
-  if (qkv_dtype == 0) return 64;   // fp32 kernel
-  if (qkv_dtype == 2) return 256;  // fp8 kernel: 8 waves
-  return 32 * bf16_waves();
+  if (qkv_dtype == 0) return 64;  // fp32 kernel: 4 waves x 16 rows
+  return 256;                     // bf16 and fp8 kernels: 8 waves x 32 rows
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, int head_dim, hipStream_t s) {
   const dim3 grid((unsigned)(a.nqt * a.heads * a.batch));
-  const int nw = bf16_waves();
-  if (head_dim == 128) {
-    if (nw == 8)
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, 8>), grid, dim3(512), 0, s, a);
-    else
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, 4>), grid, dim3(256), 0, s, a);
-  } else {
-    if (nw == 8)
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, 8>), grid, dim3(512), 0, s, a);
-    else
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, 4>), grid, dim3(256), 0, s, a);
-  }
+  if (head_dim == 128)
+    hipLaunchKernelGGL((fwd_bf16_kernel<128, 8>), grid, dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<64, 8>), grid, dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

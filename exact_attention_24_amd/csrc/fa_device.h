@@ -80,6 +80,36 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t *p) {
   return __builtin_bit_cast(uint2, r);
 }
 
+// Row-major bf16 tiles of 64 rows x D elements that are read both along rows
+// (ds_read_b128, 16 rows per pass) and down columns (ds_read_b64_tr_b16) are
+// stored without padding, their 16-byte chunks XOR-swizzled per row:
+// physical chunk = chunk ^ swz(row).  These swizzles make both read patterns
+// and the staging writes bank-conflict free (checked exhaustively on a CPU
+// model of the 64 LDS banks).
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128)
+    return 4 * (row & 3) + ((row >> 2) & 3);
+  else
+    return 4 * ((row >> 1) & 1) + ((row >> 2) & 1) + 2 * ((row >> 3) & 1);
+}
+// element offset of 16-byte chunk `chunk` of row `row`
+template <int D>
+__device__ __forceinline__ int swz_off(int row, int chunk) {
+  return row * D + ((chunk ^ swz<D>(row)) << 3);
+}
+// Per-lane element offsets of the transposed operand reads from a swizzled
+// tile: lane s reads rows 16 cc + 8 half + 4 (s / 32) + (s % 16) / 4 at
+// column 32 db + 16 ((s / 16) % 2) + 4 (s % 4); the swizzle of those rows
+// does not depend on cc, so the offset for (db, half) is a per-lane constant
+// and cc adds 16 cc D.
+template <int D>
+__device__ __forceinline__ int tr_off(int lane, int db, int half) {
+  const int row = 8 * half + 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int chunk = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  return swz_off<D>(row, chunk) + 4 * (lane & 1);
+}
+
 // XCD-aware renumbering of the linear block id: the hardware hands
 // consecutive block ids to the 8 XCDs in turn, so XCD x sees ids x, x+8, ...;
 // map them to one contiguous range of logical items per XCD so that items

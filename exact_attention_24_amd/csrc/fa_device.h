@@ -110,6 +110,62 @@ __device__ __forceinline__ int tr_off(int lane, int db, int half) {
   return swz_off<D>(row, chunk) + 4 * (lane & 1);
 }
 
+// LDS DMA of 16 bytes per lane: the 16 bytes at byte offset `off` of the
+// buffer described by `r` land at lds_wave + 16 * lane (lds_wave must be
+// wave-uniform); offsets past the end of the buffer deliver zeros.  Issued
+// from inline assembly so the compiler does not wait for its completion
+// before unrelated LDS reads; callers wait with wait_dma() and a barrier
+// before anything reads the destination.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 buffer_words(const void *base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  return (i32x4){(int)(uint32_t)p, (int)((p >> 32) & 0xffff), (int)bytes, 0x00020000};
+}
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(i32x4 r, const uint16_t *lds_wave, uint32_t off) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t *)lds_wave;
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(off), "s"(r)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// same, with the wave-uniform LDS byte address given directly
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16_at(i32x4 r, uint32_t lds_byte, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_byte), "v"(off), "s"(r)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// MFMA issued from inline assembly with the register file of every operand
+// pinned (accumulators of O in AGPRs, S in VGPRs, persistent B operands in
+// AGPRs), so the compiler never shuttles them between files.  The compiler
+// does not see these as MFMAs, so the waits the hardware does not enforce
+// are the caller's: an MFMA result is read by any other instruction only
+// after mfma_drain*() (>= 11 wait states after an 8-pass XDL op), and a VALU
+// write of an operand precedes its MFMA read by >= 2 wait states.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 vec4(const uint4 &x) { return (u32x4){x.x, x.y, x.z, x.w}; }
+__device__ __forceinline__ void mfma_a(f32x16 &acc, const uint4 &a, const uint4 &b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(vec4(a)), "v"(vec4(b)));
+}
+__device__ __forceinline__ void mfma_v_first(f32x16 &d, const uint4 &a, const u32x4 &b_agpr) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(vec4(a)), "a"(b_agpr));
+}
+__device__ __forceinline__ void mfma_v(f32x16 &d, const uint4 &a, const u32x4 &b_agpr) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(vec4(a)), "a"(b_agpr));
+}
+__device__ __forceinline__ void mfma_drain2_v(f32x16 &x, f32x16 &y) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ void mfma_drain_a(f32x16 &x) { asm volatile("s_nop 7\n\ts_nop 7" : "+a"(x)); }
+__device__ __forceinline__ void valu_to_mfma_a(f32x16 &x) { asm volatile("s_nop 1" : "+a"(x)); }
+
 // XCD-aware renumbering of the linear block id: the hardware hands
 // consecutive block ids to the 8 XCDs in turn, so XCD x sees ids x, x+8, ...;
 // map them to one contiguous range of logical items per XCD so that items

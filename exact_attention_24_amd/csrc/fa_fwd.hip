@@ -106,6 +106,13 @@ struct KvStage {
   }
 };
 
+// The running row max only moves when a tile's row max exceeds it by more
+// than kLazy (log2 units): P~ = 2^(s - m) then stays <= 2^kLazy, far inside
+// fp32 and bf16 range, and the accumulators are rescaled only when a row max
+// jumps that far (with inputs of unit scale, only on the first tile).  The
+// result is exact either way: O and LSE are formed with the same m.
+constexpr float kLazy = 8.f;
+
 // ---------------------------------------------------------------------------
 // bf16 forward with the P.V product deferred by one key tile.  8 waves of 32
 // query rows (256 rows per work-group), two waves per SIMD.  For key tile j
@@ -231,11 +238,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
-    mx = half_swap_max(mx);
-    const float m_new = fmaxf(m, mx * c);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
-    m = m_new;
+    mx = half_swap_max(mx) * c;
+    const bool up = mx > m + kLazy;
+    const float alpha = up ? fast_exp2(m - mx) : 1.f;
+    m = up ? mx : m;
+    const float m_use = m == -INFINITY ? 0.f : m;
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -298,11 +305,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
         } else if (i == 1) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[1][e]);
-          mx = half_swap_max(mx);
-          const float m_new = fmaxf(m, mx * c);
-          m_use = m_new == -INFINITY ? 0.f : m_new;
-          alpha = fast_exp2(m - m_use);
-          m = m_new;
+          mx = half_swap_max(mx) * c;
+          const bool up = mx > m + kLazy;
+          alpha = up ? fast_exp2(m - mx) : 1.f;
+          m = up ? mx : m;
+          m_use = m == -INFINITY ? 0.f : m;
         } else if (i < 10) {
           const int kb = (i - 2) >> 2, e0 = ((i - 2) & 3) * 4;
 #pragma unroll

@@ -302,7 +302,7 @@ fa_status fa_bwd(const fa_bwd_params *p, void *workspace, size_t workspace_bytes
   a.dq = p->dq; a.dk = p->dk; a.dv = p->dv;
   const size_t dsz = ((size_t)p->batch * p->heads * p->seqlen_q * sizeof(float) + 255) / 256 * 256;
   a.dpsum = static_cast<float *>(workspace);
-  a.dq_accum = need > dsz ? reinterpret_cast<float *>(static_cast<char *>(workspace) + dsz) : nullptr;
+  a.lse2 = reinterpret_cast<float *>(static_cast<char *>(workspace) + dsz);
   a.q_sb = p->q_stride[0]; a.q_st = p->q_stride[1]; a.q_sh = p->q_stride[2];
   a.k_sb = p->k_stride[0]; a.k_st = p->k_stride[1]; a.k_sh = p->k_stride[2];
   a.v_sb = p->v_stride[0]; a.v_st = p->v_stride[1]; a.v_sh = p->v_stride[2];

@@ -51,7 +51,8 @@ __device__ __forceinline__ void store_grad4(void *base, int64_t elem_off, bool f
 }
 
 // ---------------------------------------------------------------------------
-// 1. D_i = sum_c dO_ic O_ic, [batch, heads, nq] fp32
+// 1. D_i = sum_c dO_ic O_ic and LSE_i log2(e), [batch, heads, nq] fp32.
+//    A row that saw no key (LSE = -inf) gets +inf, so P = 2^(s - lse2) = 0.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dsum_kernel(BwdArgs a) {
@@ -74,30 +75,40 @@ __global__ __launch_bounds__(256) void bwd_dsum_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  if (row < total && sub == 0) a.dpsum[row] = acc;
+  if (row < total && sub == 0) {
+    a.dpsum[row] = acc;
+    const float x = a.lse[row];
+    a.lse2[row] = x == -INFINITY ? INFINITY : x * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------------------
-// 2. dK, dV: key-tile outer, query-tile inner
+// 2. dK, dV: key-tile outer, query-tile inner.  One work-group of 4 waves per
+//    128 keys (32 per wave, one wave per SIMD); per query tile of 64 rows:
+//      phase A: S = Q K^T and dP = dO V^T (K, V held as B operands in
+//               AGPRs; Q, dO row fragments read from LDS);
+//      phase B: dV^T += dO^T P^T and dK^T += Q^T dS^T (P^T, dS^T straight
+//               from the phase-A accumulators of the previous tile; dO^T,
+//               Q^T read transposed from the row-major tiles), with the
+//               VALU computing P = 2^(s c - lse2) and dS = P (dP - D) of
+//               the current tile between the MFMAs.
+//    Q, dO, lse2 and D tiles arrive by LDS DMA one tile ahead into three
+//    buffers; Q and dO are unpadded with XOR-swizzled 16-byte chunks.
 // ---------------------------------------------------------------------------
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int BC = 32 * NW;           // keys per work-group (32 per wave)
-  constexpr int BR = 64;                // queries per tile
-  constexpr int T = NW * 64;
-  constexpr int DCH = D / 8;
-  constexpr int QP = D + 8;             // row-major tile pitch (bf16)
-  constexpr int TP = BR + 8;            // transposed tile pitch (bf16)
-  constexpr int RS = BR * QP;
-  constexpr int TS = D * TP;
-  constexpr int UNITS = (BR / 4) * DCH; // 4 rows x 8 columns per unit
-  constexpr int UPT = (UNITS + T - 1) / T;
-  constexpr int STAGE_H = 2 * (RS + TS);            // Qs | Qt | dOs | dOt (bf16)
-  constexpr int STAGE_BYTES = STAGE_H * 2 + 2 * BR * 4;  // + lse2[BR], dsum[BR] (fp32)
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE_BYTES];
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int NW = 4, T = NW * 64, BC = 32 * NW, BR = 64;
+  constexpr int DCH = D / 8, TS = BR * D;  // Q or dO tile (bf16 elements)
+  constexpr int PER = BR * DCH / T;        // 16-byte DMA loads per lane per tile and tensor
+  constexpr int NK = D / 16;               // d-steps of S and dP
+  constexpr int NA = 4 * NK;               // phase-A MFMAs (S, dP) x (2 query blocks)
+  constexpr int NB = (D / 32) * 8;         // phase-B MFMAs (dV, dK) x (D/32) x (4 query chunks)
+  constexpr int BUF = 2 * TS * 2 + 2 * 1024;  // bytes per buffer: Q, dO, lse2 (1 KB slot), D (1 KB slot)
+  constexpr int RING = 8;                  // operand fragments in flight
+  __shared__ __attribute__((aligned(16))) unsigned char smem[3 * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 31, hf = lane >> 5;
   const int nq = a.nq, nk = a.nk, off = nk - nq;
   const int causal = a.causal, window = a.window;
@@ -107,31 +118,33 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int bh = item / nkt, kt = item % nkt;  // causal: low key tiles (most work) first
   const int b = bh / a.heads, h = bh % a.heads;
   const int k0 = kt * BC;
+  const int wk0 = k0 + 32 * wave;
+  const int my_k = wk0 + ql;
 
   const uint16_t *qbase = (const uint16_t *)a.q + b * a.q_sb + h * a.q_sh;
   const uint16_t *dobase = (const uint16_t *)a.dout + b * a.do_sb + h * a.do_sh;
   const uint16_t *kbase = (const uint16_t *)a.k + b * a.k_sb + h * a.k_sh;
   const uint16_t *vbase = (const uint16_t *)a.v + b * a.v_sb + h * a.v_sh;
-  const __amdgpu_buffer_rsrc_t qrs = slice_rsrc(qbase, slice_bytes(nq, a.q_st, D, 2));
-  const __amdgpu_buffer_rsrc_t dors = slice_rsrc(dobase, slice_bytes(nq, a.do_st, D, 2));
+  const i32x4 qw = buffer_words(qbase, slice_bytes(nq, a.q_st, D, 2));
+  const i32x4 dow = buffer_words(dobase, slice_bytes(nq, a.do_st, D, 2));
+  const i32x4 lw = buffer_words(a.lse2 + (int64_t)bh * nq, (uint32_t)nq * 4);
+  const i32x4 dw = buffer_words(a.dpsum + (int64_t)bh * nq, (uint32_t)nq * 4);
   const __amdgpu_buffer_rsrc_t krs = slice_rsrc(kbase, slice_bytes(nk, a.k_st, D, 2));
   const __amdgpu_buffer_rsrc_t vrs = slice_rsrc(vbase, slice_bytes(nk, a.v_st, D, 2));
   const uint32_t qst2 = (uint32_t)a.q_st * 2, dost2 = (uint32_t)a.do_st * 2;
-  const float *lse = a.lse + (int64_t)bh * nq;
-  const float *dsum = a.dpsum + (int64_t)bh * nq;
 
-  // this wave's 32 keys: B operands of S = Q K^T and dP = dO V^T
-  const int wk0 = k0 + 32 * wave;
-  const int my_k = wk0 + ql;
-  uint4 kreg[D / 16], vreg[D / 16];
+  // this wave's 32 keys: B operands of S = Q K^T and dP = dO V^T (AGPRs)
+  u32x4 kreg[NK], vreg[NK];
   {
     const uint32_t ko = (uint32_t)my_k * (uint32_t)a.k_st * 2 + hf * 16;
     const uint32_t vo = (uint32_t)my_k * (uint32_t)a.v_st * 2 + hf * 16;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      kreg[kk] = bload16(krs, ko + kk * 32);
-      vreg[kk] = bload16(vrs, vo + kk * 32);
+    for (int kk = 0; kk < NK; ++kk) {
+      kreg[kk] = vec4(bload16(krs, ko + kk * 32));
+      vreg[kk] = vec4(bload16(vrs, vo + kk * 32));
     }
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) asm volatile("s_nop 1" : "+a"(kreg[kk]), "+a"(vreg[kk]));
   }
 
   // query tiles that can see some key of this work-group
@@ -141,51 +154,34 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int it0 = q_lo / BR;
   const int it1 = q_hi > q_lo ? (q_hi + BR - 1) / BR : it0;
 
-  uint4 qu[UPT][4], du[UPT][4];
-  float lse_v = 0.f, dsum_v = 0.f;
-  auto load_tile = [&](int q0) {
-#pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int unit = tid + u * T;
-      const int g = unit / DCH, dc = unit % DCH;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        qu[u][i] = bload16(qrs, (uint32_t)(q0 + 4 * g + i) * qst2 + dc * 16);
-        du[u][i] = bload16(dors, (uint32_t)(q0 + 4 * g + i) * dost2 + dc * 16);
-      }
-    }
-    lse_v = INFINITY;  // rows past the end or without any visible key: P = 0
-    dsum_v = 0.f;
-    if (tid < BR && q0 + tid < nq) {
-      const float x = lse[q0 + tid];
-      if (x != -INFINITY) lse_v = x * kLog2e;
-      dsum_v = dsum[q0 + tid];
-    }
+  const uint32_t lds0 = lds_addr(smem);
+  auto slot = [&](int it) __attribute__((always_inline)) { return (it - it0) % 3; };
+  auto qbuf = [&](int it) __attribute__((always_inline)) { return (const uint16_t *)(smem + slot(it) * BUF); };
+  auto dobuf = [&](int it) __attribute__((always_inline)) { return qbuf(it) + TS; };
+  auto fbuf = [&](int it) __attribute__((always_inline)) {  // lse2[64] at +0, D[64] at +256 floats
+    return (const float *)(smem + slot(it) * BUF + 2 * TS * 2);
   };
-  auto store_tile = [&](int buf) {
-    uint16_t *qs = (uint16_t *)(smem + buf * STAGE_BYTES);
-    uint16_t *qt = qs + RS;
-    uint16_t *dos = qt + TS;
-    uint16_t *dot = dos + RS;
-    float *fl = (float *)(smem + buf * STAGE_BYTES + STAGE_H * 2);
+  uint32_t qgo[PER], dgo[PER];
 #pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int unit = tid + u * T;
-      if (UPT * T == UNITS || unit < UNITS) {
-        const int g = unit / DCH, dc = unit % DCH;
+  for (int i = 0; i < PER; ++i) {
+    const int sl = i * T + tid, r = sl / DCH, lc = (sl % DCH) ^ swz<D>(r);
+    qgo[i] = (uint32_t)r * qst2 + lc * 16;
+    dgo[i] = (uint32_t)r * dost2 + lc * 16;
+  }
+  auto load_tile = [&](int it) __attribute__((always_inline)) {
+    const int q0 = it * BR;
+    const uint32_t l0 = lds0 + (uint32_t)(slot(it) * BUF + wave * 1024);
+    const uint32_t gq = (uint32_t)q0 * qst2, gd = (uint32_t)q0 * dost2;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          *(uint4 *)(qs + (4 * g + i) * QP + dc * 8) = qu[u][i];
-          *(uint4 *)(dos + (4 * g + i) * QP + dc * 8) = du[u][i];
-        }
-        store_transposed_4x8(qt, TP, dc * 8, vt_group_pos(g), qu[u]);
-        store_transposed_4x8(dot, TP, dc * 8, vt_group_pos(g), du[u]);
-      }
+    for (int i = 0; i < PER; ++i) {
+      dma16_at(qw, l0 + i * T * 16, gq + qgo[i]);
+      dma16_at(dow, l0 + TS * 2 + i * T * 16, gd + dgo[i]);
     }
-    if (tid < BR) {
-      fl[tid] = lse_v;
-      fl[BR + tid] = dsum_v;
-    }
+    // 64 lse2 and 64 D values: 16 lanes of one wave each
+    if (wave == 0 && lane < 16)
+      dma16_at(lw, lds0 + (uint32_t)(slot(it) * BUF + 2 * TS * 2), (uint32_t)q0 * 4 + lane * 16);
+    if (wave == 1 && lane < 16)
+      dma16_at(dw, lds0 + (uint32_t)(slot(it) * BUF + 2 * TS * 2 + 1024), (uint32_t)q0 * 4 + lane * 16);
   };
 
   f32x16 dk[D / 32], dv[D / 32];
@@ -193,92 +189,194 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a) {
   for (int i = 0; i < D / 32; ++i) dk[i] = dv[i] = (f32x16){};
   const float c = a.scale_log2;
 
-  if (it0 < it1) {
-    load_tile(it0 * BR);
-    store_tile(0);
-  }
-  __syncthreads();
+  f32x16 s[2], dp[2];            // S and dP of the current tile, [query block]; lane = key
+  // bf16 P^T, dS^T of the previous tile, [16-query chunk]; zero before the
+  // first tile, so its products add nothing and the loop needs no branch
+  uint4 pb[4], sb[4];
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) pb[cc] = sb[cc] = (uint4){0u, 0u, 0u, 0u};
 
-  for (int it = it0; it < it1; ++it) {
-    const int buf = (it - it0) & 1;
+  // operand fragments: phase A (j < NA): j = 4 kk + 2 qb + w, w = 0: Q rows, 1: dO rows;
+  // phase B (j >= NA): j - NA = 8 db + 2 cc + w, w = 0: dO^T, 1: Q^T
+  const int kx = hf ^ swz<D>(ql);
+  auto fread = [&](int it, int j) __attribute__((always_inline)) -> uint4 {
+    if (j < NA) {
+      const int kk = j / 4, qb = (j / 2) % 2, w = j % 2;
+      const int o = (qb * 32 + ql) * D + (((2 * kk) ^ kx) << 3);
+      return w ? *(const uint4 *)(dobuf(it) + o) : *(const uint4 *)(qbuf(it) + o);
+    }
+    const int jb = j - NA, db = jb / 8, cc = (jb / 2) % 4, w = jb % 2;
+    const int o = cc * 16 * D;
+    uint2 lo, hi;
+    if (w) {
+      lo = lds_read_tr16(qbuf(it) + o + tr_off<D>(lane, db, 0));
+      hi = lds_read_tr16(qbuf(it) + o + tr_off<D>(lane, db, 1));
+    } else {
+      lo = lds_read_tr16(dobuf(it) + o + tr_off<D>(lane, db, 0));
+      hi = lds_read_tr16(dobuf(it) + o + tr_off<D>(lane, db, 1));
+    }
+    return (uint4){lo.x, lo.y, hi.x, hi.y};
+  };
+
+  // P, dS of one tile (MASK: causal / window edge); element e = 16 qb + r is
+  // query 32 qb + 8 (r / 4) + 4 hf + r % 4 of the tile
+  auto one_tile = [&](auto mask_tag, int it) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int q0 = it * BR;
-    const bool more = it + 1 < it1;
-    if (more) load_tile(q0 + BR);
-    const uint16_t *qs = (const uint16_t *)(smem + buf * STAGE_BYTES);
-    const uint16_t *qt = qs + RS;
-    const uint16_t *dos = qt + TS;
-    const uint16_t *dot = dos + RS;
-    const float *fl = (const float *)(smem + buf * STAGE_BYTES + STAGE_H * 2);
-
-    const int qmax = min(q0 + BR, nq) - 1;
-    const bool active = wk0 < nk && (!causal || wk0 <= qmax + off) &&
-                        (window <= 0 || wk0 + 31 > q0 + off - window);
-    if (active) {
-      f32x16 s[2], dp[2];
+    if (it + 1 < it1) load_tile(it + 1);
+    // phase-A fragments come from this tile, phase-B fragments from the
+    // previous one (its products are pending; before the first tile they
+    // are zero and any resident tile will do)
+    const int itp = it > it0 ? it - 1 : it;
+    auto frag = [&](int j) __attribute__((always_inline)) { return fread(j < NA ? it : itp, j); };
+    uint4 ring[RING];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        s[qb] = (f32x16){};
-        dp[qb] = (f32x16){};
-        const uint16_t *qrow = qs + (qb * 32 + ql) * QP + hf * 8;
-        const uint16_t *drow = dos + (qb * 32 + ql) * QP + hf * 8;
+    for (int j = 0; j < RING; ++j) ring[j] = frag(j);
+    const float *fl = fbuf(it);
+    // ---- phase A
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          s[qb] = mfma_bf16(*(const uint4 *)(qrow + kk * 16), kreg[kk], s[qb]);
-          dp[qb] = mfma_bf16(*(const uint4 *)(drow + kk * 16), vreg[kk], dp[qb]);
-        }
+    for (int j = 0; j < NA; ++j) {
+      const uint4 f = ring[j % RING];
+      if (j + RING < NA + NB) ring[j % RING] = frag(j + RING);
+      const int kk = j / 4, qb = (j / 2) % 2, w = j % 2;
+      if (w) {
+        if (kk == 0) mfma_v_first(dp[qb], f, vreg[0]);
+        else mfma_v(dp[qb], f, vreg[kk]);
+      } else {
+        if (kk == 0) mfma_v_first(s[qb], f, kreg[0]);
+        else mfma_v(s[qb], f, kreg[kk]);
       }
-      // accumulator layout: lane = key my_k, element r = query
-      // q0 + qb*32 + 8*(r/4) + 4*hf + r%4
-      const bool need_mask = (causal && wk0 + 31 > q0 + off) ||
-                             (window > 0 && wk0 <= qmax + off - window) || (wk0 + 32 > nk);
+    }
+    // lse2 and D of this lane's 32 query rows (4 consecutive rows per float4)
+    float4 lse4[8], d4[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const int qi = (g / 4) * 32 + 8 * (g % 4) + 4 * hf;
+      lse4[g] = *(const float4 *)(fl + qi);
+      d4[g] = *(const float4 *)(fl + 256 + qi);
+    }
+    mfma_drain2_v(s[0], s[1]);
+    mfma_drain2_v(dp[0], dp[1]);
+    if (MASK) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          const int qi = qb * 32 + 8 * rb + 4 * hf;
-          const float4 l4 = *(const float4 *)(fl + qi);
-          const float4 d4 = *(const float4 *)(fl + BR + qi);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = 4 * rb + j;
-            float p = fast_exp2(__builtin_fmaf(s[qb][r], c, -lv[j]));
-            if (need_mask) {
-              const int qpos = q0 + qi + j + off;
-              const bool ok = my_k < nk && (!causal || my_k <= qpos) && (window <= 0 || my_k > qpos - window);
-              if (!ok) p = 0.f;
-            }
-            s[qb][r] = p;
-            dp[qb][r] = p * (dp[qb][r] - dvv[j]);
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int qpos = q0 + qb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3) + off;
+          const bool ok = (!causal || my_k <= qpos) && (window <= 0 || my_k > qpos - window) &&
+                          qpos - off < nq;
+          if (!ok) s[qb][r] = -INFINITY;
         }
-      uint4 pb[BR / 16], sb[BR / 16];
-#pragma unroll
-      for (int cc = 0; cc < BR / 16; ++cc) {
-        const int qb = cc >> 1, r0 = (cc & 1) * 8;
-        pb[cc].x = pack_bf16x2(s[qb][r0 + 0], s[qb][r0 + 1]);
-        pb[cc].y = pack_bf16x2(s[qb][r0 + 2], s[qb][r0 + 3]);
-        pb[cc].z = pack_bf16x2(s[qb][r0 + 4], s[qb][r0 + 5]);
-        pb[cc].w = pack_bf16x2(s[qb][r0 + 6], s[qb][r0 + 7]);
-        sb[cc].x = pack_bf16x2(dp[qb][r0 + 0], dp[qb][r0 + 1]);
-        sb[cc].y = pack_bf16x2(dp[qb][r0 + 2], dp[qb][r0 + 3]);
-        sb[cc].z = pack_bf16x2(dp[qb][r0 + 4], dp[qb][r0 + 5]);
-        sb[cc].w = pack_bf16x2(dp[qb][r0 + 6], dp[qb][r0 + 7]);
-      }
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const uint16_t *drow = dot + (db * 32 + ql) * TP + hf * 8;
-        const uint16_t *qrow = qt + (db * 32 + ql) * TP + hf * 8;
-#pragma unroll
-        for (int cc = 0; cc < BR / 16; ++cc) {
-          dv[db] = mfma_bf16(*(const uint4 *)(drow + cc * 16), pb[cc], dv[db]);
-          dk[db] = mfma_bf16(*(const uint4 *)(qrow + cc * 16), sb[cc], dk[db]);
-        }
-      }
     }
-    if (more) store_tile(buf ^ 1);
+    // ---- phase B: the previous tile's products, this tile's P and dS
+    constexpr int EPS = 32 / NB;  // elements started per stage
+    static_assert(EPS * NB == 32, "stages must divide the lane's 32 elements");
+    auto comp = [](const float4 &v, int i) __attribute__((always_inline)) {
+      return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+    };
+    // element e = 16 qb + r; its query row's lse2 / D sit in lse4 / d4[e / 4]
+    auto elem_fma = [&](int e) __attribute__((always_inline)) {
+      s[e / 16][e % 16] = __builtin_fmaf(s[e / 16][e % 16], c, -comp(lse4[e / 4], e % 4));
+    };
+    auto elem_exp = [&](int e) __attribute__((always_inline)) { s[e / 16][e % 16] = fast_exp2(s[e / 16][e % 16]); };
+    auto elem_ds = [&](int e) __attribute__((always_inline)) {
+      dp[e / 16][e % 16] = s[e / 16][e % 16] * (dp[e / 16][e % 16] - comp(d4[e / 4], e % 4));
+    };
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int jj = NA + j;
+      const uint4 f = ring[jj % RING];
+      if (jj + RING < NA + NB) ring[jj % RING] = frag(jj + RING);
+      {
+        const int db = j / 8, cc = (j / 2) % 4, w = j % 2;
+        if (j == 0) asm volatile("s_nop 1");
+        if (w) mfma_a(dk[db], f, sb[cc]);
+        else mfma_a(dv[db], f, pb[cc]);
+      }
+      // element pipeline over the 32 elements of the lane, EPS per stage:
+      // fma at stage e / EPS, exp one stage later, dS two stages later
+#pragma unroll
+      for (int k = 0; k < EPS; ++k) {
+        if (j * EPS + k < 32) elem_fma(j * EPS + k);
+        if (j >= 1) elem_exp((j - 1) * EPS + k);
+        if (j >= 2) elem_ds((j - 2) * EPS + k);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // tail of the element pipeline
+#pragma unroll
+    for (int k = 0; k < EPS; ++k) {
+      elem_exp((NB - 1) * EPS + k);
+      elem_ds((NB - 2) * EPS + k);
+      elem_ds((NB - 1) * EPS + k);
+    }
+    // the phase-B MFMAs above have read pb / sb (operands are read at issue)
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const int qb = cc >> 1, r0 = (cc & 1) * 8;
+      uint4 &p = pb[cc], &d = sb[cc];
+      p.x = pack_bf16x2(s[qb][r0 + 0], s[qb][r0 + 1]);
+      p.y = pack_bf16x2(s[qb][r0 + 2], s[qb][r0 + 3]);
+      p.z = pack_bf16x2(s[qb][r0 + 4], s[qb][r0 + 5]);
+      p.w = pack_bf16x2(s[qb][r0 + 6], s[qb][r0 + 7]);
+      d.x = pack_bf16x2(dp[qb][r0 + 0], dp[qb][r0 + 1]);
+      d.y = pack_bf16x2(dp[qb][r0 + 2], dp[qb][r0 + 3]);
+      d.z = pack_bf16x2(dp[qb][r0 + 4], dp[qb][r0 + 5]);
+      d.w = pack_bf16x2(dp[qb][r0 + 6], dp[qb][r0 + 7]);
+    }
+    wait_dma();
     __syncthreads();
+    // the compiler may move accumulators at loop boundaries: only after the
+    // last MFMA has finished
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) asm volatile("" : "+a"(dk[i]), "+a"(dv[i]));
+    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) asm volatile("" : "+a"(dk[i]), "+a"(dv[i]));
+  };
+
+  // tiles [it0, ia) are cut by the causal diagonal, [ib, it1) by the window
+  // or the end of the queries; the rest see every key of the work-group
+  int ia = it0, ib = it1;
+  if (causal) {
+    const int lim = k0 + BC - 1 - off;  // first query row that sees all keys
+    ia = min(it1, max(it0, (lim + BR - 1) / BR));
+  }
+  if (window > 0) {
+    const int lim = k0 - off + window;  // rows >= lim lose the first key
+    ib = max(ia, min(it1, lim / BR));
+  }
+  if (it1 * BR > nq) ib = max(ia, min(ib, it1 - 1));
+
+  if (it0 < it1) load_tile(it0);
+  wait_dma();
+  __syncthreads();
+  const std::true_type masked;
+  const std::false_type whole;
+  for (int it = it0; it < ia; ++it) one_tile(masked, it);
+  for (int it = ia; it < ib; ++it) one_tile(whole, it);
+  for (int it = ib; it < it1; ++it) one_tile(masked, it);
+  // the last tile's products
+  if (it0 < it1) {
+    const int it = it1 - 1;
+    uint4 ring[RING];
+#pragma unroll
+    for (int j = 0; j < RING; ++j) ring[j] = fread(it, NA + j);
+    asm volatile("s_nop 1");
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const uint4 f = ring[j % RING];
+      if (j + RING < NB) ring[j % RING] = fread(it, NA + j + RING);
+      const int db = j / 8, cc = (j / 2) % 4, w = j % 2;
+      if (w) mfma_a(dk[db], f, sb[cc]);
+      else mfma_a(dv[db], f, pb[cc]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    mfma_drain_a(dk[i]);
+    mfma_drain_a(dv[i]);
   }
 
   // dK = scale * (dS^T Q), dV = P^T dO; lane = key, d = db*32 + 8*rb + 4*hf + 0..3
@@ -496,7 +594,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
 
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t s) {
-  constexpr int NW_KV = 4, NW_Q = 8;
+  constexpr int NW_KV = 4, NW_Q = 8;  // bwd_dkdv_kernel uses 4 waves
   const int64_t rows = (int64_t)a.batch * a.heads * a.nq;
   if (rows > 0) {
     constexpr int RPB = 256 / (D / 8);
@@ -504,7 +602,7 @@ hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t s) {
   }
   const int64_t kv_items = (int64_t)((a.nk + 32 * NW_KV - 1) / (32 * NW_KV)) * a.heads * a.batch;
   if (kv_items > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW_KV>), dim3((unsigned)kv_items), dim3(NW_KV * 64), 0, s, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)kv_items), dim3(NW_KV * 64), 0, s, a);
   const int64_t q_items = (int64_t)((a.nq + 32 * NW_Q - 1) / (32 * NW_Q)) * a.heads * a.batch;
   if (q_items > 0)
     hipLaunchKernelGGL((bwd_dq_kernel<D, NW_Q>), dim3((unsigned)q_items), dim3(NW_Q * 64), 0, s, a);
@@ -516,7 +614,8 @@ hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t s) {
 size_t bwd_workspace_bytes(int batch, int heads, int nq, int head_dim, int deterministic) {
   (void)head_dim;
   (void)deterministic;
-  return ((size_t)batch * heads * nq * sizeof(float) + 255) / 256 * 256;
+  // D and LSE * log2(e), each [batch, heads, nq] fp32 rounded up to 256 bytes
+  return 2 * (((size_t)batch * heads * nq * sizeof(float) + 255) / 256 * 256);
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs &a, int head_dim, hipStream_t s) {

@@ -33,7 +33,7 @@ struct BwdArgs {
   const float *lse;
   void *dq, *dk, *dv;
   float *dpsum;      // workspace: D_i = rowsum(dO * O), [batch, heads, nq] fp32
-  float *dq_accum;   // workspace: fp32 dQ accumulator [batch, heads, nq, d] (atomic mode)
+  float *lse2;       // workspace: LSE_i * log2(e) (+inf for rows that see no key), same shape
   int64_t q_sb, q_st, q_sh, k_sb, k_st, k_sh, v_sb, v_st, v_sh, o_sb, o_st, o_sh;
   int64_t do_sb, do_st, do_sh, dq_sb, dq_st, dq_sh, dk_sb, dk_st, dk_sh, dv_sb, dv_st, dv_sh;
   int32_t batch, heads, nq, nk;

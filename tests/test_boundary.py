@@ -137,7 +137,7 @@ def test_bwd_checks(lib):
     lse = torch.zeros(1, 2, 16, dtype=torch.float32)
     p = B.make_bwd_params(q, q, q, q, q, lse, g, g, g, causal=True)
     assert lib.fa_check_bwd(ctypes.byref(p)) == B.FA_OK
-    assert lib.fa_bwd_workspace_bytes(ctypes.byref(p)) == 256  # D: 1*2*16 fp32, rounded to 256 bytes
+    assert lib.fa_bwd_workspace_bytes(ctypes.byref(p)) == 512  # D and LSE*log2(e): 1*2*16 fp32 each, rounded to 256 bytes
     p.qkv_dtype = B.FA_FP8_E4M3
     assert lib.fa_check_bwd(ctypes.byref(p)) == B.FA_ERR_UNSUPPORTED
     p = B.make_bwd_params(q, q, q, q, q, lse, g, g, g)

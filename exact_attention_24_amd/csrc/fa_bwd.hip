@@ -398,26 +398,33 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ: query-tile outer, key-tile inner
+// 3. dQ: query-tile outer, key-tile inner.  One work-group of 4 waves per
+//    256 queries (64 per wave, two blocks of 32, one wave per SIMD); key
+//    tiles of 64 arrive by LDS DMA one tile ahead (three buffers each for K
+//    and V, unpadded, XOR-swizzled) and are processed as two sub-tiles of 32.
+//    Per sub-tile u:
+//      phase A: S^T = K Q^T and dP^T = V dO^T for both query blocks (each K
+//               or V row fragment feeds two MFMAs; Q^T, dO^T are B operands
+//               held in AGPRs; lane = query, so LSE and D are per-lane
+//               scalars), with the VALU turning S, dP of sub-tile u-1 into
+//               dS = 2^(s c - lse2) (dP - D) and packing it to bf16;
+//      phase B: dQ^T += K^T dS^T for sub-tile u-1 (K^T read transposed from
+//               the row-major K tile, in the key order of the dS^T operand).
+//    dQ is written once, no atomics.
 // ---------------------------------------------------------------------------
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int BC = 64;                // keys per tile
-  constexpr int BR = 32 * NW;           // queries per work-group
-  constexpr int T = NW * 64;
-  constexpr int DCH = D / 8;
-  constexpr int KP = D + 8;
-  constexpr int TP = BC + 8;
-  constexpr int KS = BC * KP;
-  constexpr int TS = D * TP;
-  constexpr int STAGE = 2 * KS + TS;    // Ks | Vs | Kt (bf16)
-  constexpr int KUNITS = (BC / 4) * DCH;
-  constexpr int KU = (KUNITS + T - 1) / T;
-  constexpr int VCH = (BC * DCH + T - 1) / T;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int NW = 4, T = NW * 64, QW = 64, BR = NW * QW, BC = 64;
+  constexpr int DCH = D / 8, TS = BC * D;
+  constexpr int PER = BC * DCH / T;  // DMA loads per lane per tile and tensor
+  constexpr int NK = D / 16;         // d-steps of S and dP (fragments per sub-tile and tensor)
+  constexpr int NA = 2 * NK;         // phase-A fragments per sub-tile (K, V interleaved)
+  constexpr int NF = (D / 32) * 2;   // phase-B K^T fragments per sub-tile
+  constexpr int RING = 6;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[6 * TS];  // K x3, V x3
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 31, hf = lane >> 5;
   const int nq = a.nq, nk = a.nk, off = nk - nq;
   const int causal = a.causal, window = a.window;
@@ -435,8 +442,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
   const uint16_t *vbase = (const uint16_t *)a.v + b * a.v_sb + h * a.v_sh;
   const __amdgpu_buffer_rsrc_t qrs = slice_rsrc(qbase, slice_bytes(nq, a.q_st, D, 2));
   const __amdgpu_buffer_rsrc_t dors = slice_rsrc(dobase, slice_bytes(nq, a.do_st, D, 2));
-  const __amdgpu_buffer_rsrc_t krs = slice_rsrc(kbase, slice_bytes(nk, a.k_st, D, 2));
-  const __amdgpu_buffer_rsrc_t vrs = slice_rsrc(vbase, slice_bytes(nk, a.v_st, D, 2));
+  const i32x4 kw = buffer_words(kbase, slice_bytes(nk, a.k_st, D, 2));
+  const i32x4 vw = buffer_words(vbase, slice_bytes(nk, a.v_st, D, 2));
   const uint32_t kst2 = (uint32_t)a.k_st * 2, vst2 = (uint32_t)a.v_st * 2;
 
   const int p_lo = q0 + off, p_hi = min(q0 + BR, nq) - 1 + off;
@@ -446,155 +453,273 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
   const int jt0 = kv_lo / BC;
   const int jt1 = kv_hi > kv_lo ? (kv_hi + BC - 1) / BC : jt0;
 
-  const int wq0 = q0 + 32 * wave;
+  const int wq0 = q0 + QW * wave;
   const bool wave_rows = wq0 < nq;
-  const int wp_lo = wq0 + off, wp_hi = min(wq0 + 31, nq - 1) + off;
-  const int my_q = wq0 + ql;
-  const int my_p = my_q + off;
-
-  uint4 qreg[D / 16], doreg[D / 16];
-  {
-    const uint32_t qo = (uint32_t)my_q * (uint32_t)a.q_st * 2 + hf * 16;
-    const uint32_t dqo = (uint32_t)my_q * (uint32_t)a.do_st * 2 + hf * 16;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      qreg[kk] = bload16(qrs, qo + kk * 32);
-      doreg[kk] = bload16(dors, dqo + kk * 32);
-    }
-  }
-  float lse2 = INFINITY, dsum = 0.f;  // rows past the end or without visible keys: P = 0
-  if (my_q < nq) {
-    const float x = a.lse[(int64_t)bh * nq + my_q];
-    if (x != -INFINITY) lse2 = x * kLog2e;
-    dsum = a.dpsum[(int64_t)bh * nq + my_q];
-  }
-
-  uint4 ku[KU][4], vr[VCH];
-  auto load_tile = [&](int k0) {
-#pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int unit = tid + u * T;
-      const int g = unit / DCH, dc = unit % DCH;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ku[u][i] = bload16(krs, (uint32_t)(k0 + 4 * g + i) * kst2 + dc * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int cidx = tid + i * T;
-      const int row = cidx / DCH, col = cidx % DCH;
-      vr[i] = bload16(vrs, (uint32_t)(k0 + row) * vst2 + col * 16);
-    }
+  const int wp_lo = wq0 + off, wp_hi = min(wq0 + QW - 1, nq - 1) + off;
+  auto active = [&](int k0) __attribute__((always_inline)) {  // 32 keys from k0
+    return wave_rows && (!causal || k0 <= wp_hi) && (window <= 0 || k0 + 31 > wp_lo - window);
   };
-  auto store_tile = [&](int buf) {
-    uint16_t *ks = smem + buf * STAGE;
-    uint16_t *vs = ks + KS;
-    uint16_t *kt = vs + KS;
+
+  const uint32_t lds0 = lds_addr(smem);
+  auto slot = [&](int jt) __attribute__((always_inline)) { return (jt - jt0) % 3; };
+  auto kbuf = [&](int jt) __attribute__((always_inline)) { return smem + slot(jt) * TS; };
+  auto vbuf = [&](int jt) __attribute__((always_inline)) { return smem + (3 + slot(jt)) * TS; };
+  uint32_t kgo[PER], vgo[PER];
 #pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int unit = tid + u * T;
-      if (KU * T == KUNITS || unit < KUNITS) {
-        const int g = unit / DCH, dc = unit % DCH;
+  for (int i = 0; i < PER; ++i) {
+    const int sl = i * T + tid, r = sl / DCH, lc = (sl % DCH) ^ swz<D>(r);
+    kgo[i] = (uint32_t)r * kst2 + lc * 16;
+    vgo[i] = (uint32_t)r * vst2 + lc * 16;
+  }
+  auto load_kv = [&](int jt) __attribute__((always_inline)) {
+    const uint32_t gk = (uint32_t)(jt * BC) * kst2, gv = (uint32_t)(jt * BC) * vst2;
+    const uint32_t lk = lds0 + (uint32_t)(slot(jt) * TS * 2 + wave * 1024);
+    const uint32_t lv = lds0 + (uint32_t)((3 + slot(jt)) * TS * 2 + wave * 1024);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *(uint4 *)(ks + (4 * g + i) * KP + dc * 8) = ku[u][i];
-        store_transposed_4x8(kt, TP, dc * 8, vt_group_pos(g), ku[u]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int cidx = tid + i * T;
-      if (VCH * T == BC * DCH || cidx < BC * DCH) {
-        const int row = cidx / DCH, col = cidx % DCH;
-        *(uint4 *)(vs + row * KP + col * 8) = vr[i];
-      }
+    for (int i = 0; i < PER; ++i) {
+      dma16_at(kw, lk + i * T * 16, gk + kgo[i]);
+      dma16_at(vw, lv + i * T * 16, gv + vgo[i]);
     }
   };
 
-  f32x16 acc[D / 32];
+  // Q^T and dO^T of both query blocks: B operands for the whole loop (AGPRs)
+  u32x4 qreg[2][NK], doreg[2][NK];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
+  for (int qb = 0; qb < 2; ++qb) {
+    const uint32_t r = (uint32_t)(wq0 + 32 * qb + ql);
+    const uint32_t qo = r * (uint32_t)a.q_st * 2 + hf * 16, dqo = r * (uint32_t)a.do_st * 2 + hf * 16;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      qreg[qb][kk] = vec4(bload16(qrs, qo + kk * 32));
+      doreg[qb][kk] = vec4(bload16(dors, dqo + kk * 32));
+    }
+  }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) asm volatile("s_nop 1" : "+a"(qreg[qb][kk]), "+a"(doreg[qb][kk]));
+  // per-lane LSE*log2(e) and D of the lane's two query rows
+  float lse2[2], dsum[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int my_q = wq0 + 32 * qb + ql;
+    lse2[qb] = INFINITY;  // rows past the end: P = 0
+    dsum[qb] = 0.f;
+    if (my_q < nq) {
+      lse2[qb] = a.lse2[(int64_t)bh * nq + my_q];
+      dsum[qb] = a.dpsum[(int64_t)bh * nq + my_q];
+    }
+  }
+
+  f32x16 acc[2][D / 32];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) acc[qb][i] = (f32x16){};
   const float c = a.scale_log2;
-
-  if (jt0 < jt1) {
-    load_tile(jt0 * BC);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int jt = jt0; jt < jt1; ++jt) {
-    const int buf = (jt - jt0) & 1;
-    const int k0 = jt * BC;
-    const bool more = jt + 1 < jt1;
-    if (more) load_tile(k0 + BC);
-    const uint16_t *ks = smem + buf * STAGE;
-    const uint16_t *vs = ks + KS;
-    const uint16_t *kt = vs + KS;
-
-    const bool active = wave_rows && (!causal || k0 <= wp_hi) &&
-                        (window <= 0 || k0 + BC - 1 > wp_lo - window);
-    if (active) {
-      f32x16 s[2], dp[2];
+  f32x16 s[2], dp[2];          // [query block]: S^T then P; dP^T then dS; lane = query
+  uint4 sb[2][2];              // bf16 dS^T of the pending sub-tile, [query block][16-key half]
+  const uint16_t *k_p = smem;  // K rows of the pending sub-tile
+  // the pending sub-tile before the first one has dS = 0
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = (f32x16){};
-        dp[kb] = (f32x16){};
-        const uint16_t *krow = ks + (kb * 32 + ql) * KP + hf * 8;
-        const uint16_t *vrow = vs + (kb * 32 + ql) * KP + hf * 8;
+  for (int qb = 0; qb < 2; ++qb) dp[qb] = (f32x16){};
+
+  const int kx = hf ^ swz<D>(ql);
+  // phase-A fragment kk of sub-tile (jt, kb): K rows (S) or V rows (dP)
+  auto kread = [&](int jt, int kb, int kk) __attribute__((always_inline)) -> uint4 {
+    return *(const uint4 *)(kbuf(jt) + (kb * 32 + ql) * D + (((2 * kk) ^ kx) << 3));
+  };
+  auto vread = [&](int jt, int kb, int kk) __attribute__((always_inline)) -> uint4 {
+    return *(const uint4 *)(vbuf(jt) + (kb * 32 + ql) * D + (((2 * kk) ^ kx) << 3));
+  };
+  // phase-B fragment f = (db = f / 2, h2 = f % 2) of K^T for the 32 K rows at ks
+  auto bread = [&](const uint16_t *ks, int f) __attribute__((always_inline)) -> uint4 {
+    const uint16_t *kp = ks + (f % 2) * 16 * D;
+    const uint2 lo = lds_read_tr16(kp + tr_off<D>(lane, f / 2, 0));
+    const uint2 hi = lds_read_tr16(kp + tr_off<D>(lane, f / 2, 1));
+    return (uint4){lo.x, lo.y, hi.x, hi.y};
+  };
+  // element e of query block qb is key 8 (e / 4) + 4 hf + e % 4 of the sub-tile
+  auto pack_ds = [&](int qb, int h2) __attribute__((always_inline)) {
+    const int r0 = h2 * 8;
+    uint4 &w = sb[qb][h2];
+    w.x = pack_bf16x2(dp[qb][r0 + 0], dp[qb][r0 + 1]);
+    w.y = pack_bf16x2(dp[qb][r0 + 2], dp[qb][r0 + 3]);
+    w.z = pack_bf16x2(dp[qb][r0 + 4], dp[qb][r0 + 5]);
+    w.w = pack_bf16x2(dp[qb][r0 + 6], dp[qb][r0 + 7]);
+    asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));  // keep the work in its stage
+  };
+
+  auto sub = [&](auto mask_tag, int jt, int kb) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int k0 = jt * BC + kb * 32;
+    const bool act = !MASK || active(k0);
+    // ---- S MFMAs; meanwhile dS of the pending sub-tile is packed to bf16
+    if (act) {
+      uint4 ring[RING];
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          s[kb] = mfma_bf16(*(const uint4 *)(krow + kk * 16), qreg[kk], s[kb]);
-          dp[kb] = mfma_bf16(*(const uint4 *)(vrow + kk * 16), doreg[kk], dp[kb]);
+      for (int j = 0; j < RING; ++j) ring[j] = kread(jt, kb, j);
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const uint4 f = ring[kk % RING];
+        if (kk + RING < NK) ring[kk % RING] = kread(jt, kb, kk + RING);
+        if (kk == 0) {
+          mfma_v_first(s[0], f, qreg[0][0]);
+          mfma_v_first(s[1], f, qreg[1][0]);
+        } else {
+          mfma_v(s[0], f, qreg[0][kk]);
+          mfma_v(s[1], f, qreg[1][kk]);
         }
+        constexpr int PK = NK / 4;
+        if (kk % PK == PK - 1) pack_ds((kk / PK) / 2, (kk / PK) % 2);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      const bool need_mask = (causal && k0 + BC - 1 > wp_lo) ||
-                             (window > 0 && k0 <= wp_hi - window) || (k0 + BC > nk);
+      mfma_drain2_v(s[0], s[1]);
+    } else {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int part = 0; part < 4; ++part) pack_ds(part / 2, part % 2);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(__builtin_fmaf(s[kb][r], c, -lse2));
-          if (need_mask) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            const bool ok = key < nk && (!causal || key <= my_p) && (window <= 0 || key > my_p - window);
-            if (!ok) p = 0.f;
-          }
-          dp[kb][r] = p * (dp[kb][r] - dsum);
+      for (int e = 0; e < 16; ++e) s[0][e] = s[1][e] = -INFINITY;
+    }
+    if (MASK) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int my_p = wq0 + 32 * qb + ql + off;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = k0 + 8 * (e >> 2) + 4 * hf + (e & 3);
+          const bool ok = (!causal || key <= my_p) && (window <= 0 || key > my_p - window);
+          if (!ok) s[qb][e] = -INFINITY;
         }
-      uint4 sb[4];
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        const int kb = cc >> 1, r0 = (cc & 1) * 8;
-        sb[cc].x = pack_bf16x2(dp[kb][r0 + 0], dp[kb][r0 + 1]);
-        sb[cc].y = pack_bf16x2(dp[kb][r0 + 2], dp[kb][r0 + 3]);
-        sb[cc].z = pack_bf16x2(dp[kb][r0 + 4], dp[kb][r0 + 5]);
-        sb[cc].w = pack_bf16x2(dp[kb][r0 + 6], dp[kb][r0 + 7]);
-      }
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const uint16_t *trow = kt + (db * 32 + ql) * TP + hf * 8;
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) acc[db] = mfma_bf16(*(const uint4 *)(trow + cc * 16), sb[cc], acc[db]);
       }
     }
-    if (more) store_tile(buf ^ 1);
+    // ---- dP MFMAs; meanwhile P = 2^(s c - lse2) in place
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      uint4 ring[RING];
+      if (act) {
+#pragma unroll
+        for (int j = 0; j < RING; ++j) ring[j] = vread(jt, kb, j);
+      }
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        if (act) {
+          const uint4 f = ring[kk % RING];
+          if (kk + RING < NK) ring[kk % RING] = vread(jt, kb, kk + RING);
+          if (kk == 0) {
+            mfma_v_first(dp[0], f, doreg[0][0]);
+            mfma_v_first(dp[1], f, doreg[1][0]);
+          } else {
+            mfma_v(dp[0], f, doreg[0][kk]);
+            mfma_v(dp[1], f, doreg[1][kk]);
+          }
+        }
+        constexpr int EPS = 32 / NK;
+#pragma unroll
+        for (int k = 0; k < EPS; ++k) {
+          const int e = kk * EPS + k, qb = e / 16, r = e % 16;
+          s[qb][r] = fast_exp2(__builtin_fmaf(s[qb][r], c, -lse2[qb]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (act) mfma_drain2_v(dp[0], dp[1]);
+    }
+    // ---- dQ^T += K^T dS^T of the pending sub-tile; meanwhile dS = P (dP - D)
+    {
+      uint4 ring[RING];
+#pragma unroll
+      for (int j = 0; j < RING; ++j) ring[j] = bread(k_p, j);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const uint4 kf = ring[f % RING];
+        if (f + RING < NF) ring[f % RING] = bread(k_p, f + RING);
+        mfma_a(acc[0][f / 2], kf, sb[0][f % 2]);
+        mfma_a(acc[1][f / 2], kf, sb[1][f % 2]);
+        constexpr int EPS = 32 / NF;
+#pragma unroll
+        for (int k = 0; k < EPS; ++k) {
+          const int e = f * EPS + k, qb = e / 16, r = e % 16;
+          if (act) dp[qb][r] = s[qb][r] * (dp[qb][r] - dsum[qb]);
+          else dp[qb][r] = 0.f;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    k_p = kbuf(jt) + kb * 32 * D;
+  };
+  auto step = [&](auto mask_tag, int jt) __attribute__((always_inline)) {
+    if (jt + 1 < jt1) load_kv(jt + 1);
+    sub(mask_tag, jt, 0);
+    sub(mask_tag, jt, 1);
+    wait_dma();
     __syncthreads();
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) asm volatile("" : "+a"(acc[qb][i]));
+    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) asm volatile("" : "+a"(acc[qb][i]));
+  };
+
+  int ja = jt0, jb = jt1;
+  if (window > 0) {
+    const int lim = p_hi - window;
+    ja = lim >= 0 ? min(jt1, max(jt0, lim / BC + 1)) : jt0;
   }
+  if (causal) {
+    const int lim = p_lo - (BC - 1);
+    jb = lim >= 0 ? max(ja, min(jt1, lim / BC + 1)) : ja;
+  }
+
+  if (jt0 < jt1) load_kv(jt0);
+  wait_dma();
+  __syncthreads();
+  k_p = kbuf(jt0);
+  const std::true_type masked;
+  const std::false_type whole;
+  for (int jt = jt0; jt < ja; ++jt) step(masked, jt);
+  for (int jt = ja; jt < jb; ++jt) step(whole, jt);
+  for (int jt = jb; jt < jt1; ++jt) step(masked, jt);
+  if (jt0 < jt1) {
+    // the last sub-tile's product
+#pragma unroll
+    for (int part = 0; part < 4; ++part) pack_ds(part / 2, part % 2);
+    asm volatile("s_nop 1");
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const uint4 kf = bread(k_p, f);
+      mfma_a(acc[0][f / 2], kf, sb[0][f % 2]);
+      mfma_a(acc[1][f / 2], kf, sb[1][f % 2]);
+    }
+  }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) mfma_drain_a(acc[qb][i]);
 
   // dQ = scale * dS K; lane = query, d = db*32 + 8*rb + 4*hf + 0..3
-  if (my_q < nq) {
-    const float sc = a.scale;
-    const int64_t ro = b * a.dq_sb + (int64_t)my_q * a.dq_st + h * a.dq_sh;
+  const float sc = a.scale;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int qb = 0; qb < 2; ++qb) {
+    const int my_q = wq0 + 32 * qb + ql;
+    if (my_q < nq) {
+      const int64_t ro = b * a.dq_sb + (int64_t)my_q * a.dq_st + h * a.dq_sh;
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-        store_grad4(a.dq, ro + db * 32 + 8 * rb + 4 * hf, a.grad_f32, sc * acc[db][4 * rb],
-                    sc * acc[db][4 * rb + 1], sc * acc[db][4 * rb + 2], sc * acc[db][4 * rb + 3]);
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+          store_grad4(a.dq, ro + db * 32 + 8 * rb + 4 * hf, a.grad_f32, sc * acc[qb][db][4 * rb],
+                      sc * acc[qb][db][4 * rb + 1], sc * acc[qb][db][4 * rb + 2], sc * acc[qb][db][4 * rb + 3]);
+    }
   }
 }
 
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t s) {
-  constexpr int NW_KV = 4, NW_Q = 8;  // bwd_dkdv_kernel uses 4 waves
+  constexpr int NW_KV = 4;
   const int64_t rows = (int64_t)a.batch * a.heads * a.nq;
   if (rows > 0) {
     constexpr int RPB = 256 / (D / 8);
@@ -603,9 +728,8 @@ hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t s) {
   const int64_t kv_items = (int64_t)((a.nk + 32 * NW_KV - 1) / (32 * NW_KV)) * a.heads * a.batch;
   if (kv_items > 0)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)kv_items), dim3(NW_KV * 64), 0, s, a);
-  const int64_t q_items = (int64_t)((a.nq + 32 * NW_Q - 1) / (32 * NW_Q)) * a.heads * a.batch;
-  if (q_items > 0)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, NW_Q>), dim3((unsigned)q_items), dim3(NW_Q * 64), 0, s, a);
+  const int64_t q_items = (int64_t)((a.nq + 256 - 1) / 256) * a.heads * a.batch;
+  if (q_items > 0) hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)q_items), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -13,8 +13,9 @@
 // owns one query (lane % 32) and 16 keys of each 32-key block, and its 32
 // P~ values of a 64-key tile form the B operand of one K=64 product.  The V
 // tile is stored transposed in LDS with its keys in exactly that order.
-// P is quantised without a scale: the probabilities are <= 1 and e4m3 keeps
-// 3 mantissa bits down to 2^-6 (subnormals to 2^-9).
+// P~ is quantised without a scale: it is <= 2^8 (the running max lags the
+// true one by at most 8 in log2 units) and e4m3 keeps 3 mantissa bits from
+// 2^-6 up to 448 (subnormals to 2^-9).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -211,11 +212,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx * c);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_use);
-      m = m_new;
+      mx = half_swap_max(mx) * c;
+      // the running max moves only when a row max jumps by more than 2^8
+      // (P~ <= 256 stays inside e4m3's range of 448), so the accumulators
+      // are rescaled only then
+      const bool up = mx > m + 8.f;
+      const float alpha = up ? fast_exp2(m - mx) : 1.f;
+      m = up ? mx : m;
+      const float m_use = m == -INFINITY ? 0.f : m;
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -227,8 +231,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdArgs a) {
         }
       l = l * alpha + rs;
       if (__ballot(alpha != 1.f)) {
+        float a_r = alpha;
+        asm volatile("" : "+v"(a_r));  // keep the multiplies inside this branch
 #pragma unroll
-        for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+        for (int i = 0; i < D / 32; ++i) acc[i] *= a_r;
       }
       // B operand bytes b = 0..31 <- (kb, r) = (b / 16, b % 16)
       uint4 pb0, pb1;

@@ -12,7 +12,10 @@
 // accumulator has the same 32x32 layout as the bf16 one, so each lane again
 // owns one query (lane % 32) and 16 keys of each 32-key block, and its 32
 // P~ values of a 64-key tile form the B operand of one K=64 product.  The V
-// tile is stored transposed in LDS with its keys in exactly that order.
+// tile is stored row-major; its V^T operand comes from 8-bit transposed LDS
+// reads whose source rows follow exactly that key order.  As in the bf16
+// kernel, the product of tile j-1 is issued between the softmax stages of
+// tile j.
 // P~ is quantised without a scale: it is <= 2^8 (the running max lags the
 // true one by at most 8 in log2 units) and e4m3 keeps 3 mantissa bits from
 // 2^-6 up to 448 (subnormals to 2^-9).
@@ -45,29 +48,45 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float x0, float x1, float x2, flo
   return (uint32_t)w;
 }
 
-__device__ __forceinline__ uint32_t u8_at(const uint4 &v, int e) {
-  const uint32_t w = e < 4 ? v.x : e < 8 ? v.y : e < 12 ? v.z : v.w;
-  return (w >> (8 * (e & 3))) & 0xffu;
+// 8-byte transposed LDS read (ds_read_b64_tr_b8): within each 16-lane group,
+// output lane l receives byte (l % 8) of the 8-byte chunks addressed by the
+// source lanes (l % 16) / 8 + 2 j, j = 0..7, in that order.
+__device__ __forceinline__ uint2 lds_read_tr8(const uint8_t *p) {
+  typedef int i32x2 __attribute__((ext_vector_type(2)));
+  const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2 *)(p));
+  return (uint2){(uint32_t)r.x, (uint32_t)r.y};
 }
 
-// Position of key group g (keys 4g..4g+3 of a 64-key tile) in a transposed V
-// row: lane half hf's 32 B-operand bytes are the accumulator entries
-// (kb, r) = (b / 16, b % 16), i.e. key 32 kb + 8 (r / 4) + 4 hf + r % 4.
-__device__ __forceinline__ int vt8_group_pos(int g) {
-  return 32 * (g & 1) + 16 * (g >> 3) + 4 * ((g & 7) >> 1);
+// V tiles (64 keys x D bytes) are stored row-major with their 32-byte chunks
+// XOR-swizzled per row: chunk c of row r sits at c ^ vswz<D>(r).  With it,
+// the eight rows of one transposed read (keys {0..3, 8..11} + 4 hf, shifted
+// by 16 for the upper k-slots) hit eight different 32-byte bank groups.
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  if constexpr (D == 128)
+    return ((r >> 1) & 1) + 2 * ((r >> 3) & 1);
+  else
+    return (r >> 3) & 1;
 }
 
+// B-operand byte e (0..31) of lane half hf is P~ of key 32 (e / 16) +
+// 8 ((e % 16) / 4) + 4 hf + e % 4 of the 64-key tile (the accumulator order).
+__device__ __forceinline__ int pkey(int e, int hf) {
+  return 32 * (e >> 4) + 8 * ((e & 15) >> 2) + 4 * hf + (e & 3);
+}
+
+// ---------------------------------------------------------------------------
+// FP8 forward, 8 waves of 32 query rows, two waves per SIMD, with the P.V
+// product of tile j-1 issued next to the softmax stages of tile j.
+// ---------------------------------------------------------------------------
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdArgs a) {
   constexpr int BC = 64, BR = 32 * NW, T = NW * 64;
-  constexpr int KPB = D + 16;          // K tile row pitch (bytes)
-  constexpr int VPB = BC + 16;         // V^T tile row pitch (bytes)
-  constexpr int KSB = BC * KPB, VSB = D * VPB, STAGE = KSB + VSB;
+  constexpr int KPB = D + 16;          // K tile row pitch (bytes): 16 rows of a b128 read hit distinct banks
+  constexpr int KSB = BC * KPB, VSB = BC * D;
   constexpr int DCH = D / 16;          // 16-byte chunks per row
-  constexpr int KCH = (BC * DCH + T - 1) / T;
-  constexpr int VUNITS = (BC / 4) * DCH;  // 4 keys x 16 dims
-  constexpr int VCH = (VUNITS + T - 1) / T;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  constexpr int NCH = (BC * DCH + T - 1) / T;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * KSB + 2 * VSB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
@@ -107,6 +126,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdArgs a) {
   const int wp_lo = wq0 + off, wp_hi = min(wq0 + 31, nq - 1) + off;
   const int my_q = wq0 + ql;
   const int my_p = my_q + off;
+  auto active = [&](int jt) __attribute__((always_inline)) {
+    const int k0 = jt * BC;
+    return wave_rows && (!causal || k0 <= wp_hi) && (window <= 0 || k0 + BC - 1 > wp_lo - window);
+  };
+  auto kbuf = [&](int jt) __attribute__((always_inline)) { return smem + ((jt - jt0) & 1) * KSB; };
+  auto vbuf = [&](int jt) __attribute__((always_inline)) { return smem + 2 * KSB + ((jt - jt0) & 1) * VSB; };
 
   // Q^T B operands: per 64-dim step, lane half hf holds dims [64 ks + 32 hf, +32)
   uint4 qreg[D / 64][2];
@@ -119,85 +144,106 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdArgs a) {
     }
   }
 
-  uint4 kreg[KCH], vreg[VCH][4];
-  auto load_tile = [&](int k0) {
+  // per-lane V^T operand offsets: read t (0..3) of 32-dim block db gives
+  // k-slots 8t..8t+7; this lane serves as source lane s of the transposed read
+  int voff[4];
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int cidx = tid + i * T;
-      const int row = cidx / DCH, col = cidx % DCH;
-      kreg[i] = bload16(krs, (uint32_t)(k0 + row) * kst + col * 16);
-    }
-#pragma unroll
-    for (int u = 0; u < VCH; ++u) {
-      const int unit = tid + u * T;
-      const int g = unit / DCH, dc = unit % DCH;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vreg[u][i] = bload16(vrs, (uint32_t)(k0 + 4 * g + i) * vst + dc * 16);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint8_t *ks = smem + buf * STAGE;
-    uint8_t *vt = ks + KSB;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int cidx = tid + i * T;
-      if (KCH * T == BC * DCH || cidx < BC * DCH) {
-        const int row = cidx / DCH, col = cidx % DCH;
-        *(uint4 *)(ks + row * KPB + col * 16) = kreg[i];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < VCH; ++u) {
-      const int unit = tid + u * T;
-      if (VCH * T == VUNITS || unit < VUNITS) {
-        const int g = unit / DCH, dc = unit % DCH;
-        const int pos = vt8_group_pos(g);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const uint32_t w = u8_at(vreg[u][0], e) | (u8_at(vreg[u][1], e) << 8) |
-                             (u8_at(vreg[u][2], e) << 16) | (u8_at(vreg[u][3], e) << 24);
-          *(uint32_t *)(vt + (dc * 16 + e) * VPB + pos) = w;
-        }
-      }
-    }
-  };
+  for (int t4 = 0; t4 < 4; ++t4) {
+    const int key = pkey(8 * t4 + (lane & 15) / 2, hf);
+    const int col = 8 * (lane & 1) + 16 * ((lane >> 4) & 1);  // byte within the 32-byte chunk
+    voff[t4] = key * D + col;
+  }
 
+  uint4 kreg[NCH], vreg[NCH];
+  auto load_k = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int cidx = tid + i * T;
+      kreg[i] = bload16(krs, (uint32_t)(k0 + cidx / DCH) * kst + (cidx % DCH) * 16);
+    }
+  };
+  auto load_v = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int cidx = tid + i * T;
+      vreg[i] = bload16(vrs, (uint32_t)(k0 + cidx / DCH) * vst + (cidx % DCH) * 16);
+    }
+  };
+  auto store_k = [&](uint8_t *ks) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int cidx = tid + i * T;
+      if (NCH * T == BC * DCH || cidx < BC * DCH) *(uint4 *)(ks + (cidx / DCH) * KPB + (cidx % DCH) * 16) = kreg[i];
+    }
+  };
+  auto store_v = [&](uint8_t *vs) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int cidx = tid + i * T;
+      if (NCH * T == BC * DCH || cidx < BC * DCH) {
+        const int r = cidx / DCH, c16 = cidx % DCH;
+        const int c32 = (c16 >> 1) ^ vswz<D>(r);
+        *(uint4 *)(vs + r * D + c32 * 32 + (c16 & 1) * 16) = vreg[i];
+      }
+    }
+  };
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
   float m = -INFINITY, l = 0.f;
   const float c = a.scale_log2;  // includes the q and k descales
+  f32x16 s[2];
+  uint4 pb0_prev = {0u, 0u, 0u, 0u}, pb1_prev = {0u, 0u, 0u, 0u};
+  float alpha_prev = 1.f;
 
-  if (jt0 < jt1) {
-    load_tile(jt0 * BC);
-    store_tile(0);
-  }
-  __syncthreads();
+  // per-lane swizzled V offsets for the two lane halves' keys are fixed:
+  // source lane s reads row pkey(8 t + (s % 16) / 2, s / 32)
+  int vrow_sw[4];
+#pragma unroll
+  for (int t4 = 0; t4 < 4; ++t4) vrow_sw[t4] = vswz<D>(pkey(8 * t4 + (lane & 15) / 2, hf));
 
-  for (int jt = jt0; jt < jt1; ++jt) {
-    const int buf = (jt - jt0) & 1;
+  auto vfrag = [&](const uint8_t *vs, int db, uint4 &lo, uint4 &hi) __attribute__((always_inline)) {
+    uint2 r[4];
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) r[t4] = lds_read_tr8(vs + voff[t4] + ((db ^ vrow_sw[t4]) << 5));
+    lo = (uint4){r[0].x, r[0].y, r[1].x, r[1].y};
+    hi = (uint4){r[2].x, r[2].y, r[3].x, r[3].y};
+  };
+  auto qk = [&](const uint8_t *ks) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = (f32x16){};
+      const uint8_t *krow = ks + (kb * 32 + ql) * KPB + hf * 32;
+#pragma unroll
+      for (int kk = 0; kk < D / 64; ++kk)
+        s[kb] = mfma_fp8(*(const uint4 *)(krow + kk * 64), *(const uint4 *)(krow + kk * 64 + 16), qreg[kk][0],
+                         qreg[kk][1], s[kb]);
+    }
+  };
+  auto rescale_prev = [&]() __attribute__((always_inline)) {
+    if (__ballot(alpha_prev != 1.f)) {
+      float a_r = alpha_prev;
+      asm volatile("" : "+v"(a_r));  // keep the multiplies inside this branch
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) acc[i] *= a_r;
+    }
+  };
+
+  // one key tile: K(jt+1) and V(jt) are fetched into registers meanwhile;
+  // the previous tile's D/32 product MFMAs are issued between the softmax
+  // stages of this tile
+  auto step = [&](auto mask_tag, int jt) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int k0 = jt * BC;
-    const bool more = jt + 1 < jt1;
-    if (more) load_tile(k0 + BC);
-    const uint8_t *ks = smem + buf * STAGE;
-    const uint8_t *vt = ks + KSB;
-
-    const bool active = wave_rows && (!causal || k0 <= wp_hi) &&
-                        (window <= 0 || k0 + BC - 1 > wp_lo - window);
-    if (active) {
-      f32x16 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = (f32x16){};
-        const uint8_t *krow = ks + (kb * 32 + ql) * KPB + hf * 32;
-#pragma unroll
-        for (int kk = 0; kk < D / 64; ++kk)
-          s[kb] = mfma_fp8(*(const uint4 *)(krow + kk * 64), *(const uint4 *)(krow + kk * 64 + 16),
-                           qreg[kk][0], qreg[kk][1], s[kb]);
-      }
-      const bool need_mask = (causal && k0 + BC - 1 > wp_lo) ||
-                             (window > 0 && k0 <= wp_hi - window) || (k0 + BC > nk);
-      if (need_mask) {
+    const bool more_k = jt + 1 < jt1;
+    if (!MASK || more_k) load_k(k0 + BC);
+    load_v(k0);
+    float alpha = 1.f;
+    uint4 pb0 = {0u, 0u, 0u, 0u}, pb1 = {0u, 0u, 0u, 0u};
+    const bool act = !MASK || active(jt);
+    if (act) {
+      qk(kbuf(jt));
+      if (MASK) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -207,57 +253,110 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdArgs a) {
             if (!ok) s[kb][r] = -INFINITY;
           }
       }
-      float mx = s[0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = half_swap_max(mx) * c;
-      // the running max moves only when a row max jumps by more than 2^8
-      // (P~ <= 256 stays inside e4m3's range of 448), so the accumulators
-      // are rescaled only then
-      const bool up = mx > m + 8.f;
-      const float alpha = up ? fast_exp2(m - mx) : 1.f;
-      m = up ? mx : m;
-      const float m_use = m == -INFINITY ? 0.f : m;
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
-          s[kb][r] = p;
-          rs += p;
-        }
-      l = l * alpha + rs;
-      if (__ballot(alpha != 1.f)) {
-        float a_r = alpha;
-        asm volatile("" : "+v"(a_r));  // keep the multiplies inside this branch
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) acc[i] *= a_r;
-      }
-      // B operand bytes b = 0..31 <- (kb, r) = (b / 16, b % 16)
-      uint4 pb0, pb1;
-      pb0.x = pack_fp8x4(s[0][0], s[0][1], s[0][2], s[0][3]);
-      pb0.y = pack_fp8x4(s[0][4], s[0][5], s[0][6], s[0][7]);
-      pb0.z = pack_fp8x4(s[0][8], s[0][9], s[0][10], s[0][11]);
-      pb0.w = pack_fp8x4(s[0][12], s[0][13], s[0][14], s[0][15]);
-      pb1.x = pack_fp8x4(s[1][0], s[1][1], s[1][2], s[1][3]);
-      pb1.y = pack_fp8x4(s[1][4], s[1][5], s[1][6], s[1][7]);
-      pb1.z = pack_fp8x4(s[1][8], s[1][9], s[1][10], s[1][11]);
-      pb1.w = pack_fp8x4(s[1][12], s[1][13], s[1][14], s[1][15]);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const uint8_t *vrow = vt + (db * 32 + ql) * VPB + hf * 32;
-        acc[db] = mfma_fp8(*(const uint4 *)vrow, *(const uint4 *)(vrow + 16), pb0, pb1, acc[db]);
-      }
     }
-    if (more) store_tile(buf ^ 1);
+    rescale_prev();
+    const uint8_t *vs = vbuf(jt - 1);
+    uint4 vlo, vhi;
+    vfrag(vs, 0, vlo, vhi);
+    float mx = 0.f, m_use = 0.f, rs = 0.f;
+    __builtin_amdgcn_sched_barrier(0);
+    // stages: 0 max, 1 max + new m, 2..5 exponentials (8 each), 6 pack;
+    // the product MFMA of block db is issued at stage 2 db (its operand
+    // read one stage before)
+    constexpr int NDB = D / 32;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint4 nlo, nhi;
+      const bool mf = (i % 2 == 0) && (i / 2) < NDB;
+      if (mf && i / 2 + 1 < NDB) vfrag(vs, i / 2 + 1, nlo, nhi);
+      if (mf) acc[i / 2] = mfma_fp8(vlo, vhi, pb0_prev, pb1_prev, acc[i / 2]);
+      if (mf && i / 2 + 1 < NDB) {
+        vlo = nlo;
+        vhi = nhi;
+      }
+      if (act) {
+        if (i == 0) {
+          mx = s[0][0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+        } else if (i == 1) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+          mx = half_swap_max(mx) * c;
+          // the running max moves only when a row max jumps by more than
+          // 2^8 (P~ <= 256 stays inside e4m3's range of 448)
+          const bool up = mx > m + 8.f;
+          alpha = up ? fast_exp2(m - mx) : 1.f;
+          m = up ? mx : m;
+          m_use = m == -INFINITY ? 0.f : m;
+        } else if (i < 6) {
+          const int kb = (i - 2) >> 1, r0 = ((i - 2) & 1) * 8;
+#pragma unroll
+          for (int r = r0; r < r0 + 8; ++r) {
+            const float p = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
+            s[kb][r] = p;
+            rs += p;
+          }
+          if (i == 5) l = l * alpha + rs;
+        } else if (i == 6) {
+          // B operand bytes b = 0..31 <- (kb, r) = (b / 16, b % 16)
+          pb0.x = pack_fp8x4(s[0][0], s[0][1], s[0][2], s[0][3]);
+          pb0.y = pack_fp8x4(s[0][4], s[0][5], s[0][6], s[0][7]);
+          pb0.z = pack_fp8x4(s[0][8], s[0][9], s[0][10], s[0][11]);
+          pb0.w = pack_fp8x4(s[0][12], s[0][13], s[0][14], s[0][15]);
+          pb1.x = pack_fp8x4(s[1][0], s[1][1], s[1][2], s[1][3]);
+          pb1.y = pack_fp8x4(s[1][4], s[1][5], s[1][6], s[1][7]);
+          pb1.z = pack_fp8x4(s[1][8], s[1][9], s[1][10], s[1][11]);
+          pb1.w = pack_fp8x4(s[1][12], s[1][13], s[1][14], s[1][15]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (!MASK || more_k) store_k(kbuf(jt + 1));
+    store_v(vbuf(jt));
     __syncthreads();
+    pb0_prev = pb0;
+    pb1_prev = pb1;
+    alpha_prev = alpha;
+  };
+
+  int ja = jt0, jb = jt1;
+  if (window > 0) {
+    const int lim = p_hi - window;
+    ja = lim >= 0 ? min(jt1, max(jt0, lim / BC + 1)) : jt0;
+  }
+  if (causal) {
+    const int lim = p_lo - (BC - 1);
+    jb = lim >= 0 ? max(ja, min(jt1, lim / BC + 1)) : ja;
+  }
+  jb = max(min(jb, jt1 - 1), ja);  // the last tile is masked: it has no next K tile
+
+  if (jt0 < jt1) {
+    load_k(jt0 * BC);
+    store_k(kbuf(jt0));
+  }
+  {  // the V buffer the first tile's (empty) product reads
+    uint4 *vz = (uint4 *)vbuf(jt0 - 1);
+    for (int i = tid; i < VSB / 16; i += T) vz[i] = (uint4){0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+  const std::true_type masked;
+  const std::false_type whole;
+  for (int jt = jt0; jt < ja; ++jt) step(masked, jt);
+  for (int jt = ja; jt < jb; ++jt) step(whole, jt);
+  for (int jt = jb; jt < jt1; ++jt) step(masked, jt);
+  if (jt0 < jt1) {
+    rescale_prev();
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      uint4 lo, hi;
+      vfrag(vbuf(jt1 - 1), db, lo, hi);
+      acc[db] = mfma_fp8(lo, hi, pb0_prev, pb1_prev, acc[db]);
+    }
   }
 
   // note: l sums the fp32 P~ (before quantisation), as the softmax denominator
-  const float lt = l + __shfl_xor(l, 32);
+  const float lt = half_swap_sum(l);
   const float inv = lt > 0.f ? a.v_descale / lt : 0.f;
   if (my_q < nq) {
     uint16_t *orow = (uint16_t *)a.o + b * a.o_sb + (int64_t)(seq0 + my_q) * a.o_st + h * a.o_sh;

@@ -176,6 +176,28 @@ __device__ __forceinline__ int xcd_item(int bid, int total) {
   return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
 }
 
+// Work item of forward work-group bid: (batch or sequence b, head h, query
+// tile qt).  Each XCD processes a contiguous range of items.  Dense calls
+// are (b, h)-major, so an XCD holds whole heads and their K/V stay in its
+// L2.  Packed varlen calls are head-major: every XCD then gets the same mix
+// of sequence lengths (sequence-major ranges would hand one XCD the longest
+// sequences).  Causal items run heaviest (last) query tile first.
+__device__ __forceinline__ void fwd_item(int bid, int nqt, int heads, int batch, bool varlen, bool causal, int &b,
+                                         int &h, int &qt) {
+  const int item = xcd_item(bid, nqt * heads * batch);
+  const int t = item % nqt;
+  if (varlen) {
+    const int hb = item / nqt;
+    h = hb / batch;
+    b = hb % batch;
+  } else {
+    const int bh = item / nqt;
+    b = bh / heads;
+    h = bh % heads;
+  }
+  qt = causal ? nqt - 1 - t : t;
+}
+
 // Write a unit of 4 rows x 8 bf16 columns (r[i] = row i) transposed: column
 // `col0 + e` gets the 4 values at positions pos..pos+3 of its row (pitch
 // `pitch` elements) in the tile at `t`.

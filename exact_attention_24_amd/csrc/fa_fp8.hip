@@ -92,10 +92,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int ql = lane & 31, hf = lane >> 5;
 
-  const int item = xcd_item(blockIdx.x, a.nqt * a.heads * a.batch);
-  const int bh = item / a.nqt, t = item % a.nqt;
-  const int qt = a.causal ? a.nqt - 1 - t : t;
-  const int b = bh / a.heads, h = bh % a.heads;
+  int b, h, qt;
+  fwd_item(blockIdx.x, a.nqt, a.heads, a.batch, a.cu_seqlens != nullptr, a.causal, b, h, qt);
   int seq0 = 0, nq = a.nq, nk = a.nk;
   if (a.cu_seqlens) {
     seq0 = a.cu_seqlens[b];

@@ -55,11 +55,7 @@ using namespace dev;
 // Split the (XCD-renumbered) block id into (batch, head, query tile),
 // heaviest causal tiles first.
 __device__ __forceinline__ void decode_item(const FwdArgs &a, int &b, int &h, int &qt) {
-  const int item = xcd_item(blockIdx.x, a.nqt * a.heads * a.batch);
-  const int bh = item / a.nqt, t = item % a.nqt;
-  qt = a.causal ? a.nqt - 1 - t : t;
-  b = bh / a.heads;
-  h = bh % a.heads;
+  fwd_item(blockIdx.x, a.nqt, a.heads, a.batch, a.cu_seqlens != nullptr, a.causal, b, h, qt);
 }
 
 // K/V staging with K and V of different tiles (K runs one tile ahead).

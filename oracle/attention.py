@@ -60,6 +60,7 @@ __all__ = [
     "mha_fwd",
     "mha_bwd",
     "varlen_fwd",
+    "varlen_bwd",
     "e4m3_decode",
     "fp8_dequant",
 ]
@@ -250,6 +251,35 @@ def varlen_fwd(q, k, v, cu_seqlens, scale, causal=False, window=0, heads=None, s
         for h in hs:
             o[a:b, h], lse[h, a:b] = attention_fwd(q[a:b, h], k[a:b, h], v[a:b, h], scale, causal, window)
     return o, lse
+
+
+def varlen_bwd(q, k, v, dout, cu_seqlens, scale, causal=False, window=0, heads=None, seqs=None):
+    """Gradients for packed sequences (the same layout as ``varlen_fwd``).
+
+    Each sequence is an independent attention problem, so its gradients are
+    the chain rule of ``attention_bwd`` applied within the sequence; rows of
+    other sequences get exactly zero from it.  Returns dq, dk, dv
+    [total, H, d]; ``heads`` / ``seqs`` restrict the work (others NaN).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    total, h_, _ = q.shape
+    dq = np.full(q.shape, np.nan)
+    dk = np.full(k.shape, np.nan)
+    dv = np.full(v.shape, np.nan)
+    hs = range(h_) if heads is None else heads
+    ss = range(cu.size - 1) if seqs is None else seqs
+    for s in ss:
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b == a:
+            continue
+        for h in hs:
+            dq[a:b, h], dk[a:b, h], dv[a:b, h] = attention_bwd(q[a:b, h], k[a:b, h], v[a:b, h], dout[a:b, h],
+                                                               scale, causal, window)
+    return dq, dk, dv
 
 
 def e4m3_decode(codes):

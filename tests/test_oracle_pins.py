@@ -275,6 +275,32 @@ def test_backward_finite_differences(causal, window):
         np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8)
 
 
+@pytest.mark.parametrize("causal,window", [(True, 0), (True, 2), (False, 0)])
+def test_varlen_backward_finite_differences(causal, window):
+    """Packed-sequence gradients against central differences of the packed
+    forward: the loss L = sum(dO * O) runs through varlen_fwd, so a mistake
+    in the per-sequence offsets, the masks or cross-sequence leakage shows."""
+    rng = np.random.default_rng(17)
+    cu = np.array([0, 3, 7, 8])  # lengths 3, 4, 1
+    total, heads, d, scale, h = 8, 2, 3, 0.8, 1e-6
+    q, k, v, do = (_rand(rng, total, heads, d) for _ in range(4))
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.varlen_fwd(qq, kk, vv, cu, scale, causal, window)
+        return float((do * o).sum())
+
+    grads = oracle.varlen_bwd(q, k, v, do, cu, scale, causal, window)
+    for which, g in enumerate(grads):
+        num = np.zeros_like(g)
+        for idx in np.ndindex(g.shape):
+            plus = [q.copy(), k.copy(), v.copy()]
+            minus = [q.copy(), k.copy(), v.copy()]
+            plus[which][idx] += h
+            minus[which][idx] -= h
+            num[idx] = (loss(*plus) - loss(*minus)) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8)
+
+
 @pytest.mark.parametrize("causal,window", [(True, 0), (False, 0), (True, 5)])
 def test_backward_identities(causal, window):
     rng = np.random.default_rng(15)

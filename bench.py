@@ -163,6 +163,19 @@ def extra_rows(torch, fa, steps):
         rows["varlen_32k_w4096"] = {"ms": round(med(ms), 4), "tflops": round(f / med(ms) / 1e9, 1)}
     except Exception as e:
         rows["varlen_32k_w4096"] = {"error": str(e)[:120]}
+    # varlen backward
+    try:
+        w = WORKLOADS["varlen_bwd_32k"]
+        t = workload_inputs("varlen_bwd_32k")
+        q, k, v, do, cu = (t[x].cuda() for x in ("q", "k", "v", "dout", "cu_seqlens"))
+        mx = max(t["lengths"])
+        o, lse = fa.fa_varlen_fwd(q, k, v, cu, mx, causal=True, window=w.window)
+        _, ms = time_calls(lambda: fa.fa_varlen_bwd(do, q, k, v, o, lse, cu, mx, causal=True, window=w.window),
+                           2, steps, torch)
+        f = 2.5 * 4.0 * w.head_dim * w.heads * visible_pairs_varlen(t["lengths"], True, w.window)
+        rows["varlen_bwd_32k_w4096"] = {"ms": round(med(ms), 4), "tflops": round(f / med(ms) / 1e9, 1)}
+    except Exception as e:
+        rows["varlen_bwd_32k_w4096"] = {"error": str(e)[:120]}
     # fp8 forward
     try:
         t = workload_inputs("fp8_n8192")
@@ -177,7 +190,7 @@ def extra_rows(torch, fa, steps):
     return rows
 
 
-WORKLOAD_CHOICES = ("fwd_causal", "fwd_noncausal", "bwd", "varlen", "fp8")
+WORKLOAD_CHOICES = ("fwd_causal", "fwd_noncausal", "bwd", "varlen", "varlen_bwd", "fp8")
 
 
 def make_step(name, torch, fa):
@@ -209,6 +222,18 @@ def make_step(name, torch, fa):
         f = 4.0 * w.head_dim * w.heads * visible_pairs_varlen(t["lengths"], True, w.window)
         return (lambda: fa.fa_varlen_fwd(q, k, v, cu, mx, causal=True, window=w.window), f,
                 "varlen fwd 32768 tokens H28 d128 bf16 causal window 4096", "bf16", PEAK_BF16_TFLOPS, "fa_fwd.hip")
+    if name == "varlen_bwd":
+        w = WORKLOADS["varlen_bwd_32k"]
+        t = workload_inputs("varlen_bwd_32k")
+        q, k, v, do, cu = (t[x].cuda() for x in ("q", "k", "v", "dout", "cu_seqlens"))
+        mx = max(t["lengths"])
+        o, lse = fa.fa_varlen_fwd(q, k, v, cu, mx, causal=True, window=w.window)
+        dq, dk, dv = (torch.empty(x.shape, dtype=torch.float32, device="cuda") for x in (q, k, v))
+        f = 2.5 * 4.0 * w.head_dim * w.heads * visible_pairs_varlen(t["lengths"], True, w.window)
+        return (lambda: fa.fa_varlen_bwd(do, q, k, v, o, lse, cu, mx, causal=True, window=w.window, dq=dq, dk=dk,
+                                         dv=dv), f,
+                "varlen bwd 32768 tokens H28 d128 bf16 causal window 4096, fp32 gradients", "bf16",
+                PEAK_BF16_TFLOPS, "fa_bwd.hip")
     t = workload_inputs("fp8_n8192")
     q8, k8, v8 = (t[x].cuda() for x in ("q8", "k8", "v8"))
     ds = (t["q_scale"], t["k_scale"], t["v_scale"])

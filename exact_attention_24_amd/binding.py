@@ -3,7 +3,7 @@
 Argument marshalling only: every step of the attention computation runs in
 the library's HIP kernels.  torch supplies device memory and the current
 stream.  The functions carry the C names (fa_fwd, fa_varlen_fwd, fa_bwd,
-fa_bwd_workspace_bytes, fa_check_*); status codes become exceptions the way
+fa_varlen_bwd, fa_*_workspace_bytes, fa_check_*); status codes become exceptions the way
 the pages' error table does it (ms-swift long-text page, section 4.3): a dtype
 mismatch or bad argument raises ValueError, anything else RuntimeError.
 There is no fallback: if the library is not built, every call raises.
@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 FA_F32, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_DTYPE_MISMATCH, FA_ERR_UNSUPPORTED, FA_ERR_HIP = range(5)
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _I64x3 = ctypes.c_int64 * 3
 _I64x2 = ctypes.c_int64 * 2
@@ -69,8 +69,25 @@ class BwdParams(ctypes.Structure):
     ]
 
 
+class VarlenBwdParams(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("dout", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("qkv_dtype", ctypes.c_int), ("grad_dtype", ctypes.c_int),
+        ("num_seqs", ctypes.c_int32), ("total_tokens", ctypes.c_int32), ("max_seqlen", ctypes.c_int32),
+        ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("q_stride", _I64x2), ("k_stride", _I64x2), ("v_stride", _I64x2), ("o_stride", _I64x2),
+        ("do_stride", _I64x2), ("dq_stride", _I64x2), ("dk_stride", _I64x2), ("dv_stride", _I64x2),
+        ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("deterministic", ctypes.c_int32),
+    ]
+
+
 EXPORTS = ("fa_abi_version", "fa_last_error", "fa_check_fwd", "fa_check_varlen_fwd", "fa_check_bwd",
-           "fa_fwd", "fa_varlen_fwd", "fa_bwd_workspace_bytes", "fa_bwd")
+           "fa_check_varlen_bwd", "fa_fwd", "fa_varlen_fwd", "fa_bwd_workspace_bytes", "fa_bwd",
+           "fa_varlen_bwd_workspace_bytes", "fa_varlen_bwd")
 
 _lib = None
 
@@ -87,7 +104,7 @@ def lib():
     L.fa_abi_version.restype = ctypes.c_int
     L.fa_last_error.restype = ctypes.c_char_p
     for name, ptype in (("fa_check_fwd", FwdParams), ("fa_check_varlen_fwd", VarlenFwdParams),
-                        ("fa_check_bwd", BwdParams)):
+                        ("fa_check_bwd", BwdParams), ("fa_check_varlen_bwd", VarlenBwdParams)):
         getattr(L, name).argtypes = [ctypes.POINTER(ptype)]
         getattr(L, name).restype = ctypes.c_int
     L.fa_fwd.argtypes = [ctypes.POINTER(FwdParams), ctypes.c_void_p]
@@ -98,6 +115,11 @@ def lib():
     L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.fa_bwd.argtypes = [ctypes.POINTER(BwdParams), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     L.fa_bwd.restype = ctypes.c_int
+    L.fa_varlen_bwd_workspace_bytes.argtypes = [ctypes.POINTER(VarlenBwdParams)]
+    L.fa_varlen_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.fa_varlen_bwd.argtypes = [ctypes.POINTER(VarlenBwdParams), ctypes.c_void_p, ctypes.c_size_t,
+                                ctypes.c_void_p]
+    L.fa_varlen_bwd.restype = ctypes.c_int
     if L.fa_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libfa.so ABI {L.fa_abi_version()} != binding ABI {ABI_VERSION}; rebuild")
     _lib = L
@@ -296,4 +318,63 @@ def fa_bwd(dout, q, k, v, o, lse, causal=False, window=0, softmax_scale=None, de
     nbytes = fa_bwd_workspace_bytes(p)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     _raise(lib().fa_bwd(ctypes.byref(p), ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(nbytes), _stream()))
+    return dq, dk, dv
+
+
+def make_varlen_bwd_params(dout, q, k, v, o, lse, dq, dk, dv, cu_seqlens, max_seqlen, causal=False, window=0,
+                           softmax_scale=None, deterministic=False):
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.dim() != 3:
+            raise ValueError(f"{n} must be [total_tokens, heads, head_dim] (got {tuple(t.shape)})")
+        _check_last_dim(n, t)
+    codes = {_code(t) for t in (q, k, v, o, dout)}
+    if len(codes) != 1:
+        raise ValueError("Input and output tensors must have the same dtype (q, k, v, o, dout differ)")
+    if dq.dtype != dk.dtype or dq.dtype != dv.dtype:
+        raise ValueError("dq, dk, dv must share one dtype")
+    total, h, d = q.shape
+    for t in (k, v, o, dout, dq, dk, dv):
+        if t.shape != q.shape:
+            raise ValueError("q, k, v, o, dout, dq, dk, dv must all be [total_tokens, heads, head_dim]")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 vector")
+    if lse.shape != (h, total) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [heads, total_tokens] tensor")
+    p = VarlenBwdParams()
+    p.q, p.k, p.v, p.o, p.dout, p.lse = (_ptr(t) for t in (q, k, v, o, dout, lse))
+    p.dq, p.dk, p.dv, p.cu_seqlens = _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens)
+    p.qkv_dtype, p.grad_dtype = _code(q), _code(dq)
+    p.num_seqs, p.total_tokens, p.max_seqlen = cu_seqlens.numel() - 1, total, int(max_seqlen)
+    p.heads, p.head_dim = h, d
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        setattr(p, f"{name}_stride", _I64x2(*t.stride()[:2]))
+    p.softmax_scale = _default_scale(d, softmax_scale)
+    p.causal, p.window, p.deterministic = int(bool(causal)), int(window), int(bool(deterministic))
+    return p
+
+
+def fa_check_varlen_bwd(params: VarlenBwdParams) -> int:
+    return lib().fa_check_varlen_bwd(ctypes.byref(params))
+
+
+def fa_varlen_bwd_workspace_bytes(params: VarlenBwdParams) -> int:
+    return int(lib().fa_varlen_bwd_workspace_bytes(ctypes.byref(params)))
+
+
+def fa_varlen_bwd(dout, q, k, v, o, lse, cu_seqlens, max_seqlen, causal=False, window=0, softmax_scale=None,
+                  deterministic=False, grad_dtype=torch.float32, dq=None, dk=None, dv=None):
+    """dq, dk, dv of the packed variable-length forward (q/k/v [total, H, d], lse [H, total])."""
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
+    if dk is None:
+        dk = torch.empty(k.shape, dtype=grad_dtype, device=q.device)
+    if dv is None:
+        dv = torch.empty(v.shape, dtype=grad_dtype, device=q.device)
+    p = make_varlen_bwd_params(dout, q, k, v, o, lse, dq, dk, dv, cu_seqlens, max_seqlen, causal, window,
+                               softmax_scale, deterministic)
+    _raise(lib().fa_check_varlen_bwd(ctypes.byref(p)))
+    nbytes = fa_varlen_bwd_workspace_bytes(p)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _raise(lib().fa_varlen_bwd(ctypes.byref(p), ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(nbytes),
+                               _stream()))
     return dq, dk, dv

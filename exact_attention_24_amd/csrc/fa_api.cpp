@@ -11,6 +11,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -135,6 +136,28 @@ fa_status launched(hipError_t e) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Checks shared by the dense and packed backward.
+fa_status check_bwd_common(fa_dtype qkv, fa_dtype grad, int heads, int head_dim, float scale, int causal,
+                           int window, int deterministic) {
+  if (!valid_dtype(qkv) || !valid_dtype(grad))
+    return fail(FA_ERR_INVALID_ARGUMENT, "unknown dtype code (qkv_dtype=%d, grad_dtype=%d)", (int)qkv, (int)grad);
+  if (qkv == FA_FP8_E4M3) return fail(FA_ERR_UNSUPPORTED, "the backward pass is not available for fp8 inputs");
+  if (qkv != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "the backward pass takes bf16 q/k/v/o/dout (got qkv_dtype=%d)", (int)qkv);
+  if (grad != FA_F32 && grad != FA_BF16)
+    return fail(FA_ERR_DTYPE_MISMATCH, "gradients must be fp32 or bf16 (got grad_dtype=%d)", (int)grad);
+  if (heads < 0) return fail(FA_ERR_INVALID_ARGUMENT, "heads must be >= 0 (got %d)", heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  if (!(std::isfinite(scale) && scale > 0.f))
+    return fail(FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0 (got %g)", (double)scale);
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", causal);
+  if (window < 0) return fail(FA_ERR_INVALID_ARGUMENT, "window must be >= 0 (got %d)", window);
+  if (deterministic != 0 && deterministic != 1)
+    return fail(FA_ERR_INVALID_ARGUMENT, "deterministic must be 0 or 1 (got %d)", deterministic);
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -192,28 +215,12 @@ fa_status fa_check_varlen_fwd(const fa_varlen_fwd_params *p) {
 
 fa_status fa_check_bwd(const fa_bwd_params *p) {
   if (!p) return fail(FA_ERR_INVALID_ARGUMENT, "params is NULL");
-  if (!valid_dtype(p->qkv_dtype) || !valid_dtype(p->grad_dtype))
-    return fail(FA_ERR_INVALID_ARGUMENT, "unknown dtype code (qkv_dtype=%d, grad_dtype=%d)",
-                (int)p->qkv_dtype, (int)p->grad_dtype);
-  if (p->qkv_dtype == FA_FP8_E4M3)
-    return fail(FA_ERR_UNSUPPORTED, "the backward pass is not available for fp8 inputs");
-  if (p->qkv_dtype != FA_BF16)
-    return fail(FA_ERR_UNSUPPORTED, "the backward pass takes bf16 q/k/v/o/dout (got qkv_dtype=%d)",
-                (int)p->qkv_dtype);
-  if (p->grad_dtype != FA_F32 && p->grad_dtype != FA_BF16)
-    return fail(FA_ERR_DTYPE_MISMATCH, "gradients must be fp32 or bf16 (got grad_dtype=%d)", (int)p->grad_dtype);
-  if (p->heads < 0 || p->batch < 0 || p->seqlen_q < 0 || p->seqlen_k < 0)
+  fa_status st0 = check_bwd_common(p->qkv_dtype, p->grad_dtype, p->heads, p->head_dim, p->softmax_scale,
+                                   p->causal, p->window, p->deterministic);
+  if (st0 != FA_OK) return st0;
+  if (p->batch < 0 || p->seqlen_q < 0 || p->seqlen_k < 0)
     return fail(FA_ERR_INVALID_ARGUMENT, "sizes must be >= 0 (batch=%d seqlen_q=%d seqlen_k=%d heads=%d)",
                 p->batch, p->seqlen_q, p->seqlen_k, p->heads);
-  if (p->head_dim != 64 && p->head_dim != 128)
-    return fail(FA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", p->head_dim);
-  if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f))
-    return fail(FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0 (got %g)", (double)p->softmax_scale);
-  if (p->causal != 0 && p->causal != 1)
-    return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", p->causal);
-  if (p->window < 0) return fail(FA_ERR_INVALID_ARGUMENT, "window must be >= 0 (got %d)", p->window);
-  if (p->deterministic != 0 && p->deterministic != 1)
-    return fail(FA_ERR_INVALID_ARGUMENT, "deterministic must be 0 or 1 (got %d)", p->deterministic);
   const bool q_empty = (int64_t)p->batch * p->seqlen_q * p->heads == 0;
   const bool k_empty = (int64_t)p->batch * p->seqlen_k * p->heads == 0;
   const int gb = dtype_bytes(p->grad_dtype);
@@ -228,6 +235,37 @@ fa_status fa_check_bwd(const fa_bwd_params *p) {
   if ((st = check_tensor("dk", p->dk, p->dk_stride, 3, gb, k_empty, nk, hd)) != FA_OK) return st;
   if ((st = check_tensor("dv", p->dv, p->dv_stride, 3, gb, k_empty, nk, hd)) != FA_OK) return st;
   if (!q_empty && !p->lse) return fail(FA_ERR_INVALID_ARGUMENT, "lse is NULL");
+  if (ceil_div(std::max(nq, nk), 128) * (int64_t)p->heads * p->batch > INT32_MAX)
+    return fail(FA_ERR_INVALID_ARGUMENT, "problem too large for one launch");
+  return ok();
+}
+
+fa_status fa_check_varlen_bwd(const fa_varlen_bwd_params *p) {
+  if (!p) return fail(FA_ERR_INVALID_ARGUMENT, "params is NULL");
+  fa_status st = check_bwd_common(p->qkv_dtype, p->grad_dtype, p->heads, p->head_dim, p->softmax_scale,
+                                  p->causal, p->window, p->deterministic);
+  if (st != FA_OK) return st;
+  if (p->num_seqs < 0 || p->total_tokens < 0 || p->max_seqlen < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "sizes must be >= 0 (num_seqs=%d total_tokens=%d max_seqlen=%d)",
+                p->num_seqs, p->total_tokens, p->max_seqlen);
+  if (p->max_seqlen > p->total_tokens)
+    return fail(FA_ERR_INVALID_ARGUMENT, "max_seqlen (%d) exceeds total_tokens (%d)", p->max_seqlen,
+                p->total_tokens);
+  const bool empty = (int64_t)p->total_tokens * p->heads == 0 || p->num_seqs == 0;
+  if (!empty && !p->cu_seqlens) return fail(FA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
+  const int gb = dtype_bytes(p->grad_dtype);
+  const int hd = p->head_dim, tt = p->total_tokens;
+  if ((st = check_tensor("q", p->q, p->q_stride, 2, 2, empty, tt, hd)) != FA_OK) return st;
+  if ((st = check_tensor("k", p->k, p->k_stride, 2, 2, empty, tt, hd)) != FA_OK) return st;
+  if ((st = check_tensor("v", p->v, p->v_stride, 2, 2, empty, tt, hd)) != FA_OK) return st;
+  if ((st = check_tensor("o", p->o, p->o_stride, 2, 2, empty, tt, hd)) != FA_OK) return st;
+  if ((st = check_tensor("dout", p->dout, p->do_stride, 2, 2, empty, tt, hd)) != FA_OK) return st;
+  if ((st = check_tensor("dq", p->dq, p->dq_stride, 2, gb, empty, tt, hd)) != FA_OK) return st;
+  if ((st = check_tensor("dk", p->dk, p->dk_stride, 2, gb, empty, tt, hd)) != FA_OK) return st;
+  if ((st = check_tensor("dv", p->dv, p->dv_stride, 2, gb, empty, tt, hd)) != FA_OK) return st;
+  if (!empty && !p->lse) return fail(FA_ERR_INVALID_ARGUMENT, "lse is NULL");
+  if (ceil_div(p->max_seqlen, 128) * (int64_t)p->heads * p->num_seqs > INT32_MAX)
+    return fail(FA_ERR_INVALID_ARGUMENT, "problem too large for one launch");
   return ok();
 }
 
@@ -299,10 +337,11 @@ fa_status fa_bwd(const fa_bwd_params *p, void *workspace, size_t workspace_bytes
   if ((st = check_device()) != FA_OK) return st;
   fa::BwdArgs a{};
   a.q = p->q; a.k = p->k; a.v = p->v; a.o = p->o; a.dout = p->dout; a.lse = p->lse;
-  a.dq = p->dq; a.dk = p->dk; a.dv = p->dv;
-  const size_t dsz = ((size_t)p->batch * p->heads * p->seqlen_q * sizeof(float) + 255) / 256 * 256;
+  a.dq = p->dq; a.dk = p->dk; a.dv = p->dv; a.cu_seqlens = nullptr;
+  const size_t dsz = need / 2;
   a.dpsum = static_cast<float *>(workspace);
   a.lse2 = reinterpret_cast<float *>(static_cast<char *>(workspace) + dsz);
+  a.lse_sb = (int64_t)p->heads * p->seqlen_q; a.lse_sh = p->seqlen_q;
   a.q_sb = p->q_stride[0]; a.q_st = p->q_stride[1]; a.q_sh = p->q_stride[2];
   a.k_sb = p->k_stride[0]; a.k_st = p->k_stride[1]; a.k_sh = p->k_stride[2];
   a.v_sb = p->v_stride[0]; a.v_st = p->v_stride[1]; a.v_sh = p->v_stride[2];
@@ -312,6 +351,44 @@ fa_status fa_bwd(const fa_bwd_params *p, void *workspace, size_t workspace_bytes
   a.dk_sb = p->dk_stride[0]; a.dk_st = p->dk_stride[1]; a.dk_sh = p->dk_stride[2];
   a.dv_sb = p->dv_stride[0]; a.dv_st = p->dv_stride[1]; a.dv_sh = p->dv_stride[2];
   a.batch = p->batch; a.heads = p->heads; a.nq = p->seqlen_q; a.nk = p->seqlen_k;
+  a.causal = p->causal; a.window = p->window; a.deterministic = p->deterministic;
+  a.grad_f32 = p->grad_dtype == FA_F32;
+  a.scale = p->softmax_scale;
+  a.scale_log2 = p->softmax_scale * kLog2e;
+  return launched(fa::launch_bwd_bf16(a, p->head_dim, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t fa_varlen_bwd_workspace_bytes(const fa_varlen_bwd_params *p) {
+  if (fa_check_varlen_bwd(p) != FA_OK) return 0;
+  return fa::bwd_workspace_bytes(1, p->heads, p->total_tokens, p->head_dim, p->deterministic);
+}
+
+fa_status fa_varlen_bwd(const fa_varlen_bwd_params *p, void *workspace, size_t workspace_bytes, void *stream) {
+  fa_status st = fa_check_varlen_bwd(p);
+  if (st != FA_OK) return st;
+  const size_t need = fa::bwd_workspace_bytes(1, p->heads, p->total_tokens, p->head_dim, p->deterministic);
+  if (workspace_bytes < need)
+    return fail(FA_ERR_INVALID_ARGUMENT, "workspace too small (%zu bytes, need %zu)", workspace_bytes, need);
+  if (need && !workspace) return fail(FA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(FA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if ((int64_t)p->num_seqs * p->heads * p->max_seqlen == 0) return ok();
+  if ((st = check_device()) != FA_OK) return st;
+  fa::BwdArgs a{};
+  a.q = p->q; a.k = p->k; a.v = p->v; a.o = p->o; a.dout = p->dout; a.lse = p->lse;
+  a.dq = p->dq; a.dk = p->dk; a.dv = p->dv; a.cu_seqlens = p->cu_seqlens;
+  a.dpsum = static_cast<float *>(workspace);
+  a.lse2 = reinterpret_cast<float *>(static_cast<char *>(workspace) + need / 2);
+  a.lse_sb = 0; a.lse_sh = p->total_tokens;
+  a.q_sb = 0; a.q_st = p->q_stride[0]; a.q_sh = p->q_stride[1];
+  a.k_sb = 0; a.k_st = p->k_stride[0]; a.k_sh = p->k_stride[1];
+  a.v_sb = 0; a.v_st = p->v_stride[0]; a.v_sh = p->v_stride[1];
+  a.o_sb = 0; a.o_st = p->o_stride[0]; a.o_sh = p->o_stride[1];
+  a.do_sb = 0; a.do_st = p->do_stride[0]; a.do_sh = p->do_stride[1];
+  a.dq_sb = 0; a.dq_st = p->dq_stride[0]; a.dq_sh = p->dq_stride[1];
+  a.dk_sb = 0; a.dk_st = p->dk_stride[0]; a.dk_sh = p->dk_stride[1];
+  a.dv_sb = 0; a.dv_st = p->dv_stride[0]; a.dv_sh = p->dv_stride[1];
+  a.batch = p->num_seqs; a.heads = p->heads; a.nq = p->max_seqlen; a.nk = p->max_seqlen;
   a.causal = p->causal; a.window = p->window; a.deterministic = p->deterministic;
   a.grad_f32 = p->grad_dtype == FA_F32;
   a.scale = p->softmax_scale;

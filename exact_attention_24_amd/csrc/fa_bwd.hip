@@ -9,7 +9,7 @@
 //   dV   = P^T dO,   dP = dO V^T,   dS = P * (dP - D),
 //   dK   = scale dS^T Q,   dQ = scale dS K.
 //
-// Three launches on the caller's stream:
+// Four launches on the caller's stream:
 //   1. bwd_dsum_kernel  D = rowsum(dO * O) in fp32 (workspace).
 //   2. bwd_dkdv_kernel  one work-group per tile of 32*NW keys; loops over the
 //      query tiles that see them; per tile S = Q K^T and dP = dO V^T (B
@@ -21,6 +21,8 @@
 //      key tiles; S^T = K Q^T and dP^T = V dO^T (lane = query, so LSE and D
 //      are per-lane scalars), dS^T, then dQ^T += K^T dS^T with K^T from a
 //      transposed copy of the key tile.  Written once, no atomics.
+//   4. bwd_start_kernel (causal only) the first kStartRows query rows of each
+//      sequence, which see fewer than kStartRows keys, exactly in fp32.
 // Splitting dQ from dK/dV costs the recomputation of S and dP a second time
 // (7 tile products instead of 5) but needs no cross-work-group reduction, so
 // the gradients are bitwise reproducible from call to call.
@@ -50,22 +52,53 @@ __device__ __forceinline__ void store_grad4(void *base, int64_t elem_off, bool f
   }
 }
 
+// Rows of a causal sequence that see fewer than this many keys (its first
+// kStartRows positions) are computed by bwd_start_kernel in fp32.
+constexpr int kStartRows = 64;
+
+__device__ __forceinline__ float load_grad(const void *base, int64_t off, bool f32) {
+  return f32 ? ((const float *)base)[off] : bf16_to_f32(((const uint16_t *)base)[off]);
+}
+
 // ---------------------------------------------------------------------------
-// 1. D_i = sum_c dO_ic O_ic and LSE_i log2(e), [batch, heads, nq] fp32.
+// 1. D_i = sum_c dO_ic O_ic and LSE_i log2(e), laid out like the LSE
+//    ([batch, heads, nq], or [heads, total_tokens] for packed sequences).
 //    A row that saw no key (LSE = -inf) gets +inf, so P = 2^(s - lse2) = 0.
+//    So does a row at the start of a causal sequence (fewer than
+//    kStartRows visible keys): bwd_start_kernel does those rows exactly, and
+//    the MFMA kernels then see P = 0 for them.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dsum_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256) void bwd_dsum_kernel(BwdArgs a, int64_t total) {
   constexpr int LPR = D / 8;       // lanes per row, 8 bf16 each
   constexpr int RPB = 256 / LPR;   // rows per block
   const int tid = threadIdx.x, sub = tid % LPR;
-  const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;  // (b, h, q) order
-  const int64_t total = (int64_t)a.batch * a.heads * a.nq;
+  const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;  // (b, h, q) or (h, token) order
   float acc = 0.f;
+  bool start_row = false;
   if (row < total) {
-    const int q = (int)(row % a.nq);
-    const int64_t bh = row / a.nq;
-    const int h = (int)(bh % a.heads), b = (int)(bh / a.heads);
+    int b = 0, h, q, pos, off;  // q: token row of the tensors; pos: position in its sequence
+    if (a.cu_seqlens) {
+      const int ntok = (int)a.lse_sh;
+      h = (int)(row / ntok);
+      q = (int)(row % ntok);
+      int lo = 0, hi = a.batch;  // the sequence s with cu[s] <= q < cu[s + 1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.cu_seqlens[mid] <= q) lo = mid;
+        else hi = mid;
+      }
+      pos = q - a.cu_seqlens[lo];
+      off = 0;
+    } else {
+      q = (int)(row % a.nq);
+      const int64_t bh = row / a.nq;
+      h = (int)(bh % a.heads);
+      b = (int)(bh / a.heads);
+      pos = q;
+      off = a.nk - a.nq;
+    }
+    start_row = a.causal && pos + off >= 0 && pos + off < kStartRows;
     const uint4 ov = *(const uint4 *)((const uint16_t *)a.o + b * a.o_sb + (int64_t)q * a.o_st +
                                       h * a.o_sh + sub * 8);
     const uint4 dv = *(const uint4 *)((const uint16_t *)a.dout + b * a.do_sb + (int64_t)q * a.do_st +
@@ -78,7 +111,7 @@ __global__ __launch_bounds__(256) void bwd_dsum_kernel(BwdArgs a) {
   if (row < total && sub == 0) {
     a.dpsum[row] = acc;
     const float x = a.lse[row];
-    a.lse2[row] = x == -INFINITY ? INFINITY : x * kLog2e;
+    a.lse2[row] = (x == -INFINITY || start_row) ? INFINITY : x * kLog2e;
   }
 }
 
@@ -110,25 +143,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 31, hf = lane >> 5;
-  const int nq = a.nq, nk = a.nk, off = nk - nq;
   const int causal = a.causal, window = a.window;
 
-  const int nkt = (nk + BC - 1) / BC;
-  const int item = xcd_item(blockIdx.x, nkt * a.heads * a.batch);
-  const int bh = item / nkt, kt = item % nkt;  // causal: low key tiles (most work) first
-  const int b = bh / a.heads, h = bh % a.heads;
+  // low key tiles (the most work under a causal mask) first
+  const int nkt = (a.nk + BC - 1) / BC;
+  int b, h, kt;
+  fwd_item(blockIdx.x, nkt, a.heads, a.batch, a.cu_seqlens != nullptr, false, b, h, kt);
+  int seq0 = 0, nq = a.nq, nk = a.nk;
+  if (a.cu_seqlens) {
+    seq0 = a.cu_seqlens[b];
+    nq = nk = a.cu_seqlens[b + 1] - seq0;
+  }
   const int k0 = kt * BC;
+  if (k0 >= nk) return;  // uniform for the whole work-group
+  const int off = nk - nq;
   const int wk0 = k0 + 32 * wave;
   const int my_k = wk0 + ql;
 
-  const uint16_t *qbase = (const uint16_t *)a.q + b * a.q_sb + h * a.q_sh;
-  const uint16_t *dobase = (const uint16_t *)a.dout + b * a.do_sb + h * a.do_sh;
-  const uint16_t *kbase = (const uint16_t *)a.k + b * a.k_sb + h * a.k_sh;
-  const uint16_t *vbase = (const uint16_t *)a.v + b * a.v_sb + h * a.v_sh;
+  const uint16_t *qbase = (const uint16_t *)a.q + b * a.q_sb + (int64_t)seq0 * a.q_st + h * a.q_sh;
+  const uint16_t *dobase = (const uint16_t *)a.dout + b * a.do_sb + (int64_t)seq0 * a.do_st + h * a.do_sh;
+  const uint16_t *kbase = (const uint16_t *)a.k + b * a.k_sb + (int64_t)seq0 * a.k_st + h * a.k_sh;
+  const uint16_t *vbase = (const uint16_t *)a.v + b * a.v_sb + (int64_t)seq0 * a.v_st + h * a.v_sh;
+  const int64_t lrow = b * a.lse_sb + h * a.lse_sh + seq0;
   const i32x4 qw = buffer_words(qbase, slice_bytes(nq, a.q_st, D, 2));
   const i32x4 dow = buffer_words(dobase, slice_bytes(nq, a.do_st, D, 2));
-  const i32x4 lw = buffer_words(a.lse2 + (int64_t)bh * nq, (uint32_t)nq * 4);
-  const i32x4 dw = buffer_words(a.dpsum + (int64_t)bh * nq, (uint32_t)nq * 4);
+  const i32x4 lw = buffer_words(a.lse2 + lrow, (uint32_t)nq * 4);
+  const i32x4 dw = buffer_words(a.dpsum + lrow, (uint32_t)nq * 4);
   const __amdgpu_buffer_rsrc_t krs = slice_rsrc(kbase, slice_bytes(nk, a.k_st, D, 2));
   const __amdgpu_buffer_rsrc_t vrs = slice_rsrc(vbase, slice_bytes(nk, a.v_st, D, 2));
   const uint32_t qst2 = (uint32_t)a.q_st * 2, dost2 = (uint32_t)a.do_st * 2;
@@ -382,8 +422,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // dK = scale * (dS^T Q), dV = P^T dO; lane = key, d = db*32 + 8*rb + 4*hf + 0..3
   if (my_k < nk) {
     const float sc = a.scale;
-    const int64_t kro = b * a.dk_sb + (int64_t)my_k * a.dk_st + h * a.dk_sh;
-    const int64_t vro = b * a.dv_sb + (int64_t)my_k * a.dv_st + h * a.dv_sh;
+    const int64_t kro = b * a.dk_sb + (int64_t)(seq0 + my_k) * a.dk_st + h * a.dk_sh;
+    const int64_t vro = b * a.dv_sb + (int64_t)(seq0 + my_k) * a.dv_st + h * a.dv_sh;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -426,20 +466,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 31, hf = lane >> 5;
-  const int nq = a.nq, nk = a.nk, off = nk - nq;
   const int causal = a.causal, window = a.window;
 
-  const int nqt = (nq + BR - 1) / BR;
-  const int item = xcd_item(blockIdx.x, nqt * a.heads * a.batch);
-  const int bh = item / nqt, t = item % nqt;
-  const int qt = causal ? nqt - 1 - t : t;
-  const int b = bh / a.heads, h = bh % a.heads;
+  const int nqt = (a.nq + BR - 1) / BR;
+  int b, h, qt;
+  fwd_item(blockIdx.x, nqt, a.heads, a.batch, a.cu_seqlens != nullptr, causal, b, h, qt);
+  int seq0 = 0, nq = a.nq, nk = a.nk;
+  if (a.cu_seqlens) {
+    seq0 = a.cu_seqlens[b];
+    nq = nk = a.cu_seqlens[b + 1] - seq0;
+  }
   const int q0 = qt * BR;
+  if (q0 >= nq) return;  // uniform for the whole work-group
+  const int off = nk - nq;
 
-  const uint16_t *qbase = (const uint16_t *)a.q + b * a.q_sb + h * a.q_sh;
-  const uint16_t *dobase = (const uint16_t *)a.dout + b * a.do_sb + h * a.do_sh;
-  const uint16_t *kbase = (const uint16_t *)a.k + b * a.k_sb + h * a.k_sh;
-  const uint16_t *vbase = (const uint16_t *)a.v + b * a.v_sb + h * a.v_sh;
+  const uint16_t *qbase = (const uint16_t *)a.q + b * a.q_sb + (int64_t)seq0 * a.q_st + h * a.q_sh;
+  const uint16_t *dobase = (const uint16_t *)a.dout + b * a.do_sb + (int64_t)seq0 * a.do_st + h * a.do_sh;
+  const uint16_t *kbase = (const uint16_t *)a.k + b * a.k_sb + (int64_t)seq0 * a.k_st + h * a.k_sh;
+  const uint16_t *vbase = (const uint16_t *)a.v + b * a.v_sb + (int64_t)seq0 * a.v_st + h * a.v_sh;
+  const int64_t lrow = b * a.lse_sb + h * a.lse_sh + seq0;
   const __amdgpu_buffer_rsrc_t qrs = slice_rsrc(qbase, slice_bytes(nq, a.q_st, D, 2));
   const __amdgpu_buffer_rsrc_t dors = slice_rsrc(dobase, slice_bytes(nq, a.do_st, D, 2));
   const i32x4 kw = buffer_words(kbase, slice_bytes(nk, a.k_st, D, 2));
@@ -506,8 +551,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     lse2[qb] = INFINITY;  // rows past the end: P = 0
     dsum[qb] = 0.f;
     if (my_q < nq) {
-      lse2[qb] = a.lse2[(int64_t)bh * nq + my_q];
-      dsum[qb] = a.dpsum[(int64_t)bh * nq + my_q];
+      lse2[qb] = a.lse2[lrow + my_q];
+      dsum[qb] = a.dpsum[lrow + my_q];
     }
   }
 
@@ -706,7 +751,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   for (int qb = 0; qb < 2; ++qb) {
     const int my_q = wq0 + 32 * qb + ql;
     if (my_q < nq) {
-      const int64_t ro = b * a.dq_sb + (int64_t)my_q * a.dq_st + h * a.dq_sh;
+      const int64_t ro = b * a.dq_sb + (int64_t)(seq0 + my_q) * a.dq_st + h * a.dq_sh;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -717,19 +762,214 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 4. The start of every causal sequence: query rows at positions p with
+//    p + (Nk - Nq) < kStartRows, whose visible keys all lie among the first
+//    kStartRows keys.  One work-group per (sequence, head) does this
+//    kStartRows x kStartRows block in fp32: the softmax of each row over all
+//    of its keys, D_i = sum_j P_ij dP_ij, dS = P (dP - D), then writes dQ of
+//    these rows and adds their contributions to dK and dV of the first keys.
+//    Runs after the MFMA kernels, which skipped these rows (lse2 = +inf).
+//    With few keys, P is concentrated and |dS| large; the bf16 dS operand
+//    and a D taken from the bf16 O would then cost these rows most of the
+//    accuracy the gradients have elsewhere.
+// ---------------------------------------------------------------------------
+constexpr int kStartSplit = 4;  // work-groups per (sequence, head), each 1/4 of the head dims
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_start_kernel(BwdArgs a) {
+  constexpr int T = kStartRows, PITCH = D + 8, DCH = D / 8;  // bf16 row pitch (16-byte multiple)
+  constexpr int DS = D / kStartSplit;                         // head dims of this work-group's outputs
+  constexpr int G = DS / 4, RG = 256 / G, RPT = T / RG;       // 4 dims x RPT rows per thread
+  __shared__ __attribute__((aligned(16))) uint16_t qs[T * PITCH], dos[T * PITCH], ks[T * PITCH], vs[T * PITCH];
+  __shared__ float ps[T][T + 1], dss[T][T + 1];  // S then P; dP then dS
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bh = blockIdx.x / kStartSplit, sp = blockIdx.x % kStartSplit;
+  const int b = bh / a.heads, h = bh % a.heads;
+  int seq0 = 0, nq = a.nq, nk = a.nk;
+  if (a.cu_seqlens) {
+    seq0 = a.cu_seqlens[b];
+    nq = nk = a.cu_seqlens[b + 1] - seq0;
+  }
+  const int off = nk - nq;
+  // local row r is query r - off: its last visible key is key r
+  const int r_lo = max(0, off), r_hi = min(T, nq + off), kn = min(nk, T);
+  if (r_lo >= r_hi || kn <= 0) return;  // uniform: no start rows here
+  const int window = a.window;
+  const float scale = a.scale;
+
+  const uint16_t *qg = (const uint16_t *)a.q + b * a.q_sb + h * a.q_sh;
+  const uint16_t *dog = (const uint16_t *)a.dout + b * a.do_sb + h * a.do_sh;
+  const uint16_t *kg = (const uint16_t *)a.k + b * a.k_sb + h * a.k_sh;
+  const uint16_t *vg = (const uint16_t *)a.v + b * a.v_sb + h * a.v_sh;
+  for (int idx = tid; idx < T * DCH; idx += 256) {
+    const int r = idx / DCH, ch = idx % DCH;
+    uint4 q4 = {0u, 0u, 0u, 0u}, o4 = q4, k4 = q4, v4 = q4;
+    if (r >= r_lo && r < r_hi) {
+      const int64_t t = seq0 + r - off;
+      q4 = *(const uint4 *)(qg + t * a.q_st + ch * 8);
+      o4 = *(const uint4 *)(dog + t * a.do_st + ch * 8);
+    }
+    if (r < kn) {
+      const int64_t t = seq0 + r;
+      k4 = *(const uint4 *)(kg + t * a.k_st + ch * 8);
+      v4 = *(const uint4 *)(vg + t * a.v_st + ch * 8);
+    }
+    *(uint4 *)(qs + r * PITCH + ch * 8) = q4;
+    *(uint4 *)(dos + r * PITCH + ch * 8) = o4;
+    *(uint4 *)(ks + r * PITCH + ch * 8) = k4;
+    *(uint4 *)(vs + r * PITCH + ch * 8) = v4;
+  }
+  __syncthreads();
+
+  // S = Q K^T and dP = dO V^T on MFMA (exact bf16 products, fp32 sums): wave
+  // w owns the 32 x 32 block of rows 32 (w / 2), keys 32 (w % 2)
+  {
+    const int r0 = 32 * (wave >> 1), c0 = 32 * (wave & 1), l32 = lane & 31, hf = lane >> 5;
+    f32x16 sacc = {}, dacc = {};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const int col = kk * 16 + hf * 8;
+      sacc = mfma_bf16(*(const uint4 *)(qs + (r0 + l32) * PITCH + col), *(const uint4 *)(ks + (c0 + l32) * PITCH + col),
+                       sacc);
+      dacc = mfma_bf16(*(const uint4 *)(dos + (r0 + l32) * PITCH + col),
+                       *(const uint4 *)(vs + (c0 + l32) * PITCH + col), dacc);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = r0 + 8 * (i / 4) + 4 * hf + i % 4;
+      ps[r][c0 + l32] = sacc[i] * scale;
+      dss[r][c0 + l32] = dacc[i];
+    }
+  }
+  __syncthreads();
+
+  // per row r = tid / 4 (keys c = tid % 4 + 4 j): softmax over the row's
+  // visible keys, D = sum_j P dP, dS = P (dP - D); sums across the 4 lanes
+  {
+    const int r = tid >> 2, part = tid & 3;
+    const bool row_ok = r >= r_lo && r < r_hi;
+    float sv[T / 4], m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < T / 4; ++j) {
+      const int c = part + 4 * j;
+      const bool vis = row_ok && c < kn && c <= r && (window <= 0 || c > r - window);
+      sv[j] = vis ? ps[r][c] : -INFINITY;
+      m = fmaxf(m, sv[j]);
+    }
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    float l = 0.f;
+#pragma unroll
+    for (int j = 0; j < T / 4; ++j) {
+      sv[j] = sv[j] == -INFINITY ? 0.f : expf(sv[j] - m);
+      l += sv[j];
+    }
+    l += __shfl_xor(l, 1);
+    l += __shfl_xor(l, 2);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float dd = 0.f;
+#pragma unroll
+    for (int j = 0; j < T / 4; ++j) {
+      sv[j] *= inv;
+      dd = __builtin_fmaf(sv[j], dss[r][part + 4 * j], dd);
+    }
+    dd += __shfl_xor(dd, 1);
+    dd += __shfl_xor(dd, 2);
+#pragma unroll
+    for (int j = 0; j < T / 4; ++j) {
+      const int c = part + 4 * j;
+      dss[r][c] = sv[j] * (dss[r][c] - dd);  // 0 where P = 0
+      ps[r][c] = sv[j];
+    }
+  }
+  __syncthreads();
+
+  // dQ of the start rows (written: the MFMA kernels left them zero) and their
+  // share of dK, dV of the first keys (added to what those kernels wrote),
+  // in fp32; dims d0..d0+3 of this work-group's slice, rows / keys tg + RG i
+  const int d0 = sp * DS + 4 * (tid % G), tg = tid / G;
+  auto bf4 = [](uint2 w, float (&x)[4]) __attribute__((always_inline)) {
+    x[0] = bf16_to_f32(w.x & 0xffffu);
+    x[1] = bf16_to_f32(w.x >> 16);
+    x[2] = bf16_to_f32(w.y & 0xffffu);
+    x[3] = bf16_to_f32(w.y >> 16);
+  };
+  {
+    float acc[RPT][4] = {};
+#pragma unroll 8
+    for (int c = 0; c < kn; ++c) {
+      float kx[4];
+      bf4(*(const uint2 *)(ks + c * PITCH + d0), kx);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const float ds = dss[tg + RG * i][c];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) acc[i][x] = __builtin_fmaf(ds, kx[x], acc[i][x]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = tg + RG * i;
+      if (r >= r_lo && r < r_hi)
+        store_grad4(a.dq, b * a.dq_sb + (int64_t)(seq0 + r - off) * a.dq_st + h * a.dq_sh + d0, a.grad_f32,
+                    scale * acc[i][0], scale * acc[i][1], scale * acc[i][2], scale * acc[i][3]);
+    }
+  }
+  {
+    float gk[RPT][4] = {}, gv[RPT][4] = {};
+#pragma unroll 8
+    for (int r = r_lo; r < r_hi; ++r) {
+      float qx[4], ox[4];
+      bf4(*(const uint2 *)(qs + r * PITCH + d0), qx);
+      bf4(*(const uint2 *)(dos + r * PITCH + d0), ox);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const float ds = dss[r][tg + RG * i], p = ps[r][tg + RG * i];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          gk[i][x] = __builtin_fmaf(ds, qx[x], gk[i][x]);
+          gv[i][x] = __builtin_fmaf(p, ox[x], gv[i][x]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int c = tg + RG * i;
+      if (c < kn) {
+        const int64_t ko = b * a.dk_sb + (int64_t)(seq0 + c) * a.dk_st + h * a.dk_sh + d0;
+        const int64_t vo = b * a.dv_sb + (int64_t)(seq0 + c) * a.dv_st + h * a.dv_sh + d0;
+        float k4[4], v4[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          k4[x] = load_grad(a.dk, ko + x, a.grad_f32) + scale * gk[i][x];
+          v4[x] = load_grad(a.dv, vo + x, a.grad_f32) + gv[i][x];
+        }
+        store_grad4(a.dk, ko, a.grad_f32, k4[0], k4[1], k4[2], k4[3]);
+        store_grad4(a.dv, vo, a.grad_f32, v4[0], v4[1], v4[2], v4[3]);
+      }
+    }
+  }
+}
+
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t s) {
   constexpr int NW_KV = 4;
-  const int64_t rows = (int64_t)a.batch * a.heads * a.nq;
+  // D and lse2 of every row: [batch, heads, nq], or heads x total_tokens
+  // rows for a packed call (its lse layout)
+  const int64_t rows = a.cu_seqlens ? (int64_t)a.heads * a.lse_sh : (int64_t)a.batch * a.heads * a.nq;
   if (rows > 0) {
     constexpr int RPB = 256 / (D / 8);
-    hipLaunchKernelGGL((bwd_dsum_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_dsum_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, a, rows);
   }
   const int64_t kv_items = (int64_t)((a.nk + 32 * NW_KV - 1) / (32 * NW_KV)) * a.heads * a.batch;
   if (kv_items > 0)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)kv_items), dim3(NW_KV * 64), 0, s, a);
   const int64_t q_items = (int64_t)((a.nq + 256 - 1) / 256) * a.heads * a.batch;
   if (q_items > 0) hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)q_items), dim3(256), 0, s, a);
+  const int64_t start_items = (int64_t)a.batch * a.heads * kStartSplit;
+  if (a.causal && start_items > 0 && a.nq > 0 && a.nk > 0)
+    hipLaunchKernelGGL((bwd_start_kernel<D>), dim3((unsigned)start_items), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -27,13 +27,17 @@ struct FwdArgs {
   float v_descale;               // fp8 only, 1 otherwise
 };
 
-// Kernel-side view of one backward call (dense).
+// Kernel-side view of one backward call.  Packed varlen calls set
+// cu_seqlens, zero batch strides, batch = number of sequences and
+// nq = nk = max_seqlen (grid sizing only).
 struct BwdArgs {
   const void *q, *k, *v, *o, *dout;
   const float *lse;
   void *dq, *dk, *dv;
-  float *dpsum;      // workspace: D_i = rowsum(dO * O), [batch, heads, nq] fp32
-  float *lse2;       // workspace: LSE_i * log2(e) (+inf for rows that see no key), same shape
+  const int32_t *cu_seqlens;  // null for dense calls
+  float *dpsum;      // workspace: D_i = rowsum(dO * O), laid out like lse
+  float *lse2;       // workspace: LSE_i * log2(e) (+inf for rows that see no key), laid out like lse
+  int64_t lse_sb, lse_sh;  // lse / dpsum / lse2 element strides: batch, head (token stride 1)
   int64_t q_sb, q_st, q_sh, k_sb, k_st, k_sh, v_sb, v_st, v_sh, o_sb, o_st, o_sh;
   int64_t do_sb, do_st, do_sh, dq_sb, dq_st, dq_sh, dk_sb, dk_st, dk_sh, dv_sb, dv_st, dv_sh;
   int32_t batch, heads, nq, nk;

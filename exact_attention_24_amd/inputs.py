@@ -13,6 +13,8 @@ Workloads (the shapes of the pages' examples and model configurations):
                  causal + window 4096 (packing of mixed lengths, ms-swift
                  long-text page section 5.1)
   bwd_n8192      B1 H32 N8192 d128, bf16 Q/K/V/dO, causal
+  varlen_bwd_32k the varlen_32k packing (same seed, so the same lengths and
+                 Q/K/V) plus a bf16 dO, for the packed backward
   fp8_n8192      same shape, e4m3 Q/K/V with per-tensor scales, causal
 
 Recipe: one ``torch.Generator('cpu')`` per workload seeded with its seed;
@@ -58,6 +60,8 @@ WORKLOADS = {
     "varlen_32k": Workload("varlen_32k", 1, 28, 8192, 128, "bf16", True, window=4096, seed=1004,
                            varlen_total=32768),
     "bwd_n8192": Workload("bwd_n8192", 1, 32, 8192, 128, "bf16", True, seed=1005),
+    "varlen_bwd_32k": Workload("varlen_bwd_32k", 1, 28, 8192, 128, "bf16", True, window=4096, seed=1004,
+                               varlen_total=32768),
     "fp8_n8192": Workload("fp8_n8192", 1, 32, 8192, 128, "fp8", True, seed=1005),
 }
 
@@ -105,14 +109,17 @@ def cu_seqlens_of(lengths) -> torch.Tensor:
     return torch.from_numpy(cu.astype(np.int32))
 
 
-def varlen_inputs(lengths, heads, head_dim, dtype="bf16", seed=0):
-    """Packed Q/K/V [total, H, d] and cu_seqlens for the given lengths."""
+def varlen_inputs(lengths, heads, head_dim, dtype="bf16", seed=0, with_dout=False):
+    """Packed Q/K/V [total, H, d] and cu_seqlens for the given lengths (then dO)."""
     gen = torch.Generator("cpu").manual_seed(seed)
     total = int(sum(lengths))
     q = randn(gen, (total, heads, head_dim), dtype)
     k = randn(gen, (total, heads, head_dim), dtype)
     v = randn(gen, (total, heads, head_dim), dtype)
-    return q, k, v, cu_seqlens_of(lengths)
+    if not with_dout:
+        return q, k, v, cu_seqlens_of(lengths)
+    do = randn(gen, (total, heads, head_dim), dtype)
+    return q, k, v, cu_seqlens_of(lengths), do
 
 
 def quantize_e4m3(x: torch.Tensor):
@@ -138,18 +145,21 @@ def workload_inputs(name: str, seqlen: int | None = None, heads: int | None = No
     w = WORKLOADS[name]
     n = w.seqlen if seqlen is None else seqlen
     h = w.heads if heads is None else heads
+    with_do = "bwd" in name
     if w.varlen_total:
         total = w.varlen_total if seqlen is None else seqlen
         lengths = varlen_lengths(total, w.seed)
-        q, k, v, cu = varlen_inputs(lengths, h, w.head_dim, w.dtype, w.seed)
-        return {"q": q, "k": k, "v": v, "cu_seqlens": cu, "lengths": lengths}
+        t = varlen_inputs(lengths, h, w.head_dim, w.dtype, w.seed, with_dout=with_do)
+        d = {"q": t[0], "k": t[1], "v": t[2], "cu_seqlens": t[3], "lengths": lengths}
+        if with_do:
+            d["dout"] = t[4]
+        return d
     if w.dtype == "fp8":
         q, k, v = dense_inputs(w.batch, n, h, w.head_dim, "bf16", w.seed)
         q8, sq = quantize_e4m3(q)
         k8, sk = quantize_e4m3(k)
         v8, sv = quantize_e4m3(v)
         return {"q8": q8, "k8": k8, "v8": v8, "q_scale": sq, "k_scale": sk, "v_scale": sv}
-    with_do = name.startswith("bwd")
     t = dense_inputs(w.batch, n, h, w.head_dim, w.dtype, w.seed, with_dout=with_do)
     d = {"q": t[0], "k": t[1], "v": t[2]}
     if with_do:

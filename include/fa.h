@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 typedef enum {
   FA_F32 = 0,       /* IEEE binary32 */
@@ -142,11 +142,38 @@ typedef struct {
   int32_t causal, window, deterministic;
 } fa_bwd_params;
 
+/* Packed variable-length backward: the gradients of fa_varlen_fwd, by the
+ * same recomputation as fa_bwd (packed sequences: ms-swift long-text page
+ * sections 4.3 and 5.1; recomputation: ms-swift integration page).
+ *   q, k, v, o, dout [total_tokens, heads, head_dim] bf16; x_stride = {token, head}.
+ *   lse [heads, total_tokens] fp32 contiguous, as written by fa_varlen_fwd.
+ *   dq, dk, dv [total_tokens, heads, head_dim] in grad_dtype (FA_F32 or FA_BF16).
+ *   cu_seqlens, max_seqlen: as in fa_varlen_fwd, with the same unchecked
+ *   device-side contracts.  Every token of every sequence gets its dq, dk,
+ *   dv written (zero for a token that neither sees nor is seen by any other).
+ *   deterministic: accepted for symmetry with fa_bwd; this path never uses
+ *   atomics, so repeated calls are always bitwise identical.
+ *   workspace: fa_varlen_bwd_workspace_bytes(p) bytes of device memory,
+ *   256-byte aligned, owned by the caller; contents on entry are ignored. */
+typedef struct {
+  const void *q, *k, *v, *o, *dout;
+  const float *lse;
+  void *dq, *dk, *dv;
+  const int32_t *cu_seqlens;
+  fa_dtype qkv_dtype, grad_dtype;
+  int32_t num_seqs, total_tokens, max_seqlen, heads, head_dim;
+  int64_t q_stride[2], k_stride[2], v_stride[2], o_stride[2], do_stride[2];
+  int64_t dq_stride[2], dk_stride[2], dv_stride[2];
+  float softmax_scale;
+  int32_t causal, window, deterministic;
+} fa_varlen_bwd_params;
+
 /* Host-only validation: never touches a device.  Returns the status the
  * corresponding entry point would return before launching anything. */
 fa_status fa_check_fwd(const fa_fwd_params *p);
 fa_status fa_check_varlen_fwd(const fa_varlen_fwd_params *p);
 fa_status fa_check_bwd(const fa_bwd_params *p);
+fa_status fa_check_varlen_bwd(const fa_varlen_bwd_params *p);
 
 /* Enqueue the forward: writes o (and lse when non-NULL). */
 fa_status fa_fwd(const fa_fwd_params *p, void *stream);
@@ -160,6 +187,12 @@ size_t fa_bwd_workspace_bytes(const fa_bwd_params *p);
 
 /* Enqueue the backward: writes dq, dk, dv. */
 fa_status fa_bwd(const fa_bwd_params *p, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace fa_varlen_bwd needs (0 on invalid parameters). */
+size_t fa_varlen_bwd_workspace_bytes(const fa_varlen_bwd_params *p);
+
+/* Enqueue the packed variable-length backward: writes dq, dk, dv. */
+fa_status fa_varlen_bwd(const fa_varlen_bwd_params *p, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Thread-local description of the last non-FA_OK status ("" if none). */
 const char *fa_last_error(void);

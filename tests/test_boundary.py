@@ -31,8 +31,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("fa_fwd", "fa_varlen_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_check_fwd",
-              "fa_check_varlen_fwd", "fa_check_bwd", "fa_last_error", "fa_abi_version"):
+    for n in ("fa_fwd", "fa_varlen_fwd", "fa_bwd", "fa_varlen_bwd", "fa_bwd_workspace_bytes",
+              "fa_varlen_bwd_workspace_bytes", "fa_check_fwd", "fa_check_varlen_fwd", "fa_check_bwd",
+              "fa_check_varlen_bwd", "fa_last_error", "fa_abi_version"):
         assert n in names
 
 
@@ -146,6 +147,35 @@ def test_bwd_checks(lib):
     p = B.make_bwd_params(q, q, q, q, q, lse, g, g, g)
     p.deterministic = 5
     assert lib.fa_check_bwd(ctypes.byref(p)) == B.FA_ERR_INVALID_ARGUMENT
+
+
+def test_varlen_bwd_checks(lib):
+    q = torch.zeros(40, 2, 128, dtype=torch.bfloat16)
+    g = torch.zeros(40, 2, 128, dtype=torch.float32)
+    lse = torch.zeros(2, 40, dtype=torch.float32)
+    cu = torch.tensor([0, 10, 40], dtype=torch.int32)
+    p = B.make_varlen_bwd_params(q, q, q, q, q, lse, g, g, g, cu, 30, causal=True, window=8)
+    assert lib.fa_check_varlen_bwd(ctypes.byref(p)) == B.FA_OK
+    # D and LSE*log2(e), each [heads, total_tokens] fp32 = 320 bytes, rounded up to 512
+    assert lib.fa_varlen_bwd_workspace_bytes(ctypes.byref(p)) == 1024
+    p.max_seqlen = 41
+    assert lib.fa_check_varlen_bwd(ctypes.byref(p)) == B.FA_ERR_INVALID_ARGUMENT
+    assert b"exceeds total_tokens" in lib.fa_last_error()
+    assert lib.fa_varlen_bwd_workspace_bytes(ctypes.byref(p)) == 0
+    for field, value, code in (("cu_seqlens", None, B.FA_ERR_INVALID_ARGUMENT),
+                               ("lse", None, B.FA_ERR_INVALID_ARGUMENT),
+                               ("qkv_dtype", B.FA_FP8_E4M3, B.FA_ERR_UNSUPPORTED),
+                               ("grad_dtype", B.FA_FP8_E4M3, B.FA_ERR_DTYPE_MISMATCH),
+                               ("window", -1, B.FA_ERR_INVALID_ARGUMENT),
+                               ("head_dim", 32, B.FA_ERR_UNSUPPORTED)):
+        p = B.make_varlen_bwd_params(q, q, q, q, q, lse, g, g, g, cu, 30)
+        setattr(p, field, value)
+        assert lib.fa_check_varlen_bwd(ctypes.byref(p)) == code, field
+    p = B.make_varlen_bwd_params(q, q, q, q, q, lse, g, g, g, cu, 30)
+    p.dq_stride[0] = 100  # fp32 rows 400 bytes apart: not 16-byte aligned
+    assert lib.fa_check_varlen_bwd(ctypes.byref(p)) == B.FA_ERR_INVALID_ARGUMENT
+    with pytest.raises(ValueError, match="lse"):
+        B.make_varlen_bwd_params(q, q, q, q, q, lse.t(), g, g, g, cu, 30)
 
 
 def test_python_layer_error_mapping(lib):

@@ -28,6 +28,18 @@ What is computed, and where the pages define it
   max m and exponent sum l, combined in a numerically stable way), with the
   tile loop of section 2.2.1.  It exists to pin that the tiled recombination
   equals the direct softmax; it is not the GPU algorithm.
+* ``merge_partials``: attention results over disjoint key subsets, each
+  normalised over its own keys and carried as (O_p, LSE_p), combined into the
+  result over the union.  This is the stable combination of per-block max m
+  and exponent sum l of jsqmd.com section 2.2.2, with each part written as
+  LSE_p = m_p + ln l_p; it is also the step that joins the local results of
+  ring attention (the Ring-Attention paragraph of the ms-swift integration
+  page).
+* ``kvcache_fwd``: incremental decoding against a KV cache, the
+  ``flash_attn_with_kvcache(q, k_cache, v_cache, k, v, cache_seqlens, causal)``
+  example of the MindSpore page (推理优化与KV缓存): the new k, v are written into
+  the cache at position cache_seqlens, then q attends over the cache up to and
+  including them.
 * fp8: ``e4m3_decode`` follows the OCP 8-bit floating point specification for
   E4M3 (bias 7, no infinities, S.1111.111 is NaN, max finite 448); the fp8
   forward is the plain definition applied to code * per-tensor scale (FA-3 FP8
@@ -41,6 +53,10 @@ Readings where the pages are silent
 * Causal with Nq != Nk is bottom-right aligned: query i sits at key position
   i + Nk - Nq.
 * A query row with no visible key gets O = 0 and LSE = -inf.
+* KV cache: with new keys, batch b sees keys 0 .. cache_seqlens[b] + Nq - 1
+  (the Nq new ones last); without, keys 0 .. cache_seqlens[b] - 1.  The Nq
+  queries are the last Nq positions (bottom-right causal).  Cache rows past
+  that length are never read.
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against closed
 forms, hand-derived golden values, finite differences, invariants and
@@ -61,6 +77,8 @@ __all__ = [
     "mha_bwd",
     "varlen_fwd",
     "varlen_bwd",
+    "merge_partials",
+    "kvcache_fwd",
     "e4m3_decode",
     "fp8_dequant",
 ]
@@ -280,6 +298,59 @@ def varlen_bwd(q, k, v, dout, cu_seqlens, scale, causal=False, window=0, heads=N
             dq[a:b, h], dk[a:b, h], dv[a:b, h] = attention_bwd(q[a:b, h], k[a:b, h], v[a:b, h], dout[a:b, h],
                                                                scale, causal, window)
     return dq, dk, dv
+
+
+def merge_partials(o_parts, lse_parts):
+    """Combine P partial results: o_parts [P, ..., dv], lse_parts [P, ...].
+
+    Part p is attention over its own key subset: O_p normalised over those
+    keys, LSE_p = m_p + ln l_p (natural log).  Over the union of the subsets,
+    LSE = ln sum_p exp(LSE_p) and O = sum_p exp(LSE_p - LSE) O_p, evaluated
+    relative to the largest LSE_p so that no exponent overflows.  Parts with
+    LSE_p = -inf saw no key and add nothing; if every part is -inf, O = 0 and
+    LSE = -inf.  Returns (O [..., dv], LSE [...]).
+    """
+    o = np.asarray(o_parts, dtype=np.float64)
+    lse = np.asarray(lse_parts, dtype=np.float64)
+    m = lse.max(axis=0)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    w = np.exp(lse - m_safe[None])          # [P, ...]; 0 for -inf parts
+    tot = w.sum(axis=0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        lse_out = np.where(tot > 0, m_safe + np.log(tot), -np.inf)
+        frac = np.where(tot[None] > 0, w / tot[None], 0.0)
+    o_out = (frac[..., None] * np.where(frac[..., None] > 0, o, 0.0)).sum(axis=0)
+    return o_out, lse_out
+
+
+def kvcache_fwd(q, k_cache, v_cache, cache_seqlens, scale, causal=False, window=0, k_new=None, v_new=None):
+    """Decode step against a KV cache, dense [B, N, H, d] layout.
+
+    q [B, Nq, H, d]; k_cache, v_cache [B, Lmax, H, d]; cache_seqlens [B] ints.
+    With k_new, v_new [B, Nq, H, d]: copies of the caches get them at rows
+    cache_seqlens[b] .. cache_seqlens[b] + Nq - 1, and batch b attends over
+    the first cache_seqlens[b] + Nq rows; without, over the first
+    cache_seqlens[b].  Returns (O [B, Nq, H, dv], LSE [B, H, Nq], k_cache',
+    v_cache').
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kc = np.array(k_cache, dtype=np.float64)
+    vc = np.array(v_cache, dtype=np.float64)
+    b_, nq, h_, _ = q.shape
+    lens = np.asarray(cache_seqlens, dtype=np.int64).reshape(-1)
+    if k_new is not None:
+        kn = np.asarray(k_new, dtype=np.float64)
+        vn = np.asarray(v_new, dtype=np.float64)
+        for b in range(b_):
+            kc[b, lens[b]:lens[b] + nq] = kn[b]
+            vc[b, lens[b]:lens[b] + nq] = vn[b]
+    o = np.zeros((b_, nq, h_, vc.shape[3]))
+    lse = np.zeros((b_, h_, nq))
+    for b in range(b_):
+        nk = int(lens[b]) + (nq if k_new is not None else 0)
+        for h in range(h_):
+            o[b, :, h], lse[b, h] = attention_fwd(q[b, :, h], kc[b, :nk, h], vc[b, :nk, h], scale, causal, window)
+    return o, lse, kc, vc
 
 
 def e4m3_decode(codes):

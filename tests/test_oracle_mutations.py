@@ -60,6 +60,31 @@ def _blocked_no_rescale(q, k, v, scale, causal=False, window=0, br=16, bc=16):
     return o, lse
 
 
+def _merge_unnormalised(o_parts, lse_parts):
+    o = np.asarray(o_parts, dtype=np.float64)
+    lse = np.asarray(lse_parts, dtype=np.float64)
+    m = lse.max(axis=0)
+    w = np.exp(lse - m[None])
+    return (w[..., None] * o).sum(axis=0), m + np.log(w.sum(axis=0))  # weights not divided by their sum
+
+
+def _merge_lse_without_max(o_parts, lse_parts):
+    o, _ = _ORIG_MERGE(o_parts, lse_parts)
+    lse = np.asarray(lse_parts, dtype=np.float64)
+    return o, np.log(np.exp(lse - lse.max(axis=0)[None]).sum(axis=0))  # the max is not added back
+
+
+def _kvcache_forgets_new_keys(q, k_cache, v_cache, cache_seqlens, scale, causal=False, window=0, k_new=None,
+                              v_new=None):
+    # appends, but attends over the old length only
+    o, lse, kc, vc = _ORIG_KVCACHE(q, k_cache, v_cache, cache_seqlens, scale, causal, window, k_new, v_new)
+    o2, lse2, _, _ = _ORIG_KVCACHE(q, kc, vc, np.maximum(np.asarray(cache_seqlens), 1), scale, causal, window)
+    return o2, lse2, kc, vc
+
+
+_ORIG_MERGE = oa.merge_partials
+_ORIG_KVCACHE = oa.kvcache_fwd
+
 MUTATIONS = [
     ("visible", _wrong_visible_offset, lambda: pins.test_forward_matches_torch_sdpa(17, 29, True, 0)),
     ("visible", _wrong_window, lambda: pins.test_scale_zero_is_mean_over_visible_keys(True, 4)),
@@ -68,6 +93,11 @@ MUTATIONS = [
     ("attention_bwd", _bwd_drops_d, lambda: pins.test_backward_identities(True, 0)),
     ("blocked_fwd", _blocked_no_rescale,
      lambda: pins.test_blocked_online_softmax_equals_direct(37, 8, 5, False, 0)),
+    ("merge_partials", _merge_unnormalised, lambda: pins.test_merge_closed_forms()),
+    ("merge_partials", _merge_lse_without_max,
+     lambda: pins.test_merge_of_key_chunks_equals_full_attention(False, 0, [0, 7, 19, 40])),
+    ("kvcache_fwd", _kvcache_forgets_new_keys,
+     lambda: pins.test_kvcache_decode_equals_rows_of_the_full_sequence(1, True, 0)),
 ]
 
 

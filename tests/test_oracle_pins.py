@@ -353,3 +353,120 @@ def test_e4m3_decode_all_codes_match_torch():
 def test_fp8_dequant():
     codes = np.array([0x38, 0x40, 0xB8], dtype=np.uint8)  # 1, 2, -1
     np.testing.assert_array_equal(oracle.fp8_dequant(codes, 0.5), [0.5, 1.0, -0.5])
+
+
+# --------------------------------------------------------------------------
+# merge of partial (O, LSE) results
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("causal,window,cuts", [
+    (False, 0, [0, 7, 19, 40]), (True, 0, [0, 13, 14, 40]), (True, 6, [0, 5, 22, 31, 40]), (False, 0, [0, 40]),
+])
+def test_merge_of_key_chunks_equals_full_attention(causal, window, cuts):
+    """Attention over contiguous key chunks, each computed by torch's CPU routine
+    (with torch.logsumexp for its LSE), merged by the oracle, equals torch's
+    attention over all keys.  Chunks that a row cannot see give LSE = -inf."""
+    g = torch.Generator().manual_seed(len(cuts) * 31 + window)
+    n, d = 40, 12
+    q = torch.randn(n, d, generator=g, dtype=torch.float64)
+    k = torch.randn(n, d, generator=g, dtype=torch.float64)
+    v = torch.randn(n, 9, generator=g, dtype=torch.float64)
+    mask = _torch_mask(n, n, causal, window)
+    s = (0.4 * q @ k.T).masked_fill(~mask, float("-inf"))
+    o_parts, lse_parts = [], []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        lse_p = torch.logsumexp(s[:, a:b], dim=1)
+        p = torch.softmax(s[:, a:b], dim=1).nan_to_num(0.0)  # rows that see none of these keys: 0
+        o_parts.append((p @ v[a:b]).numpy())
+        lse_parts.append(lse_p.numpy())
+    o, lse = oracle.merge_partials(np.stack(o_parts), np.stack(lse_parts))
+    ref = F.scaled_dot_product_attention(q[None], k[None], v[None], attn_mask=mask[None], scale=0.4)[0]
+    np.testing.assert_allclose(o, ref.numpy(), atol=1e-12)
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=1).numpy(), atol=1e-12)
+
+
+def test_merge_closed_forms():
+    rng = np.random.default_rng(5)
+    o1 = rng.standard_normal((3, 4, 6))
+    l1 = rng.standard_normal((3, 4))
+    # one part: identity
+    o, lse = oracle.merge_partials(o1[None], l1[None])
+    np.testing.assert_allclose(o, o1, atol=1e-15)
+    np.testing.assert_allclose(lse, l1, atol=1e-15)
+    # two equal parts: the same O, LSE + ln 2
+    o, lse = oracle.merge_partials(np.stack([o1, o1]), np.stack([l1, l1]))
+    np.testing.assert_allclose(o, o1, atol=1e-14)
+    np.testing.assert_allclose(lse, l1 + math.log(2), atol=1e-14)
+    # weights exp(LSE_p - LSE): with LSEs ln 1 and ln 3, O = (O_1 + 3 O_2) / 4, LSE = ln 4
+    o2 = rng.standard_normal((3, 4, 6))
+    o, lse = oracle.merge_partials(np.stack([o1, o2]), np.stack([np.zeros((3, 4)), np.full((3, 4), math.log(3))]))
+    np.testing.assert_allclose(o, (o1 + 3 * o2) / 4, atol=1e-14)
+    np.testing.assert_allclose(lse, math.log(4), atol=1e-14)
+    # a part with LSE = -inf adds nothing, whatever its O holds; all -inf gives 0 and -inf
+    junk = np.full_like(o1, 1e300)
+    o, lse = oracle.merge_partials(np.stack([o1, junk]), np.stack([l1, np.full((3, 4), -np.inf)]))
+    np.testing.assert_allclose(o, o1, atol=1e-15)
+    np.testing.assert_allclose(lse, l1, atol=1e-15)
+    o, lse = oracle.merge_partials(np.stack([junk, junk]), np.full((2, 3, 4), -np.inf))
+    assert (o == 0).all() and np.isneginf(lse).all()
+    # a common shift of every LSE_p leaves O alone and shifts LSE; no overflow at 1000
+    o, lse = oracle.merge_partials(np.stack([o1, o2]), np.stack([l1 + 1000.0, l1 + 1000.0 + math.log(3)]))
+    np.testing.assert_allclose(o, (o1 + 3 * o2) / 4, atol=1e-13)
+    np.testing.assert_allclose(lse, l1 + 1000.0 + math.log(4), atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# KV-cache decode
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("nq,causal,window", [(1, True, 0), (3, True, 0), (2, True, 4), (1, False, 0)])
+def test_kvcache_decode_equals_rows_of_the_full_sequence(nq, causal, window):
+    """Decoding the last nq tokens of a sequence against a cache holding the
+    earlier ones (plus the appended new keys) gives the last nq rows of the
+    full-sequence attention computed by torch's CPU routine.  Cache rows past
+    the valid length hold NaN, so reading them would show."""
+    g = torch.Generator().manual_seed(nq * 10 + window)
+    lens = [9, 0, 17]  # tokens already cached per batch entry
+    lmax, h, d = 24, 2, 8
+    b_ = len(lens)
+    x_q = torch.randn(b_, lmax, h, d, generator=g, dtype=torch.float64)
+    x_k = torch.randn(b_, lmax, h, d, generator=g, dtype=torch.float64)
+    x_v = torch.randn(b_, lmax, h, d, generator=g, dtype=torch.float64)
+    k_cache = torch.full((b_, lmax, h, d), float("nan"), dtype=torch.float64)
+    v_cache = torch.full((b_, lmax, h, d), float("nan"), dtype=torch.float64)
+    q = torch.empty(b_, nq, h, d, dtype=torch.float64)
+    k_new = torch.empty(b_, nq, h, d, dtype=torch.float64)
+    v_new = torch.empty(b_, nq, h, d, dtype=torch.float64)
+    for b, t in enumerate(lens):
+        k_cache[b, :t], v_cache[b, :t] = x_k[b, :t], x_v[b, :t]
+        q[b], k_new[b], v_new[b] = x_q[b, t:t + nq], x_k[b, t:t + nq], x_v[b, t:t + nq]
+    o, lse, kc, vc = oracle.kvcache_fwd(q.numpy(), k_cache.numpy(), v_cache.numpy(), lens, 0.3, causal, window,
+                                        k_new.numpy(), v_new.numpy())
+    for b, t in enumerate(lens):
+        n = t + nq
+        np.testing.assert_array_equal(kc[b, :n], x_k[b, :n].numpy())
+        np.testing.assert_array_equal(vc[b, :n], x_v[b, :n].numpy())
+        assert np.isnan(kc[b, n:]).all()
+        mask = _torch_mask(n, n, causal, window)
+        for hh in range(h):
+            ref = F.scaled_dot_product_attention(x_q[b, :n, hh][None], x_k[b, :n, hh][None], x_v[b, :n, hh][None],
+                                                 attn_mask=mask[None], scale=0.3)[0]
+            np.testing.assert_allclose(o[b, :, hh], ref[t:].numpy(), atol=1e-12)
+            s = (0.3 * x_q[b, :n, hh] @ x_k[b, :n, hh].T).masked_fill(~mask, float("-inf"))
+            np.testing.assert_allclose(lse[b, hh], torch.logsumexp(s, dim=1)[t:].numpy(), atol=1e-12)
+
+
+def test_kvcache_without_new_keys_reads_the_first_seqlen_rows():
+    """No new k, v: the queries attend over cache rows 0 .. seqlen-1 only, as
+    the last nq positions of that key range; brute-force loops on a tiny case."""
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((1, 2, 1, 3))
+    kc = rng.standard_normal((1, 6, 1, 3))
+    vc = rng.standard_normal((1, 6, 1, 3))
+    kc[0, 4:], vc[0, 4:] = np.nan, np.nan
+    o, lse, _, _ = oracle.kvcache_fwd(q, kc, vc, [4], 0.5, causal=True)
+    for i in range(2):
+        pos = 4 - 2 + i  # bottom-right: query i sits at key position i + Nk - Nq
+        w = [math.exp(0.5 * sum(q[0, i, 0, c] * kc[0, j, 0, c] for c in range(3))) for j in range(pos + 1)]
+        tot = sum(w)
+        for c in range(3):
+            assert abs(o[0, i, 0, c] - sum(w[j] * vc[0, j, 0, c] for j in range(pos + 1)) / tot) < 1e-12
+        assert abs(lse[0, 0, i] - math.log(tot)) < 1e-12

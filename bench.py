@@ -126,6 +126,21 @@ def cpu_baseline(budget_s=15.0):
             "seconds": round(el, 2)}
 
 
+MERGE_PARTS = 8
+
+
+def merge_inputs(torch):
+    """8 fp32 partial results of the B1 N8192 H32 d128 forward (ring-attention
+    shape: one per key segment), seeded, resident in HBM."""
+    g = torch.Generator(device="cuda").manual_seed(1006)
+    o_p = torch.randn(MERGE_PARTS, 1, 8192, 32, 128, generator=g, device="cuda")
+    lse_p = 4.0 * torch.randn(MERGE_PARTS, 1, 32, 8192, generator=g, device="cuda")
+    out = torch.empty(1, 8192, 32, 128, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(1, 32, 8192, dtype=torch.float32, device="cuda")
+    nbytes = o_p.numel() * 4 + lse_p.numel() * 4 + out.numel() * 2 + lse.numel() * 4
+    return o_p, lse_p, out, lse, nbytes
+
+
 def extra_rows(torch, fa, steps):
     """Timings of the other hot-path rows (median per call, HIP events)."""
     from exact_attention_24_amd.inputs import WORKLOADS, workload_inputs
@@ -176,6 +191,16 @@ def extra_rows(torch, fa, steps):
         rows["varlen_bwd_32k_w4096"] = {"ms": round(med(ms), 4), "tflops": round(f / med(ms) / 1e9, 1)}
     except Exception as e:
         rows["varlen_bwd_32k_w4096"] = {"error": str(e)[:120]}
+    # merge of partial results
+    try:
+        o_p, lse_p, out, lse, nbytes = merge_inputs(torch)
+        _, ms = time_calls(lambda: fa.fa_merge(o_p, lse_p, out=out, lse=lse), 2, steps, torch)
+        gbs = nbytes / med(ms) / 1e6
+        rows["merge_8parts_n8192"] = {"ms": round(med(ms), 4), "GB/s": round(gbs, 1),
+                                      "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        del o_p, lse_p, out, lse
+    except Exception as e:
+        rows["merge_8parts_n8192"] = {"error": str(e)[:120]}
     # fp8 forward
     try:
         t = workload_inputs("fp8_n8192")
@@ -190,12 +215,12 @@ def extra_rows(torch, fa, steps):
     return rows
 
 
-WORKLOAD_CHOICES = ("fwd_causal", "fwd_noncausal", "bwd", "varlen", "varlen_bwd", "fp8")
+WORKLOAD_CHOICES = ("fwd_causal", "fwd_noncausal", "bwd", "varlen", "varlen_bwd", "fp8", "merge")
 
 
 def make_step(name, torch, fa):
-    """(step fn, FLOPs per step, description, dtype, peak TFLOP/s, kernel source) of a workload,
-    inputs generated and moved to HBM before timing."""
+    """(step fn, work per step, description, dtype, peak, kernel source, unit) of a workload, inputs
+    generated and moved to HBM before timing; work is FLOPs (unit TFLOP/s) or bytes (unit GB/s)."""
     from exact_attention_24_amd.inputs import WORKLOADS, workload_inputs
     if name in ("fwd_causal", "fwd_noncausal"):
         causal = name == "fwd_causal"
@@ -206,14 +231,14 @@ def make_step(name, torch, fa):
         lse = torch.empty((1, w.heads, w.seqlen), dtype=torch.float32, device="cuda")
         desc = f"fwd B1 H32 N8192 d128 bf16 {'causal' if causal else 'non-causal'} (Llama-7B attention shape)"
         return (lambda: fa.fa_fwd(q, k, v, causal=causal, out=o, lse=lse),
-                fwd_flops(1, 32, 8192, 128, causal), desc, "bf16", PEAK_BF16_TFLOPS, "fa_fwd.hip")
+                fwd_flops(1, 32, 8192, 128, causal), desc, "bf16", PEAK_BF16_TFLOPS, "fa_fwd.hip", "TFLOP/s")
     if name == "bwd":
         t = {k_: v_.cuda() for k_, v_ in workload_inputs("bwd_n8192").items()}
         o, lse = fa.fa_fwd(t["q"], t["k"], t["v"], causal=True)
         dq, dk, dv = (torch.empty(t[x].shape, dtype=torch.float32, device="cuda") for x in ("q", "k", "v"))
         return (lambda: fa.fa_bwd(t["dout"], t["q"], t["k"], t["v"], o, lse, causal=True, dq=dq, dk=dk, dv=dv),
                 2.5 * fwd_flops(1, 32, 8192, 128, True), "bwd B1 H32 N8192 d128 bf16 causal, fp32 gradients",
-                "bf16", PEAK_BF16_TFLOPS, "fa_bwd.hip")
+                "bf16", PEAK_BF16_TFLOPS, "fa_bwd.hip", "TFLOP/s")
     if name == "varlen":
         w = WORKLOADS["varlen_32k"]
         t = workload_inputs("varlen_32k")
@@ -221,7 +246,8 @@ def make_step(name, torch, fa):
         mx = max(t["lengths"])
         f = 4.0 * w.head_dim * w.heads * visible_pairs_varlen(t["lengths"], True, w.window)
         return (lambda: fa.fa_varlen_fwd(q, k, v, cu, mx, causal=True, window=w.window), f,
-                "varlen fwd 32768 tokens H28 d128 bf16 causal window 4096", "bf16", PEAK_BF16_TFLOPS, "fa_fwd.hip")
+                "varlen fwd 32768 tokens H28 d128 bf16 causal window 4096", "bf16", PEAK_BF16_TFLOPS, "fa_fwd.hip",
+                "TFLOP/s")
     if name == "varlen_bwd":
         w = WORKLOADS["varlen_bwd_32k"]
         t = workload_inputs("varlen_bwd_32k")
@@ -233,12 +259,17 @@ def make_step(name, torch, fa):
         return (lambda: fa.fa_varlen_bwd(do, q, k, v, o, lse, cu, mx, causal=True, window=w.window, dq=dq, dk=dk,
                                          dv=dv), f,
                 "varlen bwd 32768 tokens H28 d128 bf16 causal window 4096, fp32 gradients", "bf16",
-                PEAK_BF16_TFLOPS, "fa_bwd.hip")
+                PEAK_BF16_TFLOPS, "fa_bwd.hip", "TFLOP/s")
+    if name == "merge":
+        o_p, lse_p, out, lse, nbytes = merge_inputs(torch)
+        return (lambda: fa.fa_merge(o_p, lse_p, out=out, lse=lse), nbytes,
+                "merge of 8 fp32 partial results, B1 N8192 H32 d128 -> bf16", "f32", PEAK_HBM_GBS, "fa_merge.hip",
+                "GB/s")
     t = workload_inputs("fp8_n8192")
     q8, k8, v8 = (t[x].cuda() for x in ("q8", "k8", "v8"))
     ds = (t["q_scale"], t["k_scale"], t["v_scale"])
     return (lambda: fa.fa_fwd(q8, k8, v8, causal=True, descale=ds), fwd_flops(1, 32, 8192, 128, True),
-            "fwd B1 H32 N8192 d128 fp8-e4m3 causal", "fp8_e4m3", PEAK_FP8_TFLOPS, "fa_fp8.hip")
+            "fwd B1 H32 N8192 d128 fp8-e4m3 causal", "fp8_e4m3", PEAK_FP8_TFLOPS, "fa_fp8.hip", "TFLOP/s")
 
 
 def main():
@@ -271,16 +302,18 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     fa.lib()  # fail loudly if the HIP library is missing
-    step, flops, desc, dtype, peak, src = make_step(args.workload, torch, fa)
+    headline = args.workload == "fwd_causal"
+    step, work, desc, dtype, peak, src, unit = make_step(args.workload, torch, fa)
     log(f"[bench] {torch.cuda.get_device_name(0)}; workload {desc}")
 
     wall_ms, per_call = time_calls(step, args.warmup, args.steps, torch)
     ms_per_step = wall_ms / args.steps
     kernel_ms = sum(per_call) / len(per_call)
-    value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    per_unit = 1e12 if unit == "TFLOP/s" else 1e9
+    value = work / (ms_per_step * 1e-3) / per_unit
+    achieved = work / (kernel_ms * 1e-3) / per_unit
     log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step (wall), per-call avg {kernel_ms:.4f} ms, "
-        f"{achieved:.1f} TFLOP/s")
+        f"{achieved:.1f} {unit}")
 
     if args.calib_copy:
         src_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -290,16 +323,16 @@ def main():
         log("[bench] calibration copy of 1 GiB done")
 
     sha = src_hash(src)
-    headline = args.workload == "fwd_causal"
     rows = {} if (args.no_rows or not headline) else extra_rows(torch, fa, max(5, min(args.steps, 20)))
     if rows:
         log(f"[bench] rows: {json.dumps(rows)}")
     cpu = None if (args.no_cpu_baseline or not headline) else cpu_baseline(args.cpu_budget)
 
     out = {
-        "metric": "attention fwd TFLOP/s + % MFMA peak, bf16 causal N=8192 d=128, 1 GPU",
+        "metric": "attention fwd TFLOP/s + % MFMA peak, bf16 causal N=8192 d=128, 1 GPU" if headline else
+                  f"{args.workload} {unit} (profiling workload, not the headline)",
         "value": round(value, 2),
-        "unit": "TFLOP/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -310,9 +343,9 @@ def main():
         "dtype": dtype,
         "data": "synthetic: seeded i.i.d. N(0,1) inputs (see exact_attention_24_amd/inputs.py)",
         "config": {"workload": desc, "parallelism": "none (1 GPU)"},
-        "pct_mfma_peak": round(100 * value / peak, 2),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+        "pct_mfma_peak" if unit == "TFLOP/s" else "pct_hbm_peak": round(100 * value / peak, 2),
+        "roofline": {"bound": "mfma" if unit == "TFLOP/s" else "hbm", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic_from_profile(sha) if headline else None, "kernel_src_sha": sha},
         "cpu_baseline": cpu,
         "rows": rows,

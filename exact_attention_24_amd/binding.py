@@ -22,8 +22,9 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 FA_F32, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_DTYPE_MISMATCH, FA_ERR_UNSUPPORTED, FA_ERR_HIP = range(5)
-ABI_VERSION = 2
+ABI_VERSION = 3
 
+_I64x4 = ctypes.c_int64 * 4
 _I64x3 = ctypes.c_int64 * 3
 _I64x2 = ctypes.c_int64 * 2
 
@@ -85,9 +86,19 @@ class VarlenBwdParams(ctypes.Structure):
     ]
 
 
+class MergeParams(ctypes.Structure):
+    _fields_ = [
+        ("o_parts", ctypes.c_void_p), ("lse_parts", ctypes.c_void_p), ("o", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p), ("parts_dtype", ctypes.c_int), ("o_dtype", ctypes.c_int),
+        ("num_parts", ctypes.c_int32), ("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+        ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("parts_stride", _I64x4), ("o_stride", _I64x3),
+    ]
+
+
 EXPORTS = ("fa_abi_version", "fa_last_error", "fa_check_fwd", "fa_check_varlen_fwd", "fa_check_bwd",
            "fa_check_varlen_bwd", "fa_fwd", "fa_varlen_fwd", "fa_bwd_workspace_bytes", "fa_bwd",
-           "fa_varlen_bwd_workspace_bytes", "fa_varlen_bwd")
+           "fa_varlen_bwd_workspace_bytes", "fa_varlen_bwd", "fa_check_merge", "fa_merge")
 
 _lib = None
 
@@ -104,7 +115,8 @@ def lib():
     L.fa_abi_version.restype = ctypes.c_int
     L.fa_last_error.restype = ctypes.c_char_p
     for name, ptype in (("fa_check_fwd", FwdParams), ("fa_check_varlen_fwd", VarlenFwdParams),
-                        ("fa_check_bwd", BwdParams), ("fa_check_varlen_bwd", VarlenBwdParams)):
+                        ("fa_check_bwd", BwdParams), ("fa_check_varlen_bwd", VarlenBwdParams),
+                        ("fa_check_merge", MergeParams)):
         getattr(L, name).argtypes = [ctypes.POINTER(ptype)]
         getattr(L, name).restype = ctypes.c_int
     L.fa_fwd.argtypes = [ctypes.POINTER(FwdParams), ctypes.c_void_p]
@@ -120,6 +132,8 @@ def lib():
     L.fa_varlen_bwd.argtypes = [ctypes.POINTER(VarlenBwdParams), ctypes.c_void_p, ctypes.c_size_t,
                                 ctypes.c_void_p]
     L.fa_varlen_bwd.restype = ctypes.c_int
+    L.fa_merge.argtypes = [ctypes.POINTER(MergeParams), ctypes.c_void_p]
+    L.fa_merge.restype = ctypes.c_int
     if L.fa_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libfa.so ABI {L.fa_abi_version()} != binding ABI {ABI_VERSION}; rebuild")
     _lib = L
@@ -378,3 +392,44 @@ def fa_varlen_bwd(dout, q, k, v, o, lse, cu_seqlens, max_seqlen, causal=False, w
     _raise(lib().fa_varlen_bwd(ctypes.byref(p), ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(nbytes),
                                _stream()))
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# merge of partial results
+# ---------------------------------------------------------------------------
+def make_merge_params(o_parts, lse_parts, o, lse):
+    if o_parts.dim() != 5:
+        raise ValueError(f"o_parts must be [parts, batch, seqlen, heads, head_dim] (got {tuple(o_parts.shape)})")
+    _check_last_dim("o_parts", o_parts)
+    _check_last_dim("o", o)
+    n_p, b, n, h, d = o_parts.shape
+    if o.shape != (b, n, h, d):
+        raise ValueError("o must be [batch, seqlen, heads, head_dim] of o_parts")
+    if lse_parts.shape != (n_p, b, h, n) or lse_parts.dtype != torch.float32 or not lse_parts.is_contiguous():
+        raise ValueError("lse_parts must be a contiguous float32 [parts, batch, heads, seqlen] tensor")
+    if lse is not None and (lse.shape != (b, h, n) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [batch, heads, seqlen] tensor")
+    p = MergeParams()
+    p.o_parts, p.lse_parts, p.o, p.lse = _ptr(o_parts), _ptr(lse_parts), _ptr(o), _ptr(lse)
+    p.parts_dtype, p.o_dtype = _code(o_parts), _code(o)
+    p.num_parts, p.batch, p.seqlen, p.heads, p.head_dim = n_p, b, n, h, d
+    p.parts_stride = _I64x4(*o_parts.stride()[:4])
+    p.o_stride = _I64x3(*o.stride()[:3])
+    return p
+
+
+def fa_check_merge(params: MergeParams) -> int:
+    return lib().fa_check_merge(ctypes.byref(params))
+
+
+def fa_merge(o_parts, lse_parts, out=None, lse=None, out_dtype=None, return_lse=True):
+    """Combine partial results over disjoint key subsets: o_parts [P, B, N, H, d]
+    (fp32 or bf16), lse_parts [P, B, H, N] -> O [B, N, H, d], LSE [B, H, N]."""
+    n_p, b, n, h, d = o_parts.shape
+    if out is None:
+        out = torch.empty((b, n, h, d), dtype=out_dtype or o_parts.dtype, device=o_parts.device)
+    if lse is None and return_lse:
+        lse = torch.empty((b, h, n), dtype=torch.float32, device=o_parts.device)
+    p = make_merge_params(o_parts, lse_parts, out, lse)
+    _raise(lib().fa_merge(ctypes.byref(p), _stream()))
+    return (out, lse) if return_lse else out

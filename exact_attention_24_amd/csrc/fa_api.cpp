@@ -396,4 +396,48 @@ fa_status fa_varlen_bwd(const fa_varlen_bwd_params *p, void *workspace, size_t w
   return launched(fa::launch_bwd_bf16(a, p->head_dim, reinterpret_cast<hipStream_t>(stream)));
 }
 
+fa_status fa_check_merge(const fa_merge_params *p) {
+  if (!p) return fail(FA_ERR_INVALID_ARGUMENT, "params is NULL");
+  if (!valid_dtype(p->parts_dtype) || !valid_dtype(p->o_dtype))
+    return fail(FA_ERR_INVALID_ARGUMENT, "unknown dtype code (parts_dtype=%d, o_dtype=%d)", (int)p->parts_dtype,
+                (int)p->o_dtype);
+  if ((p->parts_dtype != FA_F32 && p->parts_dtype != FA_BF16) || (p->o_dtype != FA_F32 && p->o_dtype != FA_BF16))
+    return fail(FA_ERR_DTYPE_MISMATCH, "partial and merged O must be fp32 or bf16 (got parts_dtype=%d o_dtype=%d)",
+                (int)p->parts_dtype, (int)p->o_dtype);
+  if (p->num_parts < 0 || p->batch < 0 || p->seqlen < 0 || p->heads < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "sizes must be >= 0 (num_parts=%d batch=%d seqlen=%d heads=%d)",
+                p->num_parts, p->batch, p->seqlen, p->heads);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", p->head_dim);
+  const int64_t rows = (int64_t)p->batch * p->seqlen * p->heads;
+  const bool empty = rows == 0;
+  const bool no_parts = empty || p->num_parts == 0;
+  fa_status st;
+  const int pb = dtype_bytes(p->parts_dtype), ob = dtype_bytes(p->o_dtype), hd = p->head_dim;
+  if ((st = check_tensor("o_parts", p->o_parts, p->parts_stride + 1, 3, pb, no_parts, p->seqlen, hd)) != FA_OK)
+    return st;
+  if (!no_parts && (p->parts_stride[0] < 0 || p->parts_stride[0] % (16 / pb)))
+    return fail(FA_ERR_INVALID_ARGUMENT, "o_parts part stride must be >= 0 and a multiple of %d elements", 16 / pb);
+  if (!no_parts && !p->lse_parts) return fail(FA_ERR_INVALID_ARGUMENT, "lse_parts is NULL");
+  if ((st = check_tensor("o", p->o, p->o_stride, 3, ob, empty, p->seqlen, hd)) != FA_OK) return st;
+  if ((rows + 255) / 256 * (hd / 4) > INT32_MAX) return fail(FA_ERR_INVALID_ARGUMENT, "problem too large for one launch");
+  return ok();
+}
+
+fa_status fa_merge(const fa_merge_params *p, void *stream) {
+  fa_status st = fa_check_merge(p);
+  if (st != FA_OK) return st;
+  if ((int64_t)p->batch * p->seqlen * p->heads == 0) return ok();
+  if ((st = check_device()) != FA_OK) return st;
+  fa::MergeArgs a{};
+  a.o_parts = p->o_parts; a.lse_parts = p->lse_parts; a.o = p->o; a.lse = p->lse;
+  a.p_sp = p->parts_stride[0]; a.p_sb = p->parts_stride[1]; a.p_st = p->parts_stride[2]; a.p_sh = p->parts_stride[3];
+  a.lse_sp = (int64_t)p->batch * p->heads * p->seqlen;
+  a.o_sb = p->o_stride[0]; a.o_st = p->o_stride[1]; a.o_sh = p->o_stride[2];
+  a.num_parts = p->num_parts; a.batch = p->batch; a.seqlen = p->seqlen; a.heads = p->heads;
+  a.parts_f32 = p->parts_dtype == FA_F32;
+  a.out_f32 = p->o_dtype == FA_F32;
+  return launched(fa::launch_merge(a, p->head_dim, reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -45,6 +45,19 @@ struct BwdArgs {
   float scale, scale_log2;
 };
 
+// Kernel-side view of one merge of partial results (O_p, LSE_p).
+struct MergeArgs {
+  const void *o_parts;     // [num_parts, batch, seqlen, heads, head_dim], fp32 or bf16
+  const float *lse_parts;  // [num_parts, batch, heads, seqlen] fp32, parts lse_sp elements apart
+  void *o;                 // [batch, seqlen, heads, head_dim], fp32 or bf16
+  float *lse;              // [batch, heads, seqlen] fp32, or null
+  int64_t p_sp, p_sb, p_st, p_sh;  // o_parts element strides: part, batch, token, head
+  int64_t lse_sp;
+  int64_t o_sb, o_st, o_sh;
+  int32_t num_parts, batch, seqlen, heads;
+  int32_t parts_f32, out_f32;
+};
+
 // Launchers (defined in the kernel translation units).  Each returns the
 // HIP status of its launch(es).
 hipError_t launch_fwd_bf16(const FwdArgs &a, int head_dim, hipStream_t s);
@@ -52,6 +65,7 @@ hipError_t launch_fwd_f32(const FwdArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_fwd_fp8(const FwdArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs &a, int head_dim, hipStream_t s);
 size_t bwd_workspace_bytes(int batch, int heads, int nq, int head_dim, int deterministic);
+hipError_t launch_merge(const MergeArgs &a, int head_dim, hipStream_t s);
 
 // Query-tile rows per work-group of each forward kernel (grid sizing).
 int fwd_block_rows(int qkv_dtype, int head_dim);

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 typedef enum {
   FA_F32 = 0,       /* IEEE binary32 */
@@ -168,12 +168,38 @@ typedef struct {
   int32_t causal, window, deterministic;
 } fa_varlen_bwd_params;
 
+/* Merge of partial results: attention over disjoint key subsets p, each
+ * normalised over its own keys, combined into the result over their union,
+ *     LSE = ln sum_p exp(LSE_p),   O = sum_p exp(LSE_p - LSE) O_p
+ * (the stable combination of per-block max and exponent sum of jsqmd.com
+ * section 2.2.2; the step that joins the per-segment results of ring
+ * attention, Ring-Attention paragraph of the ms-swift integration page).
+ *   o_parts [num_parts, batch, seqlen, heads, head_dim] in parts_dtype (FA_F32
+ *   or FA_BF16); parts_stride = {part, batch, token, head} element strides.
+ *   lse_parts [num_parts, batch, heads, seqlen] fp32 contiguous (natural log).
+ *   o [batch, seqlen, heads, head_dim] in o_dtype (FA_F32 or FA_BF16),
+ *   o_stride = {batch, token, head}; lse [batch, heads, seqlen] fp32
+ *   contiguous, or NULL.
+ * A part with LSE_p = -inf (it saw no key) adds nothing and its O_p row is
+ * not read; a row where every part is -inf (or num_parts = 0) gets O = 0 and
+ * LSE = -inf.  o must not overlap o_parts. */
+typedef struct {
+  const void *o_parts;
+  const float *lse_parts;
+  void *o;
+  float *lse;
+  fa_dtype parts_dtype, o_dtype;
+  int32_t num_parts, batch, seqlen, heads, head_dim;
+  int64_t parts_stride[4], o_stride[3];
+} fa_merge_params;
+
 /* Host-only validation: never touches a device.  Returns the status the
  * corresponding entry point would return before launching anything. */
 fa_status fa_check_fwd(const fa_fwd_params *p);
 fa_status fa_check_varlen_fwd(const fa_varlen_fwd_params *p);
 fa_status fa_check_bwd(const fa_bwd_params *p);
 fa_status fa_check_varlen_bwd(const fa_varlen_bwd_params *p);
+fa_status fa_check_merge(const fa_merge_params *p);
 
 /* Enqueue the forward: writes o (and lse when non-NULL). */
 fa_status fa_fwd(const fa_fwd_params *p, void *stream);
@@ -193,6 +219,9 @@ size_t fa_varlen_bwd_workspace_bytes(const fa_varlen_bwd_params *p);
 
 /* Enqueue the packed variable-length backward: writes dq, dk, dv. */
 fa_status fa_varlen_bwd(const fa_varlen_bwd_params *p, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Enqueue the merge: writes o (and lse when non-NULL). */
+fa_status fa_merge(const fa_merge_params *p, void *stream);
 
 /* Thread-local description of the last non-FA_OK status ("" if none). */
 const char *fa_last_error(void);

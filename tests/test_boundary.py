@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_varlen_fwd", "fa_bwd", "fa_varlen_bwd", "fa_bwd_workspace_bytes",
               "fa_varlen_bwd_workspace_bytes", "fa_check_fwd", "fa_check_varlen_fwd", "fa_check_bwd",
-              "fa_check_varlen_bwd", "fa_last_error", "fa_abi_version"):
+              "fa_check_varlen_bwd", "fa_merge", "fa_check_merge", "fa_last_error", "fa_abi_version"):
         assert n in names
 
 
@@ -176,6 +176,28 @@ def test_varlen_bwd_checks(lib):
     assert lib.fa_check_varlen_bwd(ctypes.byref(p)) == B.FA_ERR_INVALID_ARGUMENT
     with pytest.raises(ValueError, match="lse"):
         B.make_varlen_bwd_params(q, q, q, q, q, lse.t(), g, g, g, cu, 30)
+
+
+def test_merge_checks(lib):
+    op = torch.zeros(3, 1, 16, 2, 128, dtype=torch.float32)
+    lp = torch.zeros(3, 1, 2, 16, dtype=torch.float32)
+    o = torch.zeros(1, 16, 2, 128, dtype=torch.bfloat16)
+    p = B.make_merge_params(op, lp, o, None)
+    assert lib.fa_check_merge(ctypes.byref(p)) == B.FA_OK
+    for field, value, code in (("parts_dtype", B.FA_FP8_E4M3, B.FA_ERR_DTYPE_MISMATCH),
+                               ("o_dtype", 9, B.FA_ERR_INVALID_ARGUMENT),
+                               ("head_dim", 96, B.FA_ERR_UNSUPPORTED),
+                               ("lse_parts", None, B.FA_ERR_INVALID_ARGUMENT),
+                               ("num_parts", -1, B.FA_ERR_INVALID_ARGUMENT)):
+        p = B.make_merge_params(op, lp, o, None)
+        setattr(p, field, value)
+        assert lib.fa_check_merge(ctypes.byref(p)) == code, field
+    p = B.make_merge_params(op, lp, o, None)
+    p.num_parts, p.lse_parts, p.o_parts = 0, None, None  # no parts: every row is 0 / -inf
+    assert lib.fa_check_merge(ctypes.byref(p)) == B.FA_OK
+    p = B.make_merge_params(op, lp, o, None)
+    p.parts_stride[0] = 6  # parts not 16-byte aligned
+    assert lib.fa_check_merge(ctypes.byref(p)) == B.FA_ERR_INVALID_ARGUMENT
 
 
 def test_python_layer_error_mapping(lib):

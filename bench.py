@@ -141,6 +141,22 @@ def merge_inputs(torch):
     return o_p, lse_p, out, lse, nbytes
 
 
+def kvcache_step(torch, fa):
+    """One decode step at B8 H32 d128 with 8191 cached tokens + 1 new: the
+    step function (idempotent: it appends at the same row each time) and the
+    bytes it must move (every cached K/V row once, plus q, the new rows and O)."""
+    from exact_attention_24_amd.inputs import WORKLOADS, kvcache_inputs
+    w = WORKLOADS["kvcache_b8_h32"]
+    q, kc, vc, kn, vn = (x.cuda() for x in kvcache_inputs(w.batch, w.seqlen, w.heads, w.head_dim, 1, seed=w.seed))
+    seq = torch.full((w.batch,), w.seqlen - 1, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty(w.batch, w.heads, 1, dtype=torch.float32, device="cuda")
+    row = w.batch * w.heads * w.head_dim * 2
+    nbytes = 2 * w.seqlen * row + 4 * row + w.batch * w.heads * 4
+    fn = lambda: fa.fa_fwd_kvcache(q, kc, vc, kn, vn, cache_seqlens=seq, causal=True, out=out, lse=lse)
+    return fn, nbytes
+
+
 def extra_rows(torch, fa, steps):
     """Timings of the other hot-path rows (median per call, HIP events)."""
     from exact_attention_24_amd.inputs import WORKLOADS, workload_inputs
@@ -201,6 +217,15 @@ def extra_rows(torch, fa, steps):
         del o_p, lse_p, out, lse
     except Exception as e:
         rows["merge_8parts_n8192"] = {"error": str(e)[:120]}
+    # KV-cache decode step
+    try:
+        fn, nbytes = kvcache_step(torch, fa)
+        _, ms = time_calls(fn, 2, steps, torch)
+        gbs = nbytes / med(ms) / 1e6
+        rows["kvcache_decode_b8_h32_8k"] = {"ms": round(med(ms), 4), "GB/s": round(gbs, 1),
+                                            "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    except Exception as e:
+        rows["kvcache_decode_b8_h32_8k"] = {"error": str(e)[:120]}
     # fp8 forward
     try:
         t = workload_inputs("fp8_n8192")
@@ -215,7 +240,7 @@ def extra_rows(torch, fa, steps):
     return rows
 
 
-WORKLOAD_CHOICES = ("fwd_causal", "fwd_noncausal", "bwd", "varlen", "varlen_bwd", "fp8", "merge")
+WORKLOAD_CHOICES = ("fwd_causal", "fwd_noncausal", "bwd", "varlen", "varlen_bwd", "fp8", "merge", "kvcache")
 
 
 def make_step(name, torch, fa):
@@ -260,6 +285,10 @@ def make_step(name, torch, fa):
                                          dv=dv), f,
                 "varlen bwd 32768 tokens H28 d128 bf16 causal window 4096, fp32 gradients", "bf16",
                 PEAK_BF16_TFLOPS, "fa_bwd.hip", "TFLOP/s")
+    if name == "kvcache":
+        fn, nbytes = kvcache_step(torch, fa)
+        return (fn, nbytes, "KV-cache decode step B8 H32 d128, 8191 cached + 1 new token, causal", "bf16",
+                PEAK_HBM_GBS, "fa_decode.hip", "GB/s")
     if name == "merge":
         o_p, lse_p, out, lse, nbytes = merge_inputs(torch)
         return (lambda: fa.fa_merge(o_p, lse_p, out=out, lse=lse), nbytes,

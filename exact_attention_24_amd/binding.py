@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 FA_F32, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_DTYPE_MISMATCH, FA_ERR_UNSUPPORTED, FA_ERR_HIP = range(5)
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _I64x4 = ctypes.c_int64 * 4
 _I64x3 = ctypes.c_int64 * 3
@@ -96,9 +96,24 @@ class MergeParams(ctypes.Structure):
     ]
 
 
+class KvcacheParams(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p), ("cache_seqlens", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("qkv_dtype", ctypes.c_int),
+        ("batch", ctypes.c_int32), ("seqlen_q", ctypes.c_int32), ("cache_len", ctypes.c_int32),
+        ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("q_stride", _I64x3), ("kc_stride", _I64x3), ("vc_stride", _I64x3), ("kn_stride", _I64x3),
+        ("vn_stride", _I64x3), ("o_stride", _I64x3),
+        ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+    ]
+
+
 EXPORTS = ("fa_abi_version", "fa_last_error", "fa_check_fwd", "fa_check_varlen_fwd", "fa_check_bwd",
            "fa_check_varlen_bwd", "fa_fwd", "fa_varlen_fwd", "fa_bwd_workspace_bytes", "fa_bwd",
-           "fa_varlen_bwd_workspace_bytes", "fa_varlen_bwd", "fa_check_merge", "fa_merge")
+           "fa_varlen_bwd_workspace_bytes", "fa_varlen_bwd", "fa_check_merge", "fa_merge",
+           "fa_check_kvcache", "fa_kvcache_workspace_bytes", "fa_fwd_kvcache")
 
 _lib = None
 
@@ -116,7 +131,7 @@ def lib():
     L.fa_last_error.restype = ctypes.c_char_p
     for name, ptype in (("fa_check_fwd", FwdParams), ("fa_check_varlen_fwd", VarlenFwdParams),
                         ("fa_check_bwd", BwdParams), ("fa_check_varlen_bwd", VarlenBwdParams),
-                        ("fa_check_merge", MergeParams)):
+                        ("fa_check_merge", MergeParams), ("fa_check_kvcache", KvcacheParams)):
         getattr(L, name).argtypes = [ctypes.POINTER(ptype)]
         getattr(L, name).restype = ctypes.c_int
     L.fa_fwd.argtypes = [ctypes.POINTER(FwdParams), ctypes.c_void_p]
@@ -134,6 +149,10 @@ def lib():
     L.fa_varlen_bwd.restype = ctypes.c_int
     L.fa_merge.argtypes = [ctypes.POINTER(MergeParams), ctypes.c_void_p]
     L.fa_merge.restype = ctypes.c_int
+    L.fa_kvcache_workspace_bytes.argtypes = [ctypes.POINTER(KvcacheParams)]
+    L.fa_kvcache_workspace_bytes.restype = ctypes.c_size_t
+    L.fa_fwd_kvcache.argtypes = [ctypes.POINTER(KvcacheParams), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.fa_fwd_kvcache.restype = ctypes.c_int
     if L.fa_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libfa.so ABI {L.fa_abi_version()} != binding ABI {ABI_VERSION}; rebuild")
     _lib = L
@@ -432,4 +451,79 @@ def fa_merge(o_parts, lse_parts, out=None, lse=None, out_dtype=None, return_lse=
         lse = torch.empty((b, h, n), dtype=torch.float32, device=o_parts.device)
     p = make_merge_params(o_parts, lse_parts, out, lse)
     _raise(lib().fa_merge(ctypes.byref(p), _stream()))
+    return (out, lse) if return_lse else out
+
+
+# ---------------------------------------------------------------------------
+# KV-cache decode
+# ---------------------------------------------------------------------------
+def make_kvcache_params(q, k_cache, v_cache, k_new, v_new, cache_seqlens, o, lse, causal=False, window=0,
+                        softmax_scale=None, num_splits=0):
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("o", o)):
+        if t.dim() != 4:
+            raise ValueError(f"{n} must be [batch, seqlen, heads, head_dim] (got {tuple(t.shape)})")
+        _check_last_dim(n, t)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k and v must be given together")
+    tensors = [q, k_cache, v_cache] + ([k_new, v_new] if k_new is not None else [])
+    if len({_code(t) for t in tensors}) != 1:
+        raise ValueError("Input and output tensors must have the same dtype (q, caches, new k/v differ)")
+    b, nq, h, d = q.shape
+    lmax = k_cache.shape[1]
+    if k_cache.shape != (b, lmax, h, d) or v_cache.shape != (b, lmax, h, d):
+        raise ValueError("k_cache, v_cache must be [batch, cache_len, heads, head_dim] matching q")
+    if k_new is not None and (k_new.shape != q.shape or v_new.shape != q.shape):
+        raise ValueError("k, v must have q's shape [batch, seqlen_q, heads, head_dim]")
+    if o.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    if cache_seqlens.dtype != torch.int32 or cache_seqlens.shape != (b,) or not cache_seqlens.is_contiguous():
+        raise ValueError("cache_seqlens must be a contiguous int32 [batch] tensor")
+    if lse is not None and (lse.shape != (b, h, nq) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [batch, heads, seqlen_q] tensor")
+    p = KvcacheParams()
+    p.q, p.k_cache, p.v_cache = _ptr(q), _ptr(k_cache), _ptr(v_cache)
+    p.k_new, p.v_new = _ptr(k_new), _ptr(v_new)
+    p.cache_seqlens, p.o, p.lse = _ptr(cache_seqlens), _ptr(o), _ptr(lse)
+    p.qkv_dtype = _code(q)
+    p.batch, p.seqlen_q, p.cache_len, p.heads, p.head_dim = b, nq, lmax, h, d
+    p.q_stride = _I64x3(*q.stride()[:3])
+    p.kc_stride = _I64x3(*k_cache.stride()[:3])
+    p.vc_stride = _I64x3(*v_cache.stride()[:3])
+    if k_new is not None:
+        p.kn_stride = _I64x3(*k_new.stride()[:3])
+        p.vn_stride = _I64x3(*v_new.stride()[:3])
+    p.o_stride = _I64x3(*o.stride()[:3])
+    p.softmax_scale = _default_scale(d, softmax_scale)
+    p.causal, p.window, p.num_splits = int(bool(causal)), int(window), int(num_splits)
+    return p
+
+
+def fa_check_kvcache(params: KvcacheParams) -> int:
+    return lib().fa_check_kvcache(ctypes.byref(params))
+
+
+def fa_kvcache_workspace_bytes(params: KvcacheParams) -> int:
+    return int(lib().fa_kvcache_workspace_bytes(ctypes.byref(params)))
+
+
+def fa_fwd_kvcache(q, k_cache, v_cache, k=None, v=None, cache_seqlens=0, causal=False, window=0,
+                   softmax_scale=None, num_splits=0, out=None, lse=None, return_lse=True):
+    """One decoding step against a KV cache (the caches are updated in place
+    when k, v are given).  cache_seqlens: an int for every batch entry, or an
+    int32 [batch] tensor on the device."""
+    b, nq, h, d = q.shape
+    if isinstance(cache_seqlens, int):
+        if cache_seqlens < 0 or cache_seqlens + (nq if k is not None else 0) > k_cache.shape[1]:
+            raise ValueError(f"cache_seqlens={cache_seqlens} does not fit cache_len={k_cache.shape[1]}")
+        cache_seqlens = torch.full((b,), cache_seqlens, dtype=torch.int32, device=q.device)
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((b, h, nq), dtype=torch.float32, device=q.device)
+    p = make_kvcache_params(q, k_cache, v_cache, k, v, cache_seqlens, out, lse, causal, window, softmax_scale,
+                            num_splits)
+    _raise(lib().fa_check_kvcache(ctypes.byref(p)))
+    nbytes = fa_kvcache_workspace_bytes(p)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _raise(lib().fa_fwd_kvcache(ctypes.byref(p), ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(nbytes), _stream()))
     return (out, lse) if return_lse else out

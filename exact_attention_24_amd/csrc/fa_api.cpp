@@ -158,6 +158,24 @@ fa_status check_bwd_common(fa_dtype qkv, fa_dtype grad, int heads, int head_dim,
   return FA_OK;
 }
 
+// Key splits per (batch, head) of a KV-cache decode: enough work-groups for
+// two per CU, but no split shorter than 512 keys.
+int kvcache_splits(const fa_kvcache_params *p) {
+  if (p->num_splits > 0) return p->num_splits;
+  const int64_t bh = std::max<int64_t>(1, (int64_t)p->batch * p->heads);
+  const int64_t want = (512 + bh - 1) / bh;
+  const int64_t cap = std::max<int64_t>(1, ((int64_t)p->cache_len + 511) / 512);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(std::min(want, cap), 64));
+}
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t kvcache_ws(const fa_kvcache_params *p, int splits) {
+  if (splits <= 1) return 0;
+  const size_t rows = (size_t)splits * p->batch * p->seqlen_q * p->heads;
+  return round256(rows * p->head_dim * sizeof(float)) + round256(rows * sizeof(float));
+}
+
 }  // namespace
 
 extern "C" {
@@ -438,6 +456,100 @@ fa_status fa_merge(const fa_merge_params *p, void *stream) {
   a.parts_f32 = p->parts_dtype == FA_F32;
   a.out_f32 = p->o_dtype == FA_F32;
   return launched(fa::launch_merge(a, p->head_dim, reinterpret_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_check_kvcache(const fa_kvcache_params *p) {
+  if (!p) return fail(FA_ERR_INVALID_ARGUMENT, "params is NULL");
+  if (!valid_dtype(p->qkv_dtype)) return fail(FA_ERR_INVALID_ARGUMENT, "unknown dtype code (qkv_dtype=%d)", (int)p->qkv_dtype);
+  if (p->qkv_dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "the KV-cache decode takes bf16 q and caches (got qkv_dtype=%d)", (int)p->qkv_dtype);
+  if (p->batch < 0 || p->seqlen_q < 0 || p->cache_len < 0 || p->heads < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "sizes must be >= 0 (batch=%d seqlen_q=%d cache_len=%d heads=%d)", p->batch,
+                p->seqlen_q, p->cache_len, p->heads);
+  if (p->seqlen_q > 8)
+    return fail(FA_ERR_UNSUPPORTED, "the KV-cache decode takes at most 8 query rows (got %d)", p->seqlen_q);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", p->head_dim);
+  if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f))
+    return fail(FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0 (got %g)", (double)p->softmax_scale);
+  if (p->causal != 0 && p->causal != 1)
+    return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", p->causal);
+  if (p->window < 0) return fail(FA_ERR_INVALID_ARGUMENT, "window must be >= 0 (got %d)", p->window);
+  if (p->num_splits < 0 || p->num_splits > 256)
+    return fail(FA_ERR_INVALID_ARGUMENT, "num_splits must be in [0, 256] (got %d)", p->num_splits);
+  if ((p->k_new == nullptr) != (p->v_new == nullptr))
+    return fail(FA_ERR_INVALID_ARGUMENT, "k_new and v_new must be given together");
+  const bool empty = (int64_t)p->batch * p->seqlen_q * p->heads == 0;
+  fa_status st;
+  const int hd = p->head_dim;
+  if ((st = check_tensor("q", p->q, p->q_stride, 3, 2, empty, p->seqlen_q, hd)) != FA_OK) return st;
+  if ((st = check_tensor("o", p->o, p->o_stride, 3, 2, empty, p->seqlen_q, hd)) != FA_OK) return st;
+  const bool no_cache = empty || p->cache_len == 0;
+  if ((st = check_tensor("k_cache", p->k_cache, p->kc_stride, 3, 2, no_cache, p->cache_len, hd)) != FA_OK) return st;
+  if ((st = check_tensor("v_cache", p->v_cache, p->vc_stride, 3, 2, no_cache, p->cache_len, hd)) != FA_OK) return st;
+  if (p->k_new) {
+    if (p->cache_len < p->seqlen_q)
+      return fail(FA_ERR_INVALID_ARGUMENT, "cache_len (%d) cannot hold the %d new rows", p->cache_len, p->seqlen_q);
+    if ((st = check_tensor("k_new", p->k_new, p->kn_stride, 3, 2, empty, p->seqlen_q, hd)) != FA_OK) return st;
+    if ((st = check_tensor("v_new", p->v_new, p->vn_stride, 3, 2, empty, p->seqlen_q, hd)) != FA_OK) return st;
+  }
+  if (!empty && !p->cache_seqlens) return fail(FA_ERR_INVALID_ARGUMENT, "cache_seqlens is NULL");
+  if ((int64_t)p->batch * p->heads * kvcache_splits(p) > INT32_MAX)
+    return fail(FA_ERR_INVALID_ARGUMENT, "problem too large for one launch");
+  return ok();
+}
+
+size_t fa_kvcache_workspace_bytes(const fa_kvcache_params *p) {
+  if (fa_check_kvcache(p) != FA_OK) return 0;
+  return kvcache_ws(p, kvcache_splits(p));
+}
+
+fa_status fa_fwd_kvcache(const fa_kvcache_params *p, void *workspace, size_t workspace_bytes, void *stream) {
+  fa_status st = fa_check_kvcache(p);
+  if (st != FA_OK) return st;
+  const int splits = kvcache_splits(p);
+  const size_t need = kvcache_ws(p, splits);
+  if (workspace_bytes < need)
+    return fail(FA_ERR_INVALID_ARGUMENT, "workspace too small (%zu bytes, need %zu)", workspace_bytes, need);
+  if (need && !workspace) return fail(FA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(FA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if ((int64_t)p->batch * p->seqlen_q * p->heads == 0) return ok();
+  if ((st = check_device()) != FA_OK) return st;
+  fa::DecodeArgs a{};
+  a.q = p->q; a.k_cache = p->k_cache; a.v_cache = p->v_cache; a.k_new = p->k_new; a.v_new = p->v_new;
+  a.cache_seqlens = p->cache_seqlens; a.o = p->o; a.lse = p->lse;
+  a.q_sb = p->q_stride[0]; a.q_st = p->q_stride[1]; a.q_sh = p->q_stride[2];
+  a.kc_sb = p->kc_stride[0]; a.kc_st = p->kc_stride[1]; a.kc_sh = p->kc_stride[2];
+  a.vc_sb = p->vc_stride[0]; a.vc_st = p->vc_stride[1]; a.vc_sh = p->vc_stride[2];
+  a.kn_sb = p->kn_stride[0]; a.kn_st = p->kn_stride[1]; a.kn_sh = p->kn_stride[2];
+  a.vn_sb = p->vn_stride[0]; a.vn_st = p->vn_stride[1]; a.vn_sh = p->vn_stride[2];
+  a.o_sb = p->o_stride[0]; a.o_st = p->o_stride[1]; a.o_sh = p->o_stride[2];
+  a.batch = p->batch; a.nq = p->seqlen_q; a.cache_len = p->cache_len; a.heads = p->heads;
+  a.causal = p->causal; a.window = p->window; a.num_splits = splits;
+  a.split_len = splits == 1 ? p->cache_len : (int)((((int64_t)p->cache_len + splits - 1) / splits + 63) / 64 * 64);
+  a.scale_log2 = p->softmax_scale * kLog2e;
+  const size_t rows = (size_t)splits * p->batch * p->seqlen_q * p->heads;
+  if (splits > 1) {
+    a.o_parts = static_cast<float *>(workspace);
+    a.lse_parts = reinterpret_cast<float *>(static_cast<char *>(workspace) + round256(rows * p->head_dim * 4));
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (p->k_new) e = fa::launch_kv_append(a, p->head_dim, s);
+  if (e == hipSuccess) e = fa::launch_decode(a, p->head_dim, s);
+  if (e == hipSuccess && splits > 1) {
+    fa::MergeArgs m{};
+    m.o_parts = a.o_parts; m.lse_parts = a.lse_parts; m.o = p->o; m.lse = p->lse;
+    const int64_t hd = p->head_dim;
+    m.p_sh = hd; m.p_st = hd * p->heads; m.p_sb = m.p_st * p->seqlen_q; m.p_sp = m.p_sb * p->batch;
+    m.lse_sp = (int64_t)p->batch * p->heads * p->seqlen_q;
+    m.o_sb = p->o_stride[0]; m.o_st = p->o_stride[1]; m.o_sh = p->o_stride[2];
+    m.num_parts = splits; m.batch = p->batch; m.seqlen = p->seqlen_q; m.heads = p->heads;
+    m.parts_f32 = 1; m.out_f32 = 0;
+    e = fa::launch_merge(m, p->head_dim, s);
+  }
+  return launched(e);
 }
 
 }  // extern "C"

@@ -58,6 +58,22 @@ struct MergeArgs {
   int32_t parts_f32, out_f32;
 };
 
+// Kernel-side view of one KV-cache decode call.
+struct DecodeArgs {
+  const void *q;                    // [batch, nq, heads, d] bf16
+  void *k_cache, *v_cache;          // [batch, cache_len, heads, d] bf16
+  const void *k_new, *v_new;        // [batch, nq, heads, d] bf16, or null
+  const int32_t *cache_seqlens;     // [batch]
+  void *o;                          // [batch, nq, heads, d] bf16 (num_splits == 1)
+  float *lse;                       // [batch, heads, nq], or null (num_splits == 1)
+  float *o_parts, *lse_parts;       // workspace (num_splits > 1): [splits, batch, nq, heads, d], [splits, batch, heads, nq]
+  int64_t q_sb, q_st, q_sh, kc_sb, kc_st, kc_sh, vc_sb, vc_st, vc_sh;
+  int64_t kn_sb, kn_st, kn_sh, vn_sb, vn_st, vn_sh, o_sb, o_st, o_sh;
+  int32_t batch, nq, cache_len, heads;
+  int32_t causal, window, num_splits, split_len;
+  float scale_log2;
+};
+
 // Launchers (defined in the kernel translation units).  Each returns the
 // HIP status of its launch(es).
 hipError_t launch_fwd_bf16(const FwdArgs &a, int head_dim, hipStream_t s);
@@ -66,6 +82,8 @@ hipError_t launch_fwd_fp8(const FwdArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs &a, int head_dim, hipStream_t s);
 size_t bwd_workspace_bytes(int batch, int heads, int nq, int head_dim, int deterministic);
 hipError_t launch_merge(const MergeArgs &a, int head_dim, hipStream_t s);
+hipError_t launch_kv_append(const DecodeArgs &a, int head_dim, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, int head_dim, hipStream_t s);
 
 // Query-tile rows per work-group of each forward kernel (grid sizing).
 int fwd_block_rows(int qkv_dtype, int head_dim);

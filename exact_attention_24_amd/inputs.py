@@ -16,6 +16,10 @@ Workloads (the shapes of the pages' examples and model configurations):
   varlen_bwd_32k the varlen_32k packing (same seed, so the same lengths and
                  Q/K/V) plus a bf16 dO, for the packed backward
   fp8_n8192      same shape, e4m3 Q/K/V with per-tensor scales, causal
+  kvcache_b2_h16 the KV-cache decode loop of the MindSpore page (推理优化与KV缓存):
+                 B2, cache 2048, H16, d64, one new token per step, causal
+  kvcache_b8_h32 one decode step at the Llama-7B shape: B8, H32, d128, 8191
+                 cached tokens + 1 new (cache 8192), causal
 
 Recipe: one ``torch.Generator('cpu')`` per workload seeded with its seed;
 Q, K, V (then dO) drawn in that order as i.i.d. N(0, 1) float32 and cast to
@@ -63,6 +67,8 @@ WORKLOADS = {
     "varlen_bwd_32k": Workload("varlen_bwd_32k", 1, 28, 8192, 128, "bf16", True, window=4096, seed=1004,
                                varlen_total=32768),
     "fp8_n8192": Workload("fp8_n8192", 1, 32, 8192, 128, "fp8", True, seed=1005),
+    "kvcache_b2_h16": Workload("kvcache_b2_h16", 2, 16, 2048, 64, "bf16", True, seed=1007),
+    "kvcache_b8_h32": Workload("kvcache_b8_h32", 8, 32, 8192, 128, "bf16", True, seed=1008),
 }
 
 _TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -120,6 +126,18 @@ def varlen_inputs(lengths, heads, head_dim, dtype="bf16", seed=0, with_dout=Fals
         return q, k, v, cu_seqlens_of(lengths)
     do = randn(gen, (total, heads, head_dim), dtype)
     return q, k, v, cu_seqlens_of(lengths), do
+
+
+def kvcache_inputs(batch, cache_len, heads, head_dim, nq, seed=0):
+    """KV-cache decode inputs on the CPU: q, k_cache, v_cache, k_new, v_new,
+    drawn in that order (the caches whole, every row random)."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    q = randn(gen, (batch, nq, heads, head_dim), "bf16")
+    kc = randn(gen, (batch, cache_len, heads, head_dim), "bf16")
+    vc = randn(gen, (batch, cache_len, heads, head_dim), "bf16")
+    kn = randn(gen, (batch, nq, heads, head_dim), "bf16")
+    vn = randn(gen, (batch, nq, heads, head_dim), "bf16")
+    return q, kc, vc, kn, vn
 
 
 def quantize_e4m3(x: torch.Tensor):

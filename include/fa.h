@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 typedef enum {
   FA_F32 = 0,       /* IEEE binary32 */
@@ -193,6 +193,41 @@ typedef struct {
   int64_t parts_stride[4], o_stride[3];
 } fa_merge_params;
 
+/* KV-cache decode step (flash_attn_with_kvcache of the MindSpore page,
+ * 推理优化与KV缓存): optional new rows k_new, v_new are first written into the
+ * caches at rows cache_seqlens[b] .. cache_seqlens[b] + seqlen_q - 1; then
+ * the seqlen_q query rows of batch entry b, taken as the last seqlen_q
+ * positions, attend over cache rows 0 .. L_b - 1 with
+ * L_b = cache_seqlens[b] + (k_new ? seqlen_q : 0), with the causal /
+ * window rules of every other entry point (bottom-right aligned).
+ *   q [batch, seqlen_q, heads, head_dim] bf16, 1 <= seqlen_q <= 8 (0: no-op).
+ *   k_cache, v_cache [batch, cache_len, heads, head_dim] bf16, written only
+ *   at the appended rows.  k_new, v_new [batch, seqlen_q, heads, head_dim]
+ *   bf16, both or neither.
+ *   cache_seqlens: DEVICE int32 [batch]; unchecked contract:
+ *   0 <= cache_seqlens[b] and L_b <= cache_len.
+ *   o [batch, seqlen_q, heads, head_dim] bf16; lse [batch, heads, seqlen_q]
+ *   fp32 contiguous, or NULL.  A query row that sees no key gets O = 0 and
+ *   LSE = -inf.
+ *   num_splits: key ranges per (batch, head) processed by separate
+ *   work-groups and merged as fa_merge does; 0 lets the library choose from
+ *   batch * heads and cache_len.  It fixes the workspace size.
+ *   workspace: fa_kvcache_workspace_bytes(p) bytes of device memory,
+ *   256-byte aligned (0 bytes when one split is used). */
+typedef struct {
+  const void *q;
+  void *k_cache, *v_cache;
+  const void *k_new, *v_new;
+  const int32_t *cache_seqlens;
+  void *o;
+  float *lse;
+  fa_dtype qkv_dtype;
+  int32_t batch, seqlen_q, cache_len, heads, head_dim;
+  int64_t q_stride[3], kc_stride[3], vc_stride[3], kn_stride[3], vn_stride[3], o_stride[3];
+  float softmax_scale;
+  int32_t causal, window, num_splits;
+} fa_kvcache_params;
+
 /* Host-only validation: never touches a device.  Returns the status the
  * corresponding entry point would return before launching anything. */
 fa_status fa_check_fwd(const fa_fwd_params *p);
@@ -200,6 +235,7 @@ fa_status fa_check_varlen_fwd(const fa_varlen_fwd_params *p);
 fa_status fa_check_bwd(const fa_bwd_params *p);
 fa_status fa_check_varlen_bwd(const fa_varlen_bwd_params *p);
 fa_status fa_check_merge(const fa_merge_params *p);
+fa_status fa_check_kvcache(const fa_kvcache_params *p);
 
 /* Enqueue the forward: writes o (and lse when non-NULL). */
 fa_status fa_fwd(const fa_fwd_params *p, void *stream);
@@ -222,6 +258,14 @@ fa_status fa_varlen_bwd(const fa_varlen_bwd_params *p, void *workspace, size_t w
 
 /* Enqueue the merge: writes o (and lse when non-NULL). */
 fa_status fa_merge(const fa_merge_params *p, void *stream);
+
+/* Bytes of device workspace fa_fwd_kvcache needs (0 on invalid parameters
+ * and when one split is used). */
+size_t fa_kvcache_workspace_bytes(const fa_kvcache_params *p);
+
+/* Enqueue the KV-cache decode step: appends k_new, v_new (if given), writes o
+ * (and lse when non-NULL). */
+fa_status fa_fwd_kvcache(const fa_kvcache_params *p, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Thread-local description of the last non-FA_OK status ("" if none). */
 const char *fa_last_error(void);

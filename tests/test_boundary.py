@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_varlen_fwd", "fa_bwd", "fa_varlen_bwd", "fa_bwd_workspace_bytes",
               "fa_varlen_bwd_workspace_bytes", "fa_check_fwd", "fa_check_varlen_fwd", "fa_check_bwd",
-              "fa_check_varlen_bwd", "fa_merge", "fa_check_merge", "fa_last_error", "fa_abi_version"):
+              "fa_check_varlen_bwd", "fa_merge", "fa_check_merge", "fa_fwd_kvcache", "fa_kvcache_workspace_bytes", "fa_check_kvcache",
+              "fa_last_error", "fa_abi_version"):
         assert n in names
 
 
@@ -198,6 +199,32 @@ def test_merge_checks(lib):
     p = B.make_merge_params(op, lp, o, None)
     p.parts_stride[0] = 6  # parts not 16-byte aligned
     assert lib.fa_check_merge(ctypes.byref(p)) == B.FA_ERR_INVALID_ARGUMENT
+
+
+def test_kvcache_checks(lib):
+    q = torch.zeros(2, 1, 4, 128, dtype=torch.bfloat16)
+    kc = torch.zeros(2, 4096, 4, 128, dtype=torch.bfloat16)
+    seq = torch.zeros(2, dtype=torch.int32)
+    o = torch.zeros_like(q)
+    lse = torch.zeros(2, 4, 1, dtype=torch.float32)
+    p = B.make_kvcache_params(q, kc, kc, q, q, seq, o, lse, causal=True)
+    assert lib.fa_check_kvcache(ctypes.byref(p)) == B.FA_OK
+    # 2 x 4 (batch, head) pairs -> 8 splits (cache 4096 / 512 caps it at 8): parts 8*2*1*4*128 fp32 + LSEs
+    assert lib.fa_kvcache_workspace_bytes(ctypes.byref(p)) == 32768 + 256
+    p.num_splits = 1
+    assert lib.fa_kvcache_workspace_bytes(ctypes.byref(p)) == 0
+    for field, value, code in (("qkv_dtype", B.FA_F32, B.FA_ERR_UNSUPPORTED),
+                               ("seqlen_q", 9, B.FA_ERR_UNSUPPORTED),
+                               ("head_dim", 80, B.FA_ERR_UNSUPPORTED),
+                               ("num_splits", 300, B.FA_ERR_INVALID_ARGUMENT),
+                               ("v_new", None, B.FA_ERR_INVALID_ARGUMENT),
+                               ("cache_seqlens", None, B.FA_ERR_INVALID_ARGUMENT),
+                               ("k_cache", None, B.FA_ERR_INVALID_ARGUMENT)):
+        p = B.make_kvcache_params(q, kc, kc, q, q, seq, o, lse, causal=True)
+        setattr(p, field, value)
+        assert lib.fa_check_kvcache(ctypes.byref(p)) == code, field
+    with pytest.raises(ValueError, match="cache_seqlens"):
+        B.fa_fwd_kvcache(q, kc, kc, q, q, cache_seqlens=4096)  # no room for the new row
 
 
 def test_python_layer_error_mapping(lib):

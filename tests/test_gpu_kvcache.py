@@ -1,0 +1,108 @@
+"""GPU parity of the KV-cache decode step (fa_fwd_kvcache) against the fp64
+oracle, through the C ABI: outputs, LSE, and the cache rows it appends."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_24_amd import fa_fwd_kvcache
+from exact_attention_24_amd.inputs import WORKLOADS, kvcache_inputs
+from tests.parity import assert_close, assert_lse_close, f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _nan_tail(cache, lens, nq_new):
+    """Rows at or past each entry's valid length hold NaN (bf16), so a read shows."""
+    c = cache.clone()
+    for b, t in enumerate(lens):
+        c[b, t:] = float("nan")
+    return c
+
+
+@pytest.mark.parametrize("b,nq,h,d,lmax,lens,causal,window,new,splits", [
+    (3, 1, 2, 64, 160, [0, 5, 100], True, 0, True, 0),
+    (2, 3, 2, 128, 300, [7, 64], True, 16, True, 0),
+    (2, 8, 3, 64, 96, [9, 33], False, 0, False, 0),
+    (2, 1, 2, 128, 1100, [1000, 1099], True, 0, True, 4),
+    (2, 2, 4, 128, 700, [333, 600], True, 0, True, 3),
+    (1, 4, 2, 64, 520, [515], True, 100, True, 0),
+])
+def test_kvcache_small_elementwise(b, nq, h, d, lmax, lens, causal, window, new, splits):
+    print(f"[kvcache] b={b} nq={nq} h={h} d={d} lmax={lmax} lens={lens} causal={causal} window={window} "
+          f"new={new} splits={splits}", flush=True)
+    q, kc, vc, kn, vn = kvcache_inputs(b, lmax, h, d, nq, seed=lmax + nq)
+    kc, vc = _nan_tail(kc, lens, nq), _nan_tail(vc, lens, nq)
+    seq = torch.tensor(lens, dtype=torch.int32)
+    kcd, vcd = kc.to(DEV), vc.to(DEV)
+    o, lse = fa_fwd_kvcache(q.to(DEV), kcd, vcd, kn.to(DEV) if new else None, vn.to(DEV) if new else None,
+                            cache_seqlens=seq.to(DEV), causal=causal, window=window, num_splits=splits)
+    torch.cuda.synchronize()
+    ro, rl, rkc, rvc = oracle.kvcache_fwd(f64(q), f64(kc), f64(vc), lens, 1 / np.sqrt(d), causal, window,
+                                          f64(kn) if new else None, f64(vn) if new else None)
+    assert_close(f64(o), ro)
+    assert_lse_close(f64(lse), rl)
+    # appended rows hold the new k, v bitwise; every other row is untouched (NaN stays NaN)
+    np.testing.assert_array_equal(f64(kcd), rkc)
+    np.testing.assert_array_equal(f64(vcd), rvc)
+
+
+def test_kvcache_no_keys_and_no_queries():
+    q, kc, vc, _, _ = kvcache_inputs(2, 64, 2, 64, 1, seed=1)
+    o, lse = fa_fwd_kvcache(q.to(DEV), kc.to(DEV), vc.to(DEV), cache_seqlens=0)  # nothing cached, nothing new
+    torch.cuda.synchronize()
+    assert (o.cpu() == 0).all() and torch.isneginf(lse.cpu()).all()
+    q0 = torch.empty(2, 0, 2, 64, dtype=torch.bfloat16, device=DEV)
+    o0, _ = fa_fwd_kvcache(q0, kc.to(DEV), vc.to(DEV), cache_seqlens=3)
+    assert o0.numel() == 0
+
+
+def test_kvcache_decode_loop_of_the_pages_example():
+    """B2, cache 2048, H16, d64, causal: 100 steps, each appending one token
+    (cache_seqlens = step) and decoding it; every step against the oracle on
+    the cache as it stands, and the final cache against the appended rows."""
+    w = WORKLOADS["kvcache_b2_h16"]
+    g = torch.Generator().manual_seed(w.seed)
+    kc = torch.zeros(w.batch, w.seqlen, w.heads, w.head_dim, dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    ks, vs = [], []
+    worst = 0.0
+    for i in range(100):
+        q = torch.randn(w.batch, 1, w.heads, w.head_dim, generator=g).to(torch.bfloat16)
+        k = torch.randn(w.batch, 1, w.heads, w.head_dim, generator=g).to(torch.bfloat16)
+        v = torch.randn(w.batch, 1, w.heads, w.head_dim, generator=g).to(torch.bfloat16)
+        ks.append(k)
+        vs.append(v)
+        o, lse = fa_fwd_kvcache(q.to(DEV), kc, vc, k.to(DEV), v.to(DEV), cache_seqlens=i, causal=True)
+        if i % 9 == 0 or i == 99:
+            torch.cuda.synchronize()
+            kall, vall = torch.cat(ks, 1), torch.cat(vs, 1)
+            ro, rl = oracle.mha_fwd(f64(q), f64(kall), f64(vall), w.scale, causal=True)
+            worst = max(worst, assert_close(f64(o), ro, what=f"O step {i}")[0])
+            assert_lse_close(f64(lse), rl)
+    torch.cuda.synchronize()
+    assert torch.equal(kc[:, :100].cpu(), torch.cat(ks, 1)) and torch.equal(vc[:, :100].cpu(), torch.cat(vs, 1))
+    assert (kc[:, 100:] == 0).all()
+    print(f"[kvcache loop] worst O error {worst:.2e}", flush=True)
+
+
+def test_kvcache_llama_8k_step():
+    """B8, H32, d128, 8191 cached tokens + 1 new (cache 8192), causal, with the
+    library's split choice: one (b, h) pair per batch entry against the oracle."""
+    w = WORKLOADS["kvcache_b8_h32"]
+    q, kc, vc, kn, vn = kvcache_inputs(w.batch, w.seqlen, w.heads, w.head_dim, 1, seed=w.seed)
+    kcd, vcd = kc.to(DEV), vc.to(DEV)
+    print("[kvcache 8k] launching", flush=True)
+    o, lse = fa_fwd_kvcache(q.to(DEV), kcd, vcd, kn.to(DEV), vn.to(DEV), cache_seqlens=w.seqlen - 1, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(kcd[:, -1].cpu(), kn[:, 0]) and torch.equal(vcd[:, -1].cpu(), vn[:, 0])
+    kfull, vfull = kc.clone(), vc.clone()
+    kfull[:, -1], vfull[:, -1] = kn[:, 0], vn[:, 0]
+    o64, l64 = f64(o), f64(lse)
+    for b in range(w.batch):
+        h = (7 * b + 3) % w.heads
+        ro, rl = oracle.attention_fwd(f64(q[b, :, h]), f64(kfull[b, :, h]), f64(vfull[b, :, h]), w.scale, True, 0)
+        assert_close(o64[b, :, h], ro, what=f"O b{b} h{h}")
+        assert_lse_close(l64[b, h], rl)

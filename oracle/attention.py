@@ -40,6 +40,9 @@ What is computed, and where the pages define it
   example of the MindSpore page (推理优化与KV缓存): the new k, v are written into
   the cache at position cache_seqlens, then q attends over the cache up to and
   including them.
+* ``kvcache_paged_fwd``: the same step with the caches stored in fixed-size
+  pages (the paged storage of the same section): logical row j of batch entry
+  b is row j mod P of page block_table[b, j div P].
 * fp8: ``e4m3_decode`` follows the OCP 8-bit floating point specification for
   E4M3 (bias 7, no infinities, S.1111.111 is NaN, max finite 448); the fp8
   forward is the plain definition applied to code * per-tensor scale (FA-3 FP8
@@ -79,6 +82,8 @@ __all__ = [
     "varlen_bwd",
     "merge_partials",
     "kvcache_fwd",
+    "paged_gather",
+    "kvcache_paged_fwd",
     "e4m3_decode",
     "fp8_dequant",
 ]
@@ -351,6 +356,38 @@ def kvcache_fwd(q, k_cache, v_cache, cache_seqlens, scale, causal=False, window=
         for h in range(h_):
             o[b, :, h], lse[b, h] = attention_fwd(q[b, :, h], kc[b, :nk, h], vc[b, :nk, h], scale, causal, window)
     return o, lse, kc, vc
+
+
+def paged_gather(blocks, block_table, page):
+    """Logical caches [B, max_blocks * page, H, d] from pages [num_blocks, page, H, d]:
+    row j of entry b is blocks[block_table[b, j // page], j % page]."""
+    blocks = np.asarray(blocks)
+    table = np.asarray(block_table, dtype=np.int64)
+    b_, mb = table.shape
+    out = np.empty((b_, mb * page) + blocks.shape[2:], dtype=blocks.dtype)
+    for b in range(b_):
+        for j in range(mb * page):
+            out[b, j] = blocks[table[b, j // page], j % page]
+    return out
+
+
+def kvcache_paged_fwd(q, k_blocks, v_blocks, block_table, page, cache_seqlens, scale, causal=False, window=0,
+                      k_new=None, v_new=None):
+    """kvcache_fwd on paged caches.  Returns (O, LSE, k_blocks', v_blocks'):
+    the pages after the new rows were written to the rows they map to."""
+    kc = paged_gather(np.asarray(k_blocks, dtype=np.float64), block_table, page)
+    vc = paged_gather(np.asarray(v_blocks, dtype=np.float64), block_table, page)
+    o, lse, kc2, vc2 = kvcache_fwd(q, kc, vc, cache_seqlens, scale, causal, window, k_new, v_new)
+    kb = np.array(k_blocks, dtype=np.float64)
+    vb = np.array(v_blocks, dtype=np.float64)
+    if k_new is not None:
+        table = np.asarray(block_table, dtype=np.int64)
+        nq = np.asarray(q).shape[1]
+        for b, t in enumerate(np.asarray(cache_seqlens, dtype=np.int64).reshape(-1)):
+            for j in range(int(t), int(t) + nq):
+                kb[table[b, j // page], j % page] = kc2[b, j]
+                vb[table[b, j // page], j % page] = vc2[b, j]
+    return o, lse, kb, vb
 
 
 def e4m3_decode(codes):

@@ -82,6 +82,17 @@ def _kvcache_forgets_new_keys(q, k_cache, v_cache, cache_seqlens, scale, causal=
     return o2, lse2, kc, vc
 
 
+def _paged_gather_swaps_index(blocks, block_table, page):
+    blocks = np.asarray(blocks)
+    table = np.asarray(block_table, dtype=np.int64)
+    b_, mb = table.shape
+    out = np.empty((b_, mb * page) + blocks.shape[2:], dtype=blocks.dtype)
+    for b in range(b_):
+        for j in range(mb * page):
+            out[b, j] = blocks[table[b, j % mb], j // mb]  # page and row index confused
+    return out
+
+
 _ORIG_MERGE = oa.merge_partials
 _ORIG_KVCACHE = oa.kvcache_fwd
 
@@ -96,6 +107,7 @@ MUTATIONS = [
     ("merge_partials", _merge_unnormalised, lambda: pins.test_merge_closed_forms()),
     ("merge_partials", _merge_lse_without_max,
      lambda: pins.test_merge_of_key_chunks_equals_full_attention(False, 0, [0, 7, 19, 40])),
+    ("paged_gather", _paged_gather_swaps_index, lambda: pins.test_paged_kvcache_equals_contiguous(4)),
     ("kvcache_fwd", _kvcache_forgets_new_keys,
      lambda: pins.test_kvcache_decode_equals_rows_of_the_full_sequence(1, True, 0)),
 ]

@@ -470,3 +470,37 @@ def test_kvcache_without_new_keys_reads_the_first_seqlen_rows():
         for c in range(3):
             assert abs(o[0, i, 0, c] - sum(w[j] * vc[0, j, 0, c] for j in range(pos + 1)) / tot) < 1e-12
         assert abs(lse[0, 0, i] - math.log(tot)) < 1e-12
+
+
+@pytest.mark.parametrize("page", [1, 4, 8])
+def test_paged_kvcache_equals_contiguous(page):
+    """Pages filled by scattering a contiguous cache through a shuffled block
+    table (written here, independently of the oracle's gather) give the
+    contiguous decode's result, and the appended rows land in the pages the
+    table names."""
+    rng = np.random.default_rng(page)
+    b_, h, d, nq, lmax = 3, 2, 4, 2, 24
+    lens = [5, 0, 21]
+    mb = lmax // page
+    q = rng.standard_normal((b_, nq, h, d))
+    kc = rng.standard_normal((b_, lmax, h, d))
+    vc = rng.standard_normal((b_, lmax, h, d))
+    kn = rng.standard_normal((b_, nq, h, d))
+    vn = rng.standard_normal((b_, nq, h, d))
+    table = rng.permutation(b_ * mb + 5)[:b_ * mb].reshape(b_, mb)  # 5 pages nobody uses
+    kb = np.full((b_ * mb + 5, page, h, d), np.nan)
+    vb = np.full((b_ * mb + 5, page, h, d), np.nan)
+    for b in range(b_):
+        for j in range(lmax):
+            kb[table[b, j // page], j % page] = kc[b, j]
+            vb[table[b, j // page], j % page] = vc[b, j]
+    o, lse, kb2, vb2 = oracle.kvcache_paged_fwd(q, kb, vb, table, page, lens, 0.4, True, 0, kn, vn)
+    ro, rl, rkc, _ = oracle.kvcache_fwd(q, kc, vc, lens, 0.4, True, 0, kn, vn)
+    np.testing.assert_array_equal(o, ro)
+    np.testing.assert_array_equal(lse, rl)
+    for b, t in enumerate(lens):
+        for i in range(nq):
+            j = t + i
+            np.testing.assert_array_equal(kb2[table[b, j // page], j % page], kn[b, i])
+    unused = sorted(set(range(b_ * mb + 5)) - set(table.ravel().tolist()))
+    assert np.isnan(kb2[unused]).all()

@@ -141,19 +141,32 @@ def merge_inputs(torch):
     return o_p, lse_p, out, lse, nbytes
 
 
-def kvcache_step(torch, fa):
+def kvcache_step(torch, fa, page=0):
     """One decode step at B8 H32 d128 with 8191 cached tokens + 1 new: the
     step function (idempotent: it appends at the same row each time) and the
-    bytes it must move (every cached K/V row once, plus q, the new rows and O)."""
+    bytes it must move (every cached K/V row once, plus q, the new rows and O).
+    page > 0: the caches are cut into pages of that many rows, stored in a
+    seeded random order and addressed through a block table."""
     from exact_attention_24_amd.inputs import WORKLOADS, kvcache_inputs
     w = WORKLOADS["kvcache_b8_h32"]
     q, kc, vc, kn, vn = (x.cuda() for x in kvcache_inputs(w.batch, w.seqlen, w.heads, w.head_dim, 1, seed=w.seed))
+    table = None
+    if page:
+        mb = w.seqlen // page
+        perm = torch.randperm(w.batch * mb, generator=torch.Generator().manual_seed(9)).cuda()
+        table = perm.reshape(w.batch, mb).to(torch.int32)
+        shape = (w.batch * mb, page, w.heads, w.head_dim)
+        kb, vb = torch.empty(shape, dtype=kc.dtype, device="cuda"), torch.empty(shape, dtype=kc.dtype, device="cuda")
+        kb[perm] = kc.reshape(shape)
+        vb[perm] = vc.reshape(shape)
+        kc, vc = kb, vb
     seq = torch.full((w.batch,), w.seqlen - 1, dtype=torch.int32, device="cuda")
     out = torch.empty_like(q)
     lse = torch.empty(w.batch, w.heads, 1, dtype=torch.float32, device="cuda")
     row = w.batch * w.heads * w.head_dim * 2
     nbytes = 2 * w.seqlen * row + 4 * row + w.batch * w.heads * 4
-    fn = lambda: fa.fa_fwd_kvcache(q, kc, vc, kn, vn, cache_seqlens=seq, causal=True, out=out, lse=lse)
+    fn = lambda: fa.fa_fwd_kvcache(q, kc, vc, kn, vn, cache_seqlens=seq, causal=True, out=out, lse=lse,
+                                   block_table=table)
     return fn, nbytes
 
 
@@ -226,6 +239,14 @@ def extra_rows(torch, fa, steps):
                                             "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
     except Exception as e:
         rows["kvcache_decode_b8_h32_8k"] = {"error": str(e)[:120]}
+    try:
+        fn, nbytes = kvcache_step(torch, fa, page=256)
+        _, ms = time_calls(fn, 2, steps, torch)
+        gbs = nbytes / med(ms) / 1e6
+        rows["kvcache_paged256_decode_b8_h32_8k"] = {"ms": round(med(ms), 4), "GB/s": round(gbs, 1),
+                                                     "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    except Exception as e:
+        rows["kvcache_paged256_decode_b8_h32_8k"] = {"error": str(e)[:120]}
     # fp8 forward
     try:
         t = workload_inputs("fp8_n8192")

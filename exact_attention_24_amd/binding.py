@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 FA_F32, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_DTYPE_MISMATCH, FA_ERR_UNSUPPORTED, FA_ERR_HIP = range(5)
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _I64x4 = ctypes.c_int64 * 4
 _I64x3 = ctypes.c_int64 * 3
@@ -107,6 +107,7 @@ class KvcacheParams(ctypes.Structure):
         ("vn_stride", _I64x3), ("o_stride", _I64x3),
         ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
         ("num_splits", ctypes.c_int32),
+        ("block_table", ctypes.c_void_p), ("page_block_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
     ]
 
 
@@ -458,7 +459,7 @@ def fa_merge(o_parts, lse_parts, out=None, lse=None, out_dtype=None, return_lse=
 # KV-cache decode
 # ---------------------------------------------------------------------------
 def make_kvcache_params(q, k_cache, v_cache, k_new, v_new, cache_seqlens, o, lse, causal=False, window=0,
-                        softmax_scale=None, num_splits=0):
+                        softmax_scale=None, num_splits=0, block_table=None):
     for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("o", o)):
         if t.dim() != 4:
             raise ValueError(f"{n} must be [batch, seqlen, heads, head_dim] (got {tuple(t.shape)})")
@@ -469,9 +470,18 @@ def make_kvcache_params(q, k_cache, v_cache, k_new, v_new, cache_seqlens, o, lse
     if len({_code(t) for t in tensors}) != 1:
         raise ValueError("Input and output tensors must have the same dtype (q, caches, new k/v differ)")
     b, nq, h, d = q.shape
-    lmax = k_cache.shape[1]
-    if k_cache.shape != (b, lmax, h, d) or v_cache.shape != (b, lmax, h, d):
-        raise ValueError("k_cache, v_cache must be [batch, cache_len, heads, head_dim] matching q")
+    if block_table is None:
+        lmax = k_cache.shape[1]
+        if k_cache.shape != (b, lmax, h, d) or v_cache.shape != (b, lmax, h, d):
+            raise ValueError("k_cache, v_cache must be [batch, cache_len, heads, head_dim] matching q")
+    else:
+        nb, page = k_cache.shape[:2]
+        if k_cache.shape != (nb, page, h, d) or v_cache.shape != (nb, page, h, d):
+            raise ValueError("paged k_cache, v_cache must be [num_blocks, page_block_size, heads, head_dim]")
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != b \
+                or not block_table.is_contiguous():
+            raise ValueError("block_table must be a contiguous int32 [batch, max_blocks_per_seq] tensor")
+        lmax = block_table.shape[1] * page
     if k_new is not None and (k_new.shape != q.shape or v_new.shape != q.shape):
         raise ValueError("k, v must have q's shape [batch, seqlen_q, heads, head_dim]")
     if o.shape != q.shape:
@@ -495,6 +505,9 @@ def make_kvcache_params(q, k_cache, v_cache, k_new, v_new, cache_seqlens, o, lse
     p.o_stride = _I64x3(*o.stride()[:3])
     p.softmax_scale = _default_scale(d, softmax_scale)
     p.causal, p.window, p.num_splits = int(bool(causal)), int(window), int(num_splits)
+    if block_table is not None:
+        p.block_table = _ptr(block_table)
+        p.page_block_size, p.max_blocks_per_seq = k_cache.shape[1], block_table.shape[1]
     return p
 
 
@@ -507,21 +520,23 @@ def fa_kvcache_workspace_bytes(params: KvcacheParams) -> int:
 
 
 def fa_fwd_kvcache(q, k_cache, v_cache, k=None, v=None, cache_seqlens=0, causal=False, window=0,
-                   softmax_scale=None, num_splits=0, out=None, lse=None, return_lse=True):
+                   softmax_scale=None, num_splits=0, out=None, lse=None, return_lse=True, block_table=None):
     """One decoding step against a KV cache (the caches are updated in place
     when k, v are given).  cache_seqlens: an int for every batch entry, or an
-    int32 [batch] tensor on the device."""
+    int32 [batch] tensor on the device.  block_table (int32 [batch,
+    max_blocks]) makes k_cache, v_cache paged: [num_blocks, page, H, d]."""
     b, nq, h, d = q.shape
+    cap = k_cache.shape[1] if block_table is None else block_table.shape[1] * k_cache.shape[1]
     if isinstance(cache_seqlens, int):
-        if cache_seqlens < 0 or cache_seqlens + (nq if k is not None else 0) > k_cache.shape[1]:
-            raise ValueError(f"cache_seqlens={cache_seqlens} does not fit cache_len={k_cache.shape[1]}")
+        if cache_seqlens < 0 or cache_seqlens + (nq if k is not None else 0) > cap:
+            raise ValueError(f"cache_seqlens={cache_seqlens} does not fit cache_len={cap}")
         cache_seqlens = torch.full((b,), cache_seqlens, dtype=torch.int32, device=q.device)
     if out is None:
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((b, h, nq), dtype=torch.float32, device=q.device)
     p = make_kvcache_params(q, k_cache, v_cache, k, v, cache_seqlens, out, lse, causal, window, softmax_scale,
-                            num_splits)
+                            num_splits, block_table)
     _raise(lib().fa_check_kvcache(ctypes.byref(p)))
     nbytes = fa_kvcache_workspace_bytes(p)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)

@@ -485,8 +485,18 @@ fa_status fa_check_kvcache(const fa_kvcache_params *p) {
   if ((st = check_tensor("q", p->q, p->q_stride, 3, 2, empty, p->seqlen_q, hd)) != FA_OK) return st;
   if ((st = check_tensor("o", p->o, p->o_stride, 3, 2, empty, p->seqlen_q, hd)) != FA_OK) return st;
   const bool no_cache = empty || p->cache_len == 0;
-  if ((st = check_tensor("k_cache", p->k_cache, p->kc_stride, 3, 2, no_cache, p->cache_len, hd)) != FA_OK) return st;
-  if ((st = check_tensor("v_cache", p->v_cache, p->vc_stride, 3, 2, no_cache, p->cache_len, hd)) != FA_OK) return st;
+  int64_t cache_rows = p->cache_len;
+  if (p->block_table) {
+    const int pg = p->page_block_size;
+    if (pg <= 0 || (pg & (pg - 1)))
+      return fail(FA_ERR_INVALID_ARGUMENT, "page_block_size must be a power of two (got %d)", pg);
+    if (p->max_blocks_per_seq < 0 || (int64_t)p->cache_len > (int64_t)p->max_blocks_per_seq * pg)
+      return fail(FA_ERR_INVALID_ARGUMENT, "cache_len (%d) exceeds max_blocks_per_seq (%d) * page_block_size (%d)",
+                  p->cache_len, p->max_blocks_per_seq, pg);
+    cache_rows = pg;
+  }
+  if ((st = check_tensor("k_cache", p->k_cache, p->kc_stride, 3, 2, no_cache, cache_rows, hd)) != FA_OK) return st;
+  if ((st = check_tensor("v_cache", p->v_cache, p->vc_stride, 3, 2, no_cache, cache_rows, hd)) != FA_OK) return st;
   if (p->k_new) {
     if (p->cache_len < p->seqlen_q)
       return fail(FA_ERR_INVALID_ARGUMENT, "cache_len (%d) cannot hold the %d new rows", p->cache_len, p->seqlen_q);
@@ -529,6 +539,11 @@ fa_status fa_fwd_kvcache(const fa_kvcache_params *p, void *workspace, size_t wor
   a.causal = p->causal; a.window = p->window; a.num_splits = splits;
   a.split_len = splits == 1 ? p->cache_len : (int)((((int64_t)p->cache_len + splits - 1) / splits + 63) / 64 * 64);
   a.scale_log2 = p->softmax_scale * kLog2e;
+  a.block_table = p->block_table;
+  if (p->block_table) {
+    a.max_blocks = p->max_blocks_per_seq;
+    while ((1 << a.page_shift) < p->page_block_size) ++a.page_shift;
+  }
   const size_t rows = (size_t)splits * p->batch * p->seqlen_q * p->heads;
   if (splits > 1) {
     a.o_parts = static_cast<float *>(workspace);

@@ -18,7 +18,9 @@
 // 16 bytes each, so one wave-wide load covers 64/(d/8) keys; every lane group
 // keeps its own online-softmax state (running max m, sum l, its 8 columns of
 // O) per query, and the states of the groups, then of the waves, are joined
-// at the end.  Loads run one step ahead of the arithmetic.
+// at the end.  Loads run one step ahead of the arithmetic.  Paged caches
+// (fixed-size pages named by a block table, the paged storage of the same
+// section) differ only in how a logical row is addressed.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -39,7 +41,19 @@ constexpr float kLazy = 8.f;  // the running max moves only when a score exceeds
 // ---------------------------------------------------------------------------
 // Append: k_new, v_new rows (b, i, h) go to cache row cache_seqlens[b] + i.
 // ---------------------------------------------------------------------------
-template <int D>
+// Element offset of logical cache row j of batch entry b (block and token
+// strides sb, st): contiguous, or through the block table.
+template <bool PAGED>
+__device__ __forceinline__ int64_t cache_row(const DecodeArgs &a, int b, int j, int64_t sb, int64_t st) {
+  if constexpr (PAGED) {
+    const int blk = a.block_table[(int64_t)b * a.max_blocks + (j >> a.page_shift)];
+    return blk * sb + (int64_t)(j & ((1 << a.page_shift) - 1)) * st;
+  } else {
+    return b * sb + (int64_t)j * st;
+  }
+}
+
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void kv_append_kernel(DecodeArgs a, int64_t rows) {
   constexpr int LPR = D / 8, RPB = 256 / LPR;
   const int tid = threadIdx.x, c = tid % LPR;
@@ -48,11 +62,11 @@ __global__ __launch_bounds__(256) void kv_append_kernel(DecodeArgs a, int64_t ro
   const int h = (int)(row % a.heads);
   const int64_t bi = row / a.heads;
   const int i = (int)(bi % a.nq), b = (int)(bi / a.nq);
-  const int64_t t = (int64_t)a.cache_seqlens[b] + i;
+  const int t = a.cache_seqlens[b] + i;
   const uint4 kx = *(const uint4 *)((const uint16_t *)a.k_new + b * a.kn_sb + (int64_t)i * a.kn_st + h * a.kn_sh + c * 8);
   const uint4 vx = *(const uint4 *)((const uint16_t *)a.v_new + b * a.vn_sb + (int64_t)i * a.vn_st + h * a.vn_sh + c * 8);
-  *(uint4 *)((uint16_t *)a.k_cache + b * a.kc_sb + t * a.kc_st + h * a.kc_sh + c * 8) = kx;
-  *(uint4 *)((uint16_t *)a.v_cache + b * a.vc_sb + t * a.vc_st + h * a.vc_sh + c * 8) = vx;
+  *(uint4 *)((uint16_t *)a.k_cache + cache_row<PAGED>(a, b, t, a.kc_sb, a.kc_st) + h * a.kc_sh + c * 8) = kx;
+  *(uint4 *)((uint16_t *)a.v_cache + cache_row<PAGED>(a, b, t, a.vc_sb, a.vc_st) + h * a.vc_sh + c * 8) = vx;
 }
 
 __device__ __forceinline__ float dot8(const uint32_t (&q)[4], const uint4 &k) {
@@ -80,7 +94,7 @@ __device__ __forceinline__ void join_state(float &m, float &l, float (&acc)[N], 
 // ---------------------------------------------------------------------------
 // Decode: one work-group per (batch, head, split); NQ >= nq query rows.
 // ---------------------------------------------------------------------------
-template <int D, int NQ>
+template <int D, int NQ, bool PAGED>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr int LPK = D / 8;   // lanes per key row
   constexpr int G = 64 / LPK;  // keys per wave-wide load
@@ -118,15 +132,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
   }
 
-  const uint16_t *kb = (const uint16_t *)a.k_cache + b * a.kc_sb + h * a.kc_sh + c * 8;
-  const uint16_t *vb = (const uint16_t *)a.v_cache + b * a.vc_sb + h * a.vc_sh + c * 8;
+  const uint16_t *kb = (const uint16_t *)a.k_cache + h * a.kc_sh + c * 8;
+  const uint16_t *vb = (const uint16_t *)a.v_cache + h * a.vc_sh + c * 8;
   const int jw = wave * KW + g;  // this lane group's first key of a step
   // rows j >= hi read as zeros (and are masked)
   auto load_kv = [&](int j, uint4 &kx, uint4 &vx) __attribute__((always_inline)) {
     kx = vx = uint4{0u, 0u, 0u, 0u};
     if (j < hi) {
-      kx = *(const uint4 *)(kb + (int64_t)j * a.kc_st);
-      vx = *(const uint4 *)(vb + (int64_t)j * a.vc_st);
+      kx = *(const uint4 *)(kb + cache_row<PAGED>(a, b, j, a.kc_sb, a.kc_st));
+      vx = *(const uint4 *)(vb + cache_row<PAGED>(a, b, j, a.vc_sb, a.vc_st));
     }
   };
   uint4 kc[U], vc[U];
@@ -227,21 +241,28 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
 }
 
+template <int D, bool PAGED>
+hipError_t launch_decode_p(const DecodeArgs &a, hipStream_t s) {
+  const dim3 grid((unsigned)((int64_t)a.batch * a.heads * a.num_splits));
+  if (a.nq <= 1) hipLaunchKernelGGL((decode_kernel<D, 1, PAGED>), grid, dim3(256), 0, s, a);
+  else if (a.nq <= 2) hipLaunchKernelGGL((decode_kernel<D, 2, PAGED>), grid, dim3(256), 0, s, a);
+  else if (a.nq <= 4) hipLaunchKernelGGL((decode_kernel<D, 4, PAGED>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((decode_kernel<D, 8, PAGED>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs &a, hipStream_t s) {
-  const dim3 grid((unsigned)((int64_t)a.batch * a.heads * a.num_splits));
-  if (a.nq <= 1) hipLaunchKernelGGL((decode_kernel<D, 1>), grid, dim3(256), 0, s, a);
-  else if (a.nq <= 2) hipLaunchKernelGGL((decode_kernel<D, 2>), grid, dim3(256), 0, s, a);
-  else if (a.nq <= 4) hipLaunchKernelGGL((decode_kernel<D, 4>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((decode_kernel<D, 8>), grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+  return a.block_table ? launch_decode_p<D, true>(a, s) : launch_decode_p<D, false>(a, s);
 }
 
 template <int D>
 hipError_t launch_kv_append_d(const DecodeArgs &a, hipStream_t s) {
   const int64_t rows = (int64_t)a.batch * a.nq * a.heads;
   constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL((kv_append_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, a, rows);
+  const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
+  if (a.block_table) hipLaunchKernelGGL((kv_append_kernel<D, true>), grid, dim3(256), 0, s, a, rows);
+  else hipLaunchKernelGGL((kv_append_kernel<D, false>), grid, dim3(256), 0, s, a, rows);
   return hipGetLastError();
 }
 

@@ -72,6 +72,8 @@ struct DecodeArgs {
   int32_t batch, nq, cache_len, heads;
   int32_t causal, window, num_splits, split_len;
   float scale_log2;
+  const int32_t *block_table;       // paged caches: [batch, max_blocks] (else null; strides above are then
+  int32_t page_shift, max_blocks;   // {block, token, head} of [num_blocks, 2^page_shift, heads, d])
 };
 
 // Launchers (defined in the kernel translation units).  Each returns the

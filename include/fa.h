@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 typedef enum {
   FA_F32 = 0,       /* IEEE binary32 */
@@ -226,6 +226,17 @@ typedef struct {
   int64_t q_stride[3], kc_stride[3], vc_stride[3], kn_stride[3], vn_stride[3], o_stride[3];
   float softmax_scale;
   int32_t causal, window, num_splits;
+  /* Paged caches (the paged storage of the same section), or NULL: then
+   * k_cache, v_cache are [num_blocks, page_block_size, heads, head_dim] with
+   * kc_stride / vc_stride = {block, token, head}, and logical row j of batch
+   * entry b is row j % page_block_size of block block_table[b][j /
+   * page_block_size].  block_table: DEVICE int32 [batch, max_blocks_per_seq],
+   * row-major.  page_block_size is a power of two; cache_len (the logical
+   * capacity) must be <= max_blocks_per_seq * page_block_size.  Unchecked
+   * contract: every entry for a row below L_b names an existing block, and no
+   * two appended rows map to the same physical row. */
+  const int32_t *block_table;
+  int32_t page_block_size, max_blocks_per_seq;
 } fa_kvcache_params;
 
 /* Host-only validation: never touches a device.  Returns the status the

@@ -225,6 +225,16 @@ def test_kvcache_checks(lib):
         assert lib.fa_check_kvcache(ctypes.byref(p)) == code, field
     with pytest.raises(ValueError, match="cache_seqlens"):
         B.fa_fwd_kvcache(q, kc, kc, q, q, cache_seqlens=4096)  # no room for the new row
+    # paged: [num_blocks, page, H, d] pages and an int32 [batch, max_blocks] table
+    pages = torch.zeros(10, 64, 4, 128, dtype=torch.bfloat16)
+    table = torch.zeros(2, 5, dtype=torch.int32)
+    p = B.make_kvcache_params(q, pages, pages, q, q, seq, o, lse, causal=True, block_table=table)
+    assert lib.fa_check_kvcache(ctypes.byref(p)) == B.FA_OK and p.cache_len == 320
+    p.page_block_size = 48  # not a power of two
+    assert lib.fa_check_kvcache(ctypes.byref(p)) == B.FA_ERR_INVALID_ARGUMENT
+    p = B.make_kvcache_params(q, pages, pages, q, q, seq, o, lse, causal=True, block_table=table)
+    p.cache_len = 321  # more rows than the table can map
+    assert lib.fa_check_kvcache(ctypes.byref(p)) == B.FA_ERR_INVALID_ARGUMENT
 
 
 def test_python_layer_error_mapping(lib):

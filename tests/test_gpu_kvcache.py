@@ -106,3 +106,56 @@ def test_kvcache_llama_8k_step():
         ro, rl = oracle.attention_fwd(f64(q[b, :, h]), f64(kfull[b, :, h]), f64(vfull[b, :, h]), w.scale, True, 0)
         assert_close(o64[b, :, h], ro, what=f"O b{b} h{h}")
         assert_lse_close(l64[b, h], rl)
+
+
+def _paged(kc, vc, page, extra, seed):
+    """Scatter contiguous caches [B, L, H, d] into pages through a shuffled
+    block table; `extra` pages nobody uses hold NaN."""
+    b_, lmax = kc.shape[:2]
+    mb = lmax // page
+    g = torch.Generator().manual_seed(seed)
+    table = torch.randperm(b_ * mb + extra, generator=g)[:b_ * mb].reshape(b_, mb).to(torch.int32)
+    kb = torch.full((b_ * mb + extra, page) + tuple(kc.shape[2:]), float("nan"), dtype=kc.dtype)
+    vb = kb.clone()
+    for b in range(b_):
+        for blk in range(mb):
+            kb[table[b, blk]] = kc[b, blk * page:(blk + 1) * page]
+            vb[table[b, blk]] = vc[b, blk * page:(blk + 1) * page]
+    return kb, vb, table
+
+
+@pytest.mark.parametrize("page,nq,lens,window,splits", [
+    (16, 1, [0, 37, 190], 0, 0), (64, 3, [100, 5], 50, 2), (256, 1, [1000, 511], 0, 3),
+])
+def test_kvcache_paged_elementwise(page, nq, lens, window, splits):
+    b, h, d = len(lens), 2, 128
+    lmax = ((max(lens) + nq + page - 1) // page + 1) * page
+    print(f"[kvcache paged] page={page} nq={nq} lens={lens} window={window} splits={splits} lmax={lmax}", flush=True)
+    q, kc, vc, kn, vn = kvcache_inputs(b, lmax, h, d, nq, seed=page + nq)
+    kc, vc = _nan_tail(kc, lens, nq), _nan_tail(vc, lens, nq)
+    kb, vb, table = _paged(kc, vc, page, extra=3, seed=page)
+    kbd, vbd = kb.to(DEV), vb.to(DEV)
+    o, lse = fa_fwd_kvcache(q.to(DEV), kbd, vbd, kn.to(DEV), vn.to(DEV), cache_seqlens=torch.tensor(lens, dtype=torch.int32,
+                            device=DEV), causal=True, window=window, num_splits=splits, block_table=table.to(DEV))
+    torch.cuda.synchronize()
+    ro, rl, rkb, rvb = oracle.kvcache_paged_fwd(f64(q), f64(kb), f64(vb), table.numpy(), page, lens, 1 / np.sqrt(d),
+                                                True, window, f64(kn), f64(vn))
+    assert_close(f64(o), ro)
+    assert_lse_close(f64(lse), rl)
+    np.testing.assert_array_equal(f64(kbd), rkb)
+    np.testing.assert_array_equal(f64(vbd), rvb)
+
+
+def test_kvcache_paged_equals_contiguous_bitwise_at_8k():
+    """B8 H32 d128, 8191 cached + 1 new, pages of 256 through a shuffled table:
+    the same bits as the contiguous cache (only the addressing differs)."""
+    w = WORKLOADS["kvcache_b8_h32"]
+    q, kc, vc, kn, vn = kvcache_inputs(w.batch, w.seqlen, w.heads, w.head_dim, 1, seed=w.seed)
+    kb, vb, table = _paged(kc, vc, 256, extra=0, seed=5)
+    print("[kvcache paged 8k] launching", flush=True)
+    qd, knd, vnd = q.to(DEV), kn.to(DEV), vn.to(DEV)
+    o1, l1 = fa_fwd_kvcache(qd, kc.to(DEV), vc.to(DEV), knd, vnd, cache_seqlens=w.seqlen - 1, causal=True)
+    o2, l2 = fa_fwd_kvcache(qd, kb.to(DEV), vb.to(DEV), knd, vnd, cache_seqlens=w.seqlen - 1, causal=True,
+                            block_table=table.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

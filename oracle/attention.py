@@ -43,6 +43,22 @@ What is computed, and where the pages define it
 * ``kvcache_paged_fwd``: the same step with the caches stored in fixed-size
   pages (the paged storage of the same section): logical row j of batch entry
   b is row j mod P of page block_table[b, j div P].
+* Dropout on the attention probabilities (``dropout_p`` on every API
+  signature of the MindSpore page; fused with softmax and mask in the FA-2
+  paragraph of the ms-swift integration page): O = (P * keep * s) V with
+  LSE unchanged.  The keep mask comes from the counter-based generator
+  Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
+  as 1, 2, 3", SC 2011), written here from that paper's definition, so the
+  backward can regenerate it instead of storing it:
+    - one random byte per (query row i, key j) of head slot
+      b * heads + h: byte (j mod 4) of word ((j mod 32) div 8) of
+      Philox(counter = (2 (j div 32) + ((j div 4) mod 2), i, slot, offset),
+      key = (seed mod 2^32, seed div 2^32));
+    - the element is kept iff its byte < K = round(256 (1 - p)) (at least 1),
+      and kept values are scaled by s = 256 / K, so p is in effect rounded to
+      a multiple of 1/256 and the expectation of O is the undropped O.
+  The backward is the chain rule through the same mask: dV = (P keep s)^T
+  dO, dP = keep s (dO V^T), D = rowsum(dO * O), dS = P (dP - D).
 * fp8: ``e4m3_decode`` follows the OCP 8-bit floating point specification for
   E4M3 (bias 7, no infinities, S.1111.111 is NaN, max finite 448); the fp8
   forward is the plain definition applied to code * per-tensor scale (FA-3 FP8
@@ -80,6 +96,9 @@ __all__ = [
     "mha_bwd",
     "varlen_fwd",
     "varlen_bwd",
+    "philox4x32",
+    "dropout_bytes",
+    "dropout_keep",
     "merge_partials",
     "kvcache_fwd",
     "paged_gather",
@@ -135,36 +154,41 @@ def attention_probs(q, k, scale, causal=False, window=0, q_pos=None, nq=None):
     return p
 
 
-def attention_fwd(q, k, v, scale, causal=False, window=0, q_pos=None, nq=None):
+def attention_fwd(q, k, v, scale, causal=False, window=0, q_pos=None, nq=None, drop=None):
     """One head: q [nq_sel, d], k [nk, d], v [nk, dv] -> (O [nq_sel, dv], LSE [nq_sel]).
 
     ``q_pos`` (default 0..nq_sel-1) gives the index of each given row in a
     query sequence of length ``nq`` (default nq_sel), so that sampled rows of a
     long sequence can be checked one by one.  LSE is natural-log.
+    ``drop`` = (keep [nq_sel, nk] bool, s): dropout of the probabilities.
     """
     s = _scores(q, k, scale, causal, window, q_pos, nq)
     p, m, l = _softmax_rows(s)
+    if drop is not None:
+        p = p * drop[0] * drop[1]
     o = p @ np.asarray(v, dtype=np.float64)
     with np.errstate(divide="ignore"):
         lse = np.where(l > 0, m + np.log(l), -np.inf)
     return o, lse
 
 
-def attention_bwd(q, k, v, dout, scale, causal=False, window=0):
+def attention_bwd(q, k, v, dout, scale, causal=False, window=0, drop=None):
     """One head, all rows: gradients of L = sum(dout * O) w.r.t. q, k, v (fp64).
 
     D_i = sum_c dO_ic O_ic;  dV = P^T dO;  dP = dO V^T;  dS = P * (dP - D);
-    dQ = scale dS K;  dK = scale dS^T Q.
+    dQ = scale dS K;  dK = scale dS^T Q.  With ``drop`` = (keep, s) the
+    forward used P keep s, so dV = (P keep s)^T dO and dP = keep s (dO V^T).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     do = np.asarray(dout, dtype=np.float64)
     p = attention_probs(q, k, scale, causal, window)
-    o = p @ v
+    ks = np.ones_like(p) if drop is None else drop[0] * float(drop[1])
+    o = (p * ks) @ v
     d_row = (do * o).sum(axis=1)
-    dv = p.T @ do
-    dp = do @ v.T
+    dv = (p * ks).T @ do
+    dp = (do @ v.T) * ks
     ds = p * (dp - d_row[:, None])
     dq = float(scale) * (ds @ k)
     dk = float(scale) * (ds.T @ q)
@@ -215,12 +239,57 @@ def blocked_fwd(q, k, v, scale, causal=False, window=0, br=16, bc=16):
     return o, lse
 
 
-def mha_fwd(q, k, v, scale, causal=False, window=0, heads=None):
+def philox4x32(counter, key, rounds=10):
+    """Philox4x32 (Salmon et al., SC 2011): counter [..., 4], key (k0, k1) of
+    unsigned 32-bit words -> [..., 4] uint32.
+
+    Each round multiplies words 0 and 2 by 0xD2511F53 and 0xCD9E8D57 into
+    64-bit products (hi, lo) and forms (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1,
+    lo0); between rounds the key is bumped by the Weyl constants 0x9E3779B9
+    and 0xBB67AE85 (mod 2^32).
+    """
+    m32 = np.uint64(0xFFFFFFFF)
+    c = np.asarray(counter, dtype=np.uint64) & m32
+    c0, c1, c2, c3 = (c[..., i] for i in range(4))
+    k0 = np.uint64(int(key[0]) & 0xFFFFFFFF)
+    k1 = np.uint64(int(key[1]) & 0xFFFFFFFF)
+    for r in range(rounds):
+        if r:
+            k0 = (k0 + np.uint64(0x9E3779B9)) & m32
+            k1 = (k1 + np.uint64(0xBB67AE85)) & m32
+        p0 = np.uint64(0xD2511F53) * c0
+        p1 = np.uint64(0xCD9E8D57) * c2
+        c0, c1, c2, c3 = (p1 >> np.uint64(32)) ^ c1 ^ k0, p1 & m32, (p0 >> np.uint64(32)) ^ c3 ^ k1, p0 & m32
+    return np.stack([c0, c1, c2, c3], axis=-1).astype(np.uint32)
+
+
+def dropout_bytes(slot, q_rows, nk, seed, offset):
+    """Random bytes [len(q_rows), nk] of head slot ``slot`` (see the module
+    docstring for the element -> (counter, word, byte) map)."""
+    i = np.asarray(q_rows, dtype=np.uint64)[:, None]
+    j = np.arange(nk, dtype=np.uint64)[None, :]
+    ctr = np.stack(np.broadcast_arrays(2 * (j >> np.uint64(5)) + ((j >> np.uint64(2)) & np.uint64(1)), i,
+                                       np.uint64(slot), np.uint64(offset & 0xFFFFFFFF)), axis=-1)
+    words = philox4x32(ctr, (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF))   # [rows, nk, 4]
+    widx = np.broadcast_to(((j & np.uint64(31)) >> np.uint64(3)).astype(np.int64), words.shape[:2])
+    w = np.take_along_axis(words, widx[..., None], axis=-1)[..., 0]
+    shift = (np.uint32(8) * (j & np.uint64(3)).astype(np.uint32))
+    return ((w >> shift) & np.uint32(0xFF)).astype(np.uint8)
+
+
+def dropout_keep(slot, q_rows, nk, seed, offset, p):
+    """(keep [len(q_rows), nk] bool, s): keep iff byte < K = round(256 (1 - p)), s = 256 / K."""
+    kthr = max(1, int(round(256.0 * (1.0 - float(p)))))
+    return dropout_bytes(slot, q_rows, nk, seed, offset) < kthr, 256.0 / kthr
+
+
+def mha_fwd(q, k, v, scale, causal=False, window=0, heads=None, dropout=None):
     """Dense multi-head forward in [B, N, H, d] layout.
 
     Returns O [B, Nq, H, dv] and LSE [B, H, Nq].  ``heads`` restricts the
     computation to a list of (b, h) pairs (others are left NaN), for large
-    shapes where only sampled heads are checked.
+    shapes where only sampled heads are checked.  ``dropout`` = (p, seed,
+    offset): head slot b * H + h.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -230,11 +299,13 @@ def mha_fwd(q, k, v, scale, causal=False, window=0, heads=None):
     lse = np.full((b_, h_, nq), np.nan)
     pairs = heads if heads is not None else [(b, h) for b in range(b_) for h in range(h_)]
     for b, h in pairs:
-        o[b, :, h], lse[b, h] = attention_fwd(q[b, :, h], k[b, :, h], v[b, :, h], scale, causal, window)
+        drop = None if dropout is None else dropout_keep(b * h_ + h, range(nq), k.shape[1], dropout[1], dropout[2],
+                                                         dropout[0])
+        o[b, :, h], lse[b, h] = attention_fwd(q[b, :, h], k[b, :, h], v[b, :, h], scale, causal, window, drop=drop)
     return o, lse
 
 
-def mha_bwd(q, k, v, dout, scale, causal=False, window=0, heads=None):
+def mha_bwd(q, k, v, dout, scale, causal=False, window=0, heads=None, dropout=None):
     """Dense multi-head backward in [B, N, H, d] layout -> (dq, dk, dv)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -246,12 +317,14 @@ def mha_bwd(q, k, v, dout, scale, causal=False, window=0, heads=None):
     b_, _, h_, _ = q.shape
     pairs = heads if heads is not None else [(b, h) for b in range(b_) for h in range(h_)]
     for b, h in pairs:
+        drop = None if dropout is None else dropout_keep(b * h_ + h, range(q.shape[1]), k.shape[1], dropout[1],
+                                                         dropout[2], dropout[0])
         dq[b, :, h], dk[b, :, h], dv[b, :, h] = attention_bwd(
-            q[b, :, h], k[b, :, h], v[b, :, h], dout[b, :, h], scale, causal, window)
+            q[b, :, h], k[b, :, h], v[b, :, h], dout[b, :, h], scale, causal, window, drop=drop)
     return dq, dk, dv
 
 
-def varlen_fwd(q, k, v, cu_seqlens, scale, causal=False, window=0, heads=None, seqs=None):
+def varlen_fwd(q, k, v, cu_seqlens, scale, causal=False, window=0, heads=None, seqs=None, dropout=None):
     """Packed sequences: q/k/v [total, H, d]; sequence s spans rows
     cu_seqlens[s]:cu_seqlens[s+1] and attends only within itself.
 
@@ -272,11 +345,13 @@ def varlen_fwd(q, k, v, cu_seqlens, scale, causal=False, window=0, heads=None, s
         if b == a:
             continue
         for h in hs:
-            o[a:b, h], lse[h, a:b] = attention_fwd(q[a:b, h], k[a:b, h], v[a:b, h], scale, causal, window)
+            drop = None if dropout is None else dropout_keep(s * h_ + h, range(b - a), b - a, dropout[1], dropout[2],
+                                                             dropout[0])
+            o[a:b, h], lse[h, a:b] = attention_fwd(q[a:b, h], k[a:b, h], v[a:b, h], scale, causal, window, drop=drop)
     return o, lse
 
 
-def varlen_bwd(q, k, v, dout, cu_seqlens, scale, causal=False, window=0, heads=None, seqs=None):
+def varlen_bwd(q, k, v, dout, cu_seqlens, scale, causal=False, window=0, heads=None, seqs=None, dropout=None):
     """Gradients for packed sequences (the same layout as ``varlen_fwd``).
 
     Each sequence is an independent attention problem, so its gradients are
@@ -300,8 +375,10 @@ def varlen_bwd(q, k, v, dout, cu_seqlens, scale, causal=False, window=0, heads=N
         if b == a:
             continue
         for h in hs:
+            drop = None if dropout is None else dropout_keep(s * h_ + h, range(b - a), b - a, dropout[1], dropout[2],
+                                                             dropout[0])
             dq[a:b, h], dk[a:b, h], dv[a:b, h] = attention_bwd(q[a:b, h], k[a:b, h], v[a:b, h], dout[a:b, h],
-                                                               scale, causal, window)
+                                                               scale, causal, window, drop=drop)
     return dq, dk, dv
 
 

@@ -93,6 +93,26 @@ def _paged_gather_swaps_index(blocks, block_table, page):
     return out
 
 
+def _philox_no_key_bump(counter, key, rounds=10):
+    m32 = np.uint64(0xFFFFFFFF)
+    c = np.asarray(counter, dtype=np.uint64) & m32
+    c0, c1, c2, c3 = (c[..., i] for i in range(4))
+    k0, k1 = np.uint64(int(key[0])), np.uint64(int(key[1]))
+    for _ in range(rounds):  # the key schedule is forgotten
+        p0 = np.uint64(0xD2511F53) * c0
+        p1 = np.uint64(0xCD9E8D57) * c2
+        c0, c1, c2, c3 = (p1 >> np.uint64(32)) ^ c1 ^ k0, p1 & m32, (p0 >> np.uint64(32)) ^ c3 ^ k1, p0 & m32
+    return np.stack([c0, c1, c2, c3], axis=-1).astype(np.uint32)
+
+
+def _bwd_mask_only_in_dv(q, k, v, dout, scale, causal=False, window=0, drop=None):
+    dq, dk, dv = _ORIG_BWD(q, k, v, dout, scale, causal, window, drop=None)  # dP, D without the mask
+    if drop is not None:
+        p = oa.attention_probs(q, k, scale, causal, window)
+        dv = (p * drop[0] * drop[1]).T @ np.asarray(dout, dtype=np.float64)
+    return dq, dk, dv
+
+
 _ORIG_MERGE = oa.merge_partials
 _ORIG_KVCACHE = oa.kvcache_fwd
 
@@ -107,6 +127,8 @@ MUTATIONS = [
     ("merge_partials", _merge_unnormalised, lambda: pins.test_merge_closed_forms()),
     ("merge_partials", _merge_lse_without_max,
      lambda: pins.test_merge_of_key_chunks_equals_full_attention(False, 0, [0, 7, 19, 40])),
+    ("philox4x32", _philox_no_key_bump, lambda: pins.test_philox_known_answers()),
+    ("attention_bwd", _bwd_mask_only_in_dv, lambda: pins.test_dropout_backward_finite_differences(True, 0)),
     ("paged_gather", _paged_gather_swaps_index, lambda: pins.test_paged_kvcache_equals_contiguous(4)),
     ("kvcache_fwd", _kvcache_forgets_new_keys,
      lambda: pins.test_kvcache_decode_equals_rows_of_the_full_sequence(1, True, 0)),

@@ -504,3 +504,108 @@ def test_paged_kvcache_equals_contiguous(page):
             np.testing.assert_array_equal(kb2[table[b, j // page], j % page], kn[b, i])
     unused = sorted(set(range(b_ * mb + 5)) - set(table.ravel().tolist()))
     assert np.isnan(kb2[unused]).all()
+
+
+# --------------------------------------------------------------------------
+# dropout: the counter-based generator and the dropped attention
+# --------------------------------------------------------------------------
+PHILOX_KAT = os.path.join(os.path.dirname(__file__), "golden", "philox4x32_kat.json")
+
+
+def test_philox_known_answers():
+    with open(PHILOX_KAT, encoding="utf-8") as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        ctr = np.array([int(x, 16) for x in c["counter"]], dtype=np.uint64)
+        key = [int(x, 16) for x in c["key"]]
+        out = oracle.philox4x32(ctr, key)
+        assert [int(x) for x in out] == [int(x, 16) for x in c["out"]]
+
+
+def test_dropout_bytes_map_and_uniformity():
+    """Each byte is the stated byte of the stated Philox word (checked element
+    by element on a small block), and over 2^18 bytes every value is about
+    equally frequent (chi-square, 255 degrees of freedom)."""
+    seed, off, slot = 0x0123456789ABCDEF, 5, 9
+    b = oracle.dropout_bytes(slot, [0, 1, 7, 40], 70, seed, off)
+    for a, i in enumerate([0, 1, 7, 40]):
+        for j in range(70):
+            ctr = np.array([2 * (j // 32) + (j // 4) % 2, i, slot, off], dtype=np.uint64)
+            w = oracle.philox4x32(ctr, (seed & 0xFFFFFFFF, seed >> 32))[(j % 32) // 8]
+            assert b[a, j] == (int(w) >> (8 * (j % 4))) & 0xFF
+    big = oracle.dropout_bytes(3, range(512), 512, 42, 0).ravel()
+    counts = np.bincount(big, minlength=256)
+    expect = big.size / 256
+    chi2 = ((counts - expect) ** 2 / expect).sum()
+    assert chi2 < 255 + 6 * math.sqrt(2 * 255)
+
+
+@pytest.mark.parametrize("p", [0.1, 0.5, 0.9])
+def test_dropout_keep_rate_and_scale(p):
+    keep, s = oracle.dropout_keep(2, range(256), 1024, 7, 3, p)
+    kthr = round(256 * (1 - p))
+    assert s == 256 / kthr
+    sigma = math.sqrt(kthr / 256 * (1 - kthr / 256) / keep.size)
+    assert abs(keep.mean() - kthr / 256) < 5 * sigma
+    # other seeds, offsets and slots give other masks
+    assert (oracle.dropout_keep(2, range(256), 1024, 8, 3, p)[0] != keep).mean() > 0.05
+    assert (oracle.dropout_keep(2, range(256), 1024, 7, 4, p)[0] != keep).mean() > 0.05
+    assert (oracle.dropout_keep(3, range(256), 1024, 7, 3, p)[0] != keep).mean() > 0.05
+
+
+def test_dropout_p_zero_keeps_everything():
+    rng = np.random.default_rng(1)
+    q, k, v = (rng.standard_normal((20, 8)) for _ in range(3))
+    drop = oracle.dropout_keep(0, range(20), 20, 99, 0, 0.0)
+    assert drop[0].all() and drop[1] == 1.0
+    o1, l1 = oracle.attention_fwd(q, k, v, 0.3, True, 0, drop=drop)
+    o2, l2 = oracle.attention_fwd(q, k, v, 0.3, True, 0)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_dropout_is_unbiased():
+    """The mean of O over many seeds approaches the undropped O (the scale
+    256/K makes the expectation exact); LSE does not depend on the mask."""
+    rng = np.random.default_rng(2)
+    q, k, v = (rng.standard_normal((12, 8)) for _ in range(3))
+    o_ref, l_ref = oracle.attention_fwd(q, k, v, 0.5, True, 0)
+    n = 600
+    acc = np.zeros_like(o_ref)
+    for seed in range(n):
+        o, lse = oracle.attention_fwd(q, k, v, 0.5, True, 0, drop=oracle.dropout_keep(0, range(12), 12, seed, 0, 0.3))
+        np.testing.assert_array_equal(lse, l_ref)
+        acc += o
+    # per element the mask variance is p/(1-p) of P^2 V^2 summed over keys; 6 sigma
+    p_eff = 1 - round(256 * 0.7) / 256
+    probs = oracle.attention_probs(q, k, 0.5, True, 0)
+    sd = np.sqrt(p_eff / (1 - p_eff) * (probs ** 2) @ (v ** 2) / n)
+    assert (np.abs(acc / n - o_ref) <= 6 * sd + 1e-12).all()
+
+
+@pytest.mark.parametrize("causal,window", [(True, 0), (False, 0), (True, 5)])
+def test_dropout_backward_finite_differences(causal, window):
+    """With the mask fixed, O is a smooth function of q, k, v: the oracle's
+    gradients match central differences of L = sum(dO * O)."""
+    rng = np.random.default_rng(3)
+    n, d = 9, 4
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    drop = oracle.dropout_keep(1, range(n), n, 1234, 0, 0.4)
+    assert not drop[0].all() and drop[0].any()
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, 0.7, causal, window, drop=drop)
+
+    def loss(qq, kk, vv):
+        return (do * oracle.attention_fwd(qq, kk, vv, 0.7, causal, window, drop=drop)[0]).sum()
+
+    eps = 1e-6
+    for g, x, which in ((dq, q, 0), (dk, k, 1), (dv, v, 2)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[which], args_m[which] = xp, xm
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        np.testing.assert_allclose(g, num, atol=1e-7)

@@ -195,6 +195,18 @@ def extra_rows(torch, fa, steps):
         rows["bwd_causal_n8192"] = {"ms": round(med(ms), 4), "tflops": round(f / med(ms) / 1e9, 1)}
     except Exception as e:  # not available in this build
         rows["bwd_causal_n8192"] = {"error": str(e)[:120]}
+    # dropout (p = 0.1) forward and backward at the same shape
+    try:
+        t = {k_: v_.cuda() for k_, v_ in workload_inputs("bwd_n8192").items() if hasattr(v_, "cuda")}
+        kw = dict(causal=True, dropout_p=0.1, seed=1234, offset=0)
+        _, ms = time_calls(lambda: fa.fa_fwd(t["q"], t["k"], t["v"], **kw), 2, steps, torch)
+        f = fwd_flops(1, 32, 8192, 128, True)
+        rows["fwd_causal_dropout0.1_n8192"] = {"ms": round(med(ms), 4), "tflops": round(f / med(ms) / 1e9, 1)}
+        o, lse = fa.fa_fwd(t["q"], t["k"], t["v"], **kw)
+        _, ms = time_calls(lambda: fa.fa_bwd(t["dout"], t["q"], t["k"], t["v"], o, lse, **kw), 2, steps, torch)
+        rows["bwd_causal_dropout0.1_n8192"] = {"ms": round(med(ms), 4), "tflops": round(2.5 * f / med(ms) / 1e9, 1)}
+    except Exception as e:
+        rows["fwd_causal_dropout0.1_n8192"] = {"error": str(e)[:120]}
     # varlen
     try:
         w = WORKLOADS["varlen_32k"]

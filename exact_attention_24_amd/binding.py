@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 FA_F32, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_DTYPE_MISMATCH, FA_ERR_UNSUPPORTED, FA_ERR_HIP = range(5)
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 _I64x4 = ctypes.c_int64 * 4
 _I64x3 = ctypes.c_int64 * 3
@@ -39,6 +39,7 @@ class FwdParams(ctypes.Structure):
         ("q_stride", _I64x3), ("k_stride", _I64x3), ("v_stride", _I64x3), ("o_stride", _I64x3),
         ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
         ("q_descale", ctypes.c_float), ("k_descale", ctypes.c_float), ("v_descale", ctypes.c_float),
+        ("dropout_p", ctypes.c_float), ("dropout_offset", ctypes.c_uint32), ("dropout_seed", ctypes.c_uint64),
     ]
 
 
@@ -52,6 +53,7 @@ class VarlenFwdParams(ctypes.Structure):
         ("q_stride", _I64x2), ("k_stride", _I64x2), ("v_stride", _I64x2), ("o_stride", _I64x2),
         ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
         ("q_descale", ctypes.c_float), ("k_descale", ctypes.c_float), ("v_descale", ctypes.c_float),
+        ("dropout_p", ctypes.c_float), ("dropout_offset", ctypes.c_uint32), ("dropout_seed", ctypes.c_uint64),
     ]
 
 
@@ -67,6 +69,7 @@ class BwdParams(ctypes.Structure):
         ("do_stride", _I64x3), ("dq_stride", _I64x3), ("dk_stride", _I64x3), ("dv_stride", _I64x3),
         ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
         ("deterministic", ctypes.c_int32),
+        ("dropout_p", ctypes.c_float), ("dropout_offset", ctypes.c_uint32), ("dropout_seed", ctypes.c_uint64),
     ]
 
 
@@ -83,6 +86,7 @@ class VarlenBwdParams(ctypes.Structure):
         ("do_stride", _I64x2), ("dq_stride", _I64x2), ("dk_stride", _I64x2), ("dv_stride", _I64x2),
         ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
         ("deterministic", ctypes.c_int32),
+        ("dropout_p", ctypes.c_float), ("dropout_offset", ctypes.c_uint32), ("dropout_seed", ctypes.c_uint64),
     ]
 
 
@@ -196,6 +200,17 @@ def _check_last_dim(name, t):
         raise ValueError(f"{name} must be contiguous in its last (head_dim) dimension")
 
 
+def _set_dropout(p, dropout_p, seed, offset):
+    """Dropout fields of a params struct; a nonzero p needs an explicit seed,
+    since the backward must regenerate the forward's mask from it."""
+    dropout_p = float(dropout_p)
+    if dropout_p > 0.0 and seed is None:
+        raise ValueError("dropout_p > 0 needs a seed (pass the same seed and offset to the backward)")
+    p.dropout_p = dropout_p
+    p.dropout_seed = int(seed or 0) & 0xFFFFFFFFFFFFFFFF
+    p.dropout_offset = int(offset) & 0xFFFFFFFF
+
+
 def _default_scale(d, softmax_scale):
     return 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
 
@@ -203,7 +218,8 @@ def _default_scale(d, softmax_scale):
 # ---------------------------------------------------------------------------
 # forward
 # ---------------------------------------------------------------------------
-def make_fwd_params(q, k, v, o, lse, causal=False, window=0, softmax_scale=None, descale=(1.0, 1.0, 1.0)):
+def make_fwd_params(q, k, v, o, lse, causal=False, window=0, softmax_scale=None, descale=(1.0, 1.0, 1.0),
+                    dropout_p=0.0, seed=None, offset=0):
     for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
         if t.dim() != 4:
             raise ValueError(f"{n} must be [batch, seqlen, heads, head_dim] (got {tuple(t.shape)})")
@@ -227,6 +243,7 @@ def make_fwd_params(q, k, v, o, lse, causal=False, window=0, softmax_scale=None,
     p.softmax_scale = _default_scale(d, softmax_scale)
     p.causal, p.window = int(bool(causal)), int(window)
     p.q_descale, p.k_descale, p.v_descale = (float(x) for x in descale)
+    _set_dropout(p, dropout_p, seed, offset)
     return p
 
 
@@ -235,11 +252,13 @@ def fa_check_fwd(params: FwdParams) -> int:
 
 
 def fa_fwd(q, k, v, causal=False, window=0, softmax_scale=None, out=None, lse=None,
-           return_lse=True, descale=(1.0, 1.0, 1.0)):
+           return_lse=True, descale=(1.0, 1.0, 1.0), dropout_p=0.0, seed=None, offset=0):
     """O (and LSE) of exact attention; q [B,Nq,H,d], k/v [B,Nk,H,d] on the GPU.
 
     bf16 in -> bf16 out, fp32 -> fp32, float8_e4m3fn (with per-tensor
     ``descale`` = (q, k, v)) -> bf16.  ``softmax_scale`` None means 1/sqrt(d).
+    ``dropout_p`` > 0 (bf16): dropout of the probabilities from the Philox
+    stream of (``seed``, ``offset``); pass the same to ``fa_bwd``.
     """
     odt = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
     b, nq, h, d = q.shape
@@ -247,13 +266,13 @@ def fa_fwd(q, k, v, causal=False, window=0, softmax_scale=None, out=None, lse=No
         out = torch.empty((b, nq, h, d), dtype=odt, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((b, h, nq), dtype=torch.float32, device=q.device)
-    p = make_fwd_params(q, k, v, out, lse, causal, window, softmax_scale, descale)
+    p = make_fwd_params(q, k, v, out, lse, causal, window, softmax_scale, descale, dropout_p, seed, offset)
     _raise(lib().fa_fwd(ctypes.byref(p), _stream()))
     return (out, lse) if return_lse else out
 
 
 def make_varlen_params(q, k, v, o, lse, cu_seqlens, max_seqlen, causal=False, window=0, softmax_scale=None,
-                       descale=(1.0, 1.0, 1.0)):
+                       descale=(1.0, 1.0, 1.0), dropout_p=0.0, seed=None, offset=0):
     for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
         if t.dim() != 3:
             raise ValueError(f"{n} must be [total_tokens, heads, head_dim] (got {tuple(t.shape)})")
@@ -279,6 +298,7 @@ def make_varlen_params(q, k, v, o, lse, cu_seqlens, max_seqlen, causal=False, wi
     p.softmax_scale = _default_scale(d, softmax_scale)
     p.causal, p.window = int(bool(causal)), int(window)
     p.q_descale, p.k_descale, p.v_descale = (float(x) for x in descale)
+    _set_dropout(p, dropout_p, seed, offset)
     return p
 
 
@@ -287,7 +307,7 @@ def fa_check_varlen_fwd(params: VarlenFwdParams) -> int:
 
 
 def fa_varlen_fwd(q, k, v, cu_seqlens, max_seqlen, causal=False, window=0, softmax_scale=None, out=None,
-                  lse=None, return_lse=True, descale=(1.0, 1.0, 1.0)):
+                  lse=None, return_lse=True, descale=(1.0, 1.0, 1.0), dropout_p=0.0, seed=None, offset=0):
     """Packed variable-length forward: q/k/v [total, H, d], int32 cu_seqlens [nseq+1]."""
     odt = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
     total, h, d = q.shape
@@ -295,7 +315,8 @@ def fa_varlen_fwd(q, k, v, cu_seqlens, max_seqlen, causal=False, window=0, softm
         out = torch.empty((total, h, d), dtype=odt, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((h, total), dtype=torch.float32, device=q.device)
-    p = make_varlen_params(q, k, v, out, lse, cu_seqlens, max_seqlen, causal, window, softmax_scale, descale)
+    p = make_varlen_params(q, k, v, out, lse, cu_seqlens, max_seqlen, causal, window, softmax_scale, descale,
+                           dropout_p, seed, offset)
     _raise(lib().fa_varlen_fwd(ctypes.byref(p), _stream()))
     return (out, lse) if return_lse else out
 
@@ -304,7 +325,7 @@ def fa_varlen_fwd(q, k, v, cu_seqlens, max_seqlen, causal=False, window=0, softm
 # backward
 # ---------------------------------------------------------------------------
 def make_bwd_params(dout, q, k, v, o, lse, dq, dk, dv, causal=False, window=0, softmax_scale=None,
-                    deterministic=False):
+                    deterministic=False, dropout_p=0.0, seed=None, offset=0):
     for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
         if t.dim() != 4:
             raise ValueError(f"{n} must be [batch, seqlen, heads, head_dim] (got {tuple(t.shape)})")
@@ -327,6 +348,7 @@ def make_bwd_params(dout, q, k, v, o, lse, dq, dk, dv, causal=False, window=0, s
         setattr(p, f"{name}_stride", _I64x3(*t.stride()[:3]))
     p.softmax_scale = _default_scale(d, softmax_scale)
     p.causal, p.window, p.deterministic = int(bool(causal)), int(window), int(bool(deterministic))
+    _set_dropout(p, dropout_p, seed, offset)
     return p
 
 
@@ -339,7 +361,7 @@ def fa_bwd_workspace_bytes(params: BwdParams) -> int:
 
 
 def fa_bwd(dout, q, k, v, o, lse, causal=False, window=0, softmax_scale=None, deterministic=False,
-           grad_dtype=torch.float32, dq=None, dk=None, dv=None):
+           grad_dtype=torch.float32, dq=None, dk=None, dv=None, dropout_p=0.0, seed=None, offset=0):
     """dq, dk, dv of exact attention, recomputing P from the forward's LSE."""
     if dq is None:
         dq = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
@@ -347,7 +369,8 @@ def fa_bwd(dout, q, k, v, o, lse, causal=False, window=0, softmax_scale=None, de
         dk = torch.empty(k.shape, dtype=grad_dtype, device=q.device)
     if dv is None:
         dv = torch.empty(v.shape, dtype=grad_dtype, device=q.device)
-    p = make_bwd_params(dout, q, k, v, o, lse, dq, dk, dv, causal, window, softmax_scale, deterministic)
+    p = make_bwd_params(dout, q, k, v, o, lse, dq, dk, dv, causal, window, softmax_scale, deterministic,
+                        dropout_p, seed, offset)
     _raise(lib().fa_check_bwd(ctypes.byref(p)))
     nbytes = fa_bwd_workspace_bytes(p)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
@@ -356,7 +379,7 @@ def fa_bwd(dout, q, k, v, o, lse, causal=False, window=0, softmax_scale=None, de
 
 
 def make_varlen_bwd_params(dout, q, k, v, o, lse, dq, dk, dv, cu_seqlens, max_seqlen, causal=False, window=0,
-                           softmax_scale=None, deterministic=False):
+                           softmax_scale=None, deterministic=False, dropout_p=0.0, seed=None, offset=0):
     for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
         if t.dim() != 3:
             raise ValueError(f"{n} must be [total_tokens, heads, head_dim] (got {tuple(t.shape)})")
@@ -384,6 +407,7 @@ def make_varlen_bwd_params(dout, q, k, v, o, lse, dq, dk, dv, cu_seqlens, max_se
         setattr(p, f"{name}_stride", _I64x2(*t.stride()[:2]))
     p.softmax_scale = _default_scale(d, softmax_scale)
     p.causal, p.window, p.deterministic = int(bool(causal)), int(window), int(bool(deterministic))
+    _set_dropout(p, dropout_p, seed, offset)
     return p
 
 
@@ -396,7 +420,8 @@ def fa_varlen_bwd_workspace_bytes(params: VarlenBwdParams) -> int:
 
 
 def fa_varlen_bwd(dout, q, k, v, o, lse, cu_seqlens, max_seqlen, causal=False, window=0, softmax_scale=None,
-                  deterministic=False, grad_dtype=torch.float32, dq=None, dk=None, dv=None):
+                  deterministic=False, grad_dtype=torch.float32, dq=None, dk=None, dv=None, dropout_p=0.0, seed=None,
+                  offset=0):
     """dq, dk, dv of the packed variable-length forward (q/k/v [total, H, d], lse [H, total])."""
     if dq is None:
         dq = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
@@ -405,7 +430,7 @@ def fa_varlen_bwd(dout, q, k, v, o, lse, cu_seqlens, max_seqlen, causal=False, w
     if dv is None:
         dv = torch.empty(v.shape, dtype=grad_dtype, device=q.device)
     p = make_varlen_bwd_params(dout, q, k, v, o, lse, dq, dk, dv, cu_seqlens, max_seqlen, causal, window,
-                               softmax_scale, deterministic)
+                               softmax_scale, deterministic, dropout_p, seed, offset)
     _raise(lib().fa_check_varlen_bwd(ctypes.byref(p)))
     nbytes = fa_varlen_bwd_workspace_bytes(p)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)

@@ -136,6 +136,25 @@ fa_status launched(hipError_t e) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Dropout: validate p for the dtype and fill the kernel-side fields.
+fa_status check_dropout(float p, fa_dtype qkv) {
+  if (!(std::isfinite(p) && p >= 0.f && p < 1.f))
+    return fail(FA_ERR_INVALID_ARGUMENT, "dropout_p must be in [0, 1) (got %g)", (double)p);
+  if (p > 0.f && qkv != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "dropout is available for bf16 inputs only (got qkv_dtype=%d)", (int)qkv);
+  return FA_OK;
+}
+
+template <class Args>
+void set_dropout(Args &a, float p, uint64_t seed, uint32_t offset) {
+  const long kthr = std::max(1L, std::lround(256.0 * (1.0 - (double)p)));
+  a.drop_k = kthr >= 256 ? 0u : (uint32_t)kthr;  // p < 1/512: nothing is dropped
+  a.drop_scale = a.drop_k ? 256.f / (float)a.drop_k : 1.f;
+  a.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
+  a.seed_hi = (uint32_t)(seed >> 32);
+  a.drop_offset = offset;
+}
+
 // Checks shared by the dense and packed backward.
 fa_status check_bwd_common(fa_dtype qkv, fa_dtype grad, int heads, int head_dim, float scale, int causal,
                            int window, int deterministic) {
@@ -189,6 +208,7 @@ fa_status fa_check_fwd(const fa_fwd_params *p) {
   fa_status st = check_fwd_common(p->qkv_dtype, p->o_dtype, p->heads, p->head_dim, p->softmax_scale,
                                   p->causal, p->window, p->q_descale, p->k_descale, p->v_descale);
   if (st != FA_OK) return st;
+  if ((st = check_dropout(p->dropout_p, p->qkv_dtype)) != FA_OK) return st;
   if (p->batch < 0 || p->seqlen_q < 0 || p->seqlen_k < 0)
     return fail(FA_ERR_INVALID_ARGUMENT, "sizes must be >= 0 (batch=%d seqlen_q=%d seqlen_k=%d)", p->batch,
                 p->seqlen_q, p->seqlen_k);
@@ -211,6 +231,7 @@ fa_status fa_check_varlen_fwd(const fa_varlen_fwd_params *p) {
   fa_status st = check_fwd_common(p->qkv_dtype, p->o_dtype, p->heads, p->head_dim, p->softmax_scale,
                                   p->causal, p->window, p->q_descale, p->k_descale, p->v_descale);
   if (st != FA_OK) return st;
+  if ((st = check_dropout(p->dropout_p, p->qkv_dtype)) != FA_OK) return st;
   if (p->num_seqs < 0 || p->total_tokens < 0 || p->max_seqlen < 0)
     return fail(FA_ERR_INVALID_ARGUMENT, "sizes must be >= 0 (num_seqs=%d total_tokens=%d max_seqlen=%d)",
                 p->num_seqs, p->total_tokens, p->max_seqlen);
@@ -236,6 +257,7 @@ fa_status fa_check_bwd(const fa_bwd_params *p) {
   fa_status st0 = check_bwd_common(p->qkv_dtype, p->grad_dtype, p->heads, p->head_dim, p->softmax_scale,
                                    p->causal, p->window, p->deterministic);
   if (st0 != FA_OK) return st0;
+  if ((st0 = check_dropout(p->dropout_p, p->qkv_dtype)) != FA_OK) return st0;
   if (p->batch < 0 || p->seqlen_q < 0 || p->seqlen_k < 0)
     return fail(FA_ERR_INVALID_ARGUMENT, "sizes must be >= 0 (batch=%d seqlen_q=%d seqlen_k=%d heads=%d)",
                 p->batch, p->seqlen_q, p->seqlen_k, p->heads);
@@ -263,6 +285,7 @@ fa_status fa_check_varlen_bwd(const fa_varlen_bwd_params *p) {
   fa_status st = check_bwd_common(p->qkv_dtype, p->grad_dtype, p->heads, p->head_dim, p->softmax_scale,
                                   p->causal, p->window, p->deterministic);
   if (st != FA_OK) return st;
+  if ((st = check_dropout(p->dropout_p, p->qkv_dtype)) != FA_OK) return st;
   if (p->num_seqs < 0 || p->total_tokens < 0 || p->max_seqlen < 0)
     return fail(FA_ERR_INVALID_ARGUMENT, "sizes must be >= 0 (num_seqs=%d total_tokens=%d max_seqlen=%d)",
                 p->num_seqs, p->total_tokens, p->max_seqlen);
@@ -304,6 +327,7 @@ fa_status fa_fwd(const fa_fwd_params *p, void *stream) {
   a.causal = p->causal; a.window = p->window;
   a.scale_log2 = p->softmax_scale * kLog2e * p->q_descale * p->k_descale;
   a.v_descale = p->v_descale;
+  set_dropout(a, p->dropout_p, p->dropout_seed, p->dropout_offset);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   switch (p->qkv_dtype) {
     case FA_F32: return launched(fa::launch_fwd_f32(a, p->head_dim, s));
@@ -329,6 +353,7 @@ fa_status fa_varlen_fwd(const fa_varlen_fwd_params *p, void *stream) {
   a.causal = p->causal; a.window = p->window;
   a.scale_log2 = p->softmax_scale * kLog2e * p->q_descale * p->k_descale;
   a.v_descale = p->v_descale;
+  set_dropout(a, p->dropout_p, p->dropout_seed, p->dropout_offset);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   switch (p->qkv_dtype) {
     case FA_F32: return launched(fa::launch_fwd_f32(a, p->head_dim, s));
@@ -373,6 +398,7 @@ fa_status fa_bwd(const fa_bwd_params *p, void *workspace, size_t workspace_bytes
   a.grad_f32 = p->grad_dtype == FA_F32;
   a.scale = p->softmax_scale;
   a.scale_log2 = p->softmax_scale * kLog2e;
+  set_dropout(a, p->dropout_p, p->dropout_seed, p->dropout_offset);
   return launched(fa::launch_bwd_bf16(a, p->head_dim, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -411,6 +437,7 @@ fa_status fa_varlen_bwd(const fa_varlen_bwd_params *p, void *workspace, size_t w
   a.grad_f32 = p->grad_dtype == FA_F32;
   a.scale = p->softmax_scale;
   a.scale_log2 = p->softmax_scale * kLog2e;
+  set_dropout(a, p->dropout_p, p->dropout_seed, p->dropout_offset);
   return launched(fa::launch_bwd_bf16(a, p->head_dim, reinterpret_cast<hipStream_t>(stream)));
 }
 

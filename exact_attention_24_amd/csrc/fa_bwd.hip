@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void bwd_dsum_kernel(BwdArgs a, int64_t total)
 //    Q, dO, lse2 and D tiles arrive by LDS DMA one tile ahead into three
 //    buffers; Q and dO are unpadded with XOR-swizzled 16-byte chunks.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool DROP>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NW = 4, T = NW * 64, BC = 32 * NW, BR = 64;
   constexpr int DCH = D / 8, TS = BR * D;  // Q or dO tile (bf16 elements)
@@ -139,6 +139,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BUF = 2 * TS * 2 + 2 * 1024;  // bytes per buffer: Q, dO, lse2 (1 KB slot), D (1 KB slot)
   constexpr int RING = 8;                  // operand fragments in flight
   __shared__ __attribute__((aligned(16))) unsigned char smem[3 * BUF];
+  // dropout: per wave, the keep bits of the tile's 64 query rows against the
+  // wave's 32 keys (one word per row, bit = key)
+  __shared__ __attribute__((aligned(16))) uint32_t drop_rec[DROP ? NW * 64 : 4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -258,12 +261,50 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     return (uint4){lo.x, lo.y, hi.x, hi.y};
   };
 
+  // Dropout keep flags of this lane's 32 elements (bit e), for tile row q0.
+  // The random bytes come in query-row order (one Philox call covers 16 keys
+  // of one row), the lane needs them in key order: each lane makes the two
+  // calls of row q0 + lane, packs the 32 flags into one word in LDS, and
+  // reads back the words of the 32 rows it holds.
+  const uint32_t dslot = (uint32_t)(b * a.heads + h);
+  auto drop_mask = [&](int q0) __attribute__((always_inline)) -> uint32_t {
+    const uint32_t kblk = (uint32_t)(k0 >> 5) + (uint32_t)wave, qi = (uint32_t)(q0 + lane);
+    const Philox x0 = philox10(2u * kblk, qi, dslot, a.drop_offset, a.seed_lo, a.seed_hi);
+    const Philox x1 = philox10(2u * kblk + 1u, qi, dslot, a.drop_offset, a.seed_lo, a.seed_hi);
+    uint32_t rec = 0;
+#pragma unroll
+    for (int jj = 0; jj < 32; ++jj) {  // key jj of the block: call (jj >> 2) & 1, element 4 (jj >> 3) + jj % 4
+      const uint32_t w = ((jj >> 2) & 1) ? x1.c[jj >> 3] : x0.c[jj >> 3];
+      rec |= (((w >> (8 * (jj & 3))) & 0xFFu) < a.drop_k ? 1u : 0u) << jj;
+    }
+    drop_rec[wave * 64 + lane] = rec;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's words are in LDS
+    uint32_t em = 0;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {  // rows 32 (g / 4) + 8 (g % 4) + 4 hf + 0..3
+      const uint4 rr = *(const uint4 *)(drop_rec + wave * 64 + 32 * (g >> 2) + 8 * (g & 3) + 4 * hf);
+      const int e0 = 16 * (g >> 2) + 4 * (g & 3);
+      em |= ((rr.x >> ql) & 1u) << e0;
+      em |= ((rr.y >> ql) & 1u) << (e0 + 1);
+      em |= ((rr.z >> ql) & 1u) << (e0 + 2);
+      em |= ((rr.w >> ql) & 1u) << (e0 + 3);
+    }
+    return em;
+  };
+
   // P, dS of one tile (MASK: causal / window edge); element e = 16 qb + r is
   // query 32 qb + 8 (r / 4) + 4 hf + r % 4 of the tile
   auto one_tile = [&](auto mask_tag, int it) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int q0 = it * BR;
     if (it + 1 < it1) load_tile(it + 1);
+    uint32_t emask = 0;
+    if constexpr (DROP) emask = drop_mask(q0);
+    // keep ? scale : 0 for element e (1 without dropout)
+    auto kf = [&](int e) __attribute__((always_inline)) -> float {
+      if constexpr (DROP) return ((emask >> e) & 1u) ? a.drop_scale : 0.f;
+      else return 1.f;
+    };
     // phase-A fragments come from this tile, phase-B fragments from the
     // previous one (its products are pending; before the first tile they
     // are zero and any resident tile will do)
@@ -320,7 +361,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     };
     auto elem_exp = [&](int e) __attribute__((always_inline)) { s[e / 16][e % 16] = fast_exp2(s[e / 16][e % 16]); };
     auto elem_ds = [&](int e) __attribute__((always_inline)) {
-      dp[e / 16][e % 16] = s[e / 16][e % 16] * (dp[e / 16][e % 16] - comp(d4[e / 4], e % 4));
+      if constexpr (DROP)
+        dp[e / 16][e % 16] =
+            s[e / 16][e % 16] * __builtin_fmaf(dp[e / 16][e % 16], kf(e), -comp(d4[e / 4], e % 4));
+      else
+        dp[e / 16][e % 16] = s[e / 16][e % 16] * (dp[e / 16][e % 16] - comp(d4[e / 4], e % 4));
     };
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -356,6 +401,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     for (int cc = 0; cc < 4; ++cc) {
       const int qb = cc >> 1, r0 = (cc & 1) * 8;
       uint4 &p = pb[cc], &d = sb[cc];
+      if constexpr (DROP) {  // dV takes the dropped, rescaled P
+#pragma unroll
+        for (int r = r0; r < r0 + 8; ++r) s[qb][r] *= kf(16 * qb + r);
+      }
       p.x = pack_bf16x2(s[qb][r0 + 0], s[qb][r0 + 1]);
       p.y = pack_bf16x2(s[qb][r0 + 2], s[qb][r0 + 3]);
       p.z = pack_bf16x2(s[qb][r0 + 4], s[qb][r0 + 5]);
@@ -452,7 +501,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 //               the row-major K tile, in the key order of the dS^T operand).
 //    dQ is written once, no atomics.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool DROP>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   constexpr int NW = 4, T = NW * 64, QW = 64, BR = NW * QW, BC = 64;
   constexpr int DCH = D / 8, TS = BC * D;
@@ -569,6 +618,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) dp[qb] = (f32x16){};
 
+  // dropout: the keep bytes of a sub-tile's 32 keys for the lane's two query
+  // rows, one Philox call each; its 10 rounds are spread over the 2 NK
+  // stages of the S and dP MFMAs, round r at stage r * 2 NK / 10
+  const uint32_t dslot = (uint32_t)(b * a.heads + h);
+  Philox rx[2];
+  auto drop_rounds = [&](int stage) __attribute__((always_inline)) {
+    if constexpr (DROP) {
+#pragma unroll
+      for (int r = 0; r < 10; ++r)
+        if (r * 2 * NK / 10 == stage) {
+          philox_round(rx[0], philox_k0(a.seed_lo, r), philox_k1(a.seed_hi, r));
+          philox_round(rx[1], philox_k0(a.seed_lo, r), philox_k1(a.seed_hi, r));
+        }
+    }
+  };
+  // dS = P (dP keep scale - D) for DROP (kf = keep ? scale : 0), else P (dP - D)
+  auto kfac = [&](int qb, int r) __attribute__((always_inline)) -> float {
+    if constexpr (DROP) return drop_keep(rx[qb], r, a.drop_k) ? a.drop_scale : 0.f;
+    else return 1.f;
+  };
+
   const int kx = hf ^ swz<D>(ql);
   // phase-A fragment kk of sub-tile (jt, kb): K rows (S) or V rows (dP)
   auto kread = [&](int jt, int kb, int kk) __attribute__((always_inline)) -> uint4 {
@@ -599,6 +669,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int k0 = jt * BC + kb * 32;
     const bool act = !MASK || active(k0);
+    if constexpr (DROP) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        rx[qb].c[0] = 2u * (uint32_t)(k0 >> 5) + (uint32_t)hf;
+        rx[qb].c[1] = (uint32_t)(wq0 + 32 * qb + ql);
+        rx[qb].c[2] = dslot;
+        rx[qb].c[3] = a.drop_offset;
+      }
+    }
     // ---- S MFMAs; meanwhile dS of the pending sub-tile is packed to bf16
     if (act) {
       uint4 ring[RING];
@@ -617,12 +696,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
         }
         constexpr int PK = NK / 4;
         if (kk % PK == PK - 1) pack_ds((kk / PK) / 2, (kk / PK) % 2);
+        drop_rounds(kk);
         __builtin_amdgcn_sched_barrier(0);
       }
       mfma_drain2_v(s[0], s[1]);
     } else {
 #pragma unroll
       for (int part = 0; part < 4; ++part) pack_ds(part / 2, part % 2);
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) drop_rounds(kk);
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[0][e] = s[1][e] = -INFINITY;
     }
@@ -665,6 +747,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
           const int e = kk * EPS + k, qb = e / 16, r = e % 16;
           s[qb][r] = fast_exp2(__builtin_fmaf(s[qb][r], c, -lse2[qb]));
         }
+        drop_rounds(NK + kk);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (act) mfma_drain2_v(dp[0], dp[1]);
@@ -684,7 +767,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int k = 0; k < EPS; ++k) {
           const int e = f * EPS + k, qb = e / 16, r = e % 16;
-          if (act) dp[qb][r] = s[qb][r] * (dp[qb][r] - dsum[qb]);
+          if (act) dp[qb][r] = s[qb][r] * (DROP ? __builtin_fmaf(dp[qb][r], kfac(qb, r), -dsum[qb]) : dp[qb][r] - dsum[qb]);
           else dp[qb][r] = 0.f;
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -797,6 +880,7 @@ __global__ __launch_bounds__(256) void bwd_start_kernel(BwdArgs a) {
   if (r_lo >= r_hi || kn <= 0) return;  // uniform: no start rows here
   const int window = a.window;
   const float scale = a.scale;
+  const uint32_t dslot = (uint32_t)(b * a.heads + h);
 
   const uint16_t *qg = (const uint16_t *)a.q + b * a.q_sb + h * a.q_sh;
   const uint16_t *dog = (const uint16_t *)a.dout + b * a.do_sb + h * a.do_sh;
@@ -868,19 +952,40 @@ __global__ __launch_bounds__(256) void bwd_start_kernel(BwdArgs a) {
     l += __shfl_xor(l, 1);
     l += __shfl_xor(l, 2);
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    float dd = 0.f;
+    // dropout: kf = keep ? scale : 0 per key (keys c < 64: blocks 0, 1)
+    float kfv[T / 4];
+#pragma unroll
+    for (int j = 0; j < T / 4; ++j) kfv[j] = 1.f;
+    if (a.drop_k) {
+      const uint32_t qi = (uint32_t)(r - off);
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const Philox x = philox10(2u * cb + hh, qi, dslot, a.drop_offset, a.seed_lo, a.seed_hi);
+#pragma unroll
+          for (int j = 0; j < T / 4; ++j) {
+            const int c = part + 4 * j;  // (c >> 2) & 1 == j & 1, c >> 5 == j >> 3
+            if ((j >> 3) == cb && (j & 1) == hh) {
+              const uint32_t byte = (x.c[(c & 31) >> 3] >> (8 * (c & 3))) & 0xFFu;
+              kfv[j] = byte < a.drop_k ? a.drop_scale : 0.f;
+            }
+          }
+        }
+    }
+    float dd = 0.f;  // D = sum_j P_j kf_j dP_j
 #pragma unroll
     for (int j = 0; j < T / 4; ++j) {
       sv[j] *= inv;
-      dd = __builtin_fmaf(sv[j], dss[r][part + 4 * j], dd);
+      dd = __builtin_fmaf(sv[j] * kfv[j], dss[r][part + 4 * j], dd);
     }
     dd += __shfl_xor(dd, 1);
     dd += __shfl_xor(dd, 2);
 #pragma unroll
     for (int j = 0; j < T / 4; ++j) {
       const int c = part + 4 * j;
-      dss[r][c] = sv[j] * (dss[r][c] - dd);  // 0 where P = 0
-      ps[r][c] = sv[j];
+      dss[r][c] = sv[j] * __builtin_fmaf(kfv[j], dss[r][c], -dd);  // 0 where P = 0
+      ps[r][c] = sv[j] * kfv[j];
     }
   }
   __syncthreads();
@@ -963,10 +1068,15 @@ hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t s) {
     hipLaunchKernelGGL((bwd_dsum_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, a, rows);
   }
   const int64_t kv_items = (int64_t)((a.nk + 32 * NW_KV - 1) / (32 * NW_KV)) * a.heads * a.batch;
-  if (kv_items > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)kv_items), dim3(NW_KV * 64), 0, s, a);
+  if (kv_items > 0) {
+    if (a.drop_k) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)kv_items), dim3(NW_KV * 64), 0, s, a);
+    else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)kv_items), dim3(NW_KV * 64), 0, s, a);
+  }
   const int64_t q_items = (int64_t)((a.nq + 256 - 1) / 256) * a.heads * a.batch;
-  if (q_items > 0) hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)q_items), dim3(256), 0, s, a);
+  if (q_items > 0) {
+    if (a.drop_k) hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)q_items), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)q_items), dim3(256), 0, s, a);
+  }
   const int64_t start_items = (int64_t)a.batch * a.heads * kStartSplit;
   if (a.causal && start_items > 0 && a.nq > 0 && a.nk > 0)
     hipLaunchKernelGGL((bwd_start_kernel<D>), dim3((unsigned)start_items), dim3(256), 0, s, a);

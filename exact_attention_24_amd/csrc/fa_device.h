@@ -212,5 +212,50 @@ __device__ __forceinline__ void store_transposed_4x8(uint16_t *t, int pitch, int
   }
 }
 
+// ---------------------------------------------------------------------------
+// Dropout randomness: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel
+// random numbers: as easy as 1, 2, 3", SC 2011).  Each round multiplies words
+// 0 and 2 by 0xD2511F53 / 0xCD9E8D57 into 64-bit products and forms
+// (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0); the key is bumped by the Weyl
+// constants 0x9E3779B9 / 0xBB67AE85 between rounds.
+//
+// The attention element (query row i, key j) of head slot b * heads + h
+// draws byte (j & 3) of word ((j & 31) >> 3) of the call with counter
+// (2 (j >> 5) + ((j >> 2) & 1), i, slot, offset): one call covers the 16
+// elements that one lane half holds of a 32-key block in the MFMA
+// accumulator layout (keys 8 (r / 4) + 4 hf + r % 4, r = 0..15), so lane
+// half hf of key block kb makes exactly one call.  The element is kept iff
+// its byte < drop_k.
+// ---------------------------------------------------------------------------
+struct Philox {
+  uint32_t c[4];
+};
+
+__device__ __forceinline__ void philox_round(Philox &x, uint32_t k0, uint32_t k1) {
+  const uint32_t lo0 = 0xD2511F53u * x.c[0], hi0 = __umulhi(0xD2511F53u, x.c[0]);
+  const uint32_t lo1 = 0xCD9E8D57u * x.c[2], hi1 = __umulhi(0xCD9E8D57u, x.c[2]);
+  x.c[0] = hi1 ^ x.c[1] ^ k0;
+  x.c[1] = lo1;
+  x.c[2] = hi0 ^ x.c[3] ^ k1;
+  x.c[3] = lo0;
+}
+
+// Key of round r (0-based).
+__device__ __forceinline__ uint32_t philox_k0(uint32_t seed_lo, int r) { return seed_lo + 0x9E3779B9u * (uint32_t)r; }
+__device__ __forceinline__ uint32_t philox_k1(uint32_t seed_hi, int r) { return seed_hi + 0xBB67AE85u * (uint32_t)r; }
+
+__device__ __forceinline__ Philox philox10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t seed_lo,
+                                           uint32_t seed_hi) {
+  Philox x{{c0, c1, c2, c3}};
+#pragma unroll
+  for (int r = 0; r < 10; ++r) philox_round(x, philox_k0(seed_lo, r), philox_k1(seed_hi, r));
+  return x;
+}
+
+// Keep flag of accumulator element r (0..15) from its call's output.
+__device__ __forceinline__ bool drop_keep(const Philox &x, int r, uint32_t drop_k) {
+  return ((x.c[r >> 2] >> (8 * (r & 3))) & 0xFFu) < drop_k;
+}
+
 }  // namespace dev
 }  // namespace fa

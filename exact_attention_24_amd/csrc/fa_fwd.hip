@@ -118,7 +118,7 @@ constexpr float kLazy = 8.f;
 // and both waves of a SIMD keep feeding the matrix cores from LDS.  K is
 // staged one tile ahead of V (LDS rings of two for each).
 // ---------------------------------------------------------------------------
-template <int D, int NW>
+template <int D, int NW, bool DROP>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int T = NW * 64, BR = NW * 32;
   using St = KvStage<D, T>;
@@ -163,6 +163,19 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int wp_lo = wq0 + off, wp_hi = min(wq0 + 31, nq - 1) + off;
   const int my_q = wq0 + ql;
   const int my_p = my_q + off;
+  const uint32_t slot = (uint32_t)(b * a.heads + h);  // dropout counter word 2
+  // dropout randomness of key block (2 jt + kb) for this lane's query
+  auto drop_init = [&](Philox &x, int jt, int kb) __attribute__((always_inline)) {
+    x.c[0] = 2u * (uint32_t)(2 * jt + kb) + (uint32_t)hf;
+    x.c[1] = (uint32_t)my_q;
+    x.c[2] = slot;
+    x.c[3] = a.drop_offset;
+  };
+  auto drop_apply = [&](const Philox &x, f32x16 &sv, int r0, int r1) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = r0; e < r1; ++e)
+      if (!drop_keep(x, e, a.drop_k)) sv[e] = 0.f;
+  };
   auto active = [&](int jt) __attribute__((always_inline)) {
     const int k0 = jt * BC;
     return wave_rows && (!causal || k0 <= wp_hi) && (window <= 0 || k0 + BC - 1 > wp_lo - window);
@@ -249,6 +262,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
         rs += p;
       }
     l = l * alpha + rs;
+    if constexpr (DROP) {  // the row sum above is of the undropped P~
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        Philox x;
+        drop_init(x, k0 / BC, kb);
+        x = philox10(x.c[0], x.c[1], x.c[2], x.c[3], a.seed_lo, a.seed_hi);
+        drop_apply(x, s[kb], 0, 16);
+      }
+    }
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
       const int kb = cc >> 1, r0 = (cc & 1) * 8;
@@ -288,11 +310,22 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
       va[0] = vread(0);
       va[1] = vread(1);
       float mx = 0.f, m_use = 0.f, rs = 0.f;
+      Philox rx[2];
+      if constexpr (DROP) {
+        drop_init(rx[0], jt, 0);
+        drop_init(rx[1], jt, 1);
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         if (i + 2 < NOP) va[i + 2] = vread(i + 2);
         if (i < NOP) acc[i / 4] = mfma_bf16(va[i], pb_prev[i % 4], acc[i / 4]);
+        if constexpr (DROP) {  // one Philox round of each key block per stage
+          if (i < 10) {
+            philox_round(rx[0], philox_k0(a.seed_lo, i), philox_k1(a.seed_hi, i));
+            philox_round(rx[1], philox_k0(a.seed_lo, i), philox_k1(a.seed_hi, i));
+          }
+        }
         // softmax stage i
         if (i == 0) {
           mx = s[0][0];
@@ -317,6 +350,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
           if (i == 9) l = l * alpha + rs;
         } else if (i < 14) {
           const int cc = i - 10, kb = cc >> 1, r0 = (cc & 1) * 8;
+          if constexpr (DROP) drop_apply(rx[kb], s[kb], r0, r0 + 8);  // after the row sum
           pb[cc].x = pack_bf16x2(s[kb][r0 + 0], s[kb][r0 + 1]);
           pb[cc].y = pack_bf16x2(s[kb][r0 + 2], s[kb][r0 + 3]);
           pb[cc].z = pack_bf16x2(s[kb][r0 + 4], s[kb][r0 + 5]);
@@ -379,7 +413,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
 
   // epilogue: O = acc / l (bf16, round to nearest even), LSE = (m + log2 l) ln 2
   const float lt = half_swap_sum(l);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float inv = lt > 0.f ? (DROP ? a.drop_scale : 1.f) / lt : 0.f;
   if (my_q < nq) {
     uint16_t *orow = (uint16_t *)a.o + b * a.o_sb + (int64_t)(seq0 + my_q) * a.o_st + h * a.o_sh;
 #pragma unroll
@@ -501,10 +535,13 @@ int fwd_block_rows(int qkv_dtype, int head_dim) {
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, int head_dim, hipStream_t s) {
   const dim3 grid((unsigned)(a.nqt * a.heads * a.batch));
-  if (head_dim == 128)
-    hipLaunchKernelGGL((fwd_bf16_kernel<128, 8>), grid, dim3(512), 0, s, a);
-  else
-    hipLaunchKernelGGL((fwd_bf16_kernel<64, 8>), grid, dim3(512), 0, s, a);
+  if (a.drop_k) {
+    if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_kernel<128, 8, true>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<64, 8, true>), grid, dim3(512), 0, s, a);
+  } else {
+    if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_kernel<128, 8, false>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<64, 8, false>), grid, dim3(512), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -25,6 +25,10 @@ struct FwdArgs {
   int32_t causal, window;
   float scale_log2;              // softmax_scale * log2(e) (* q, k descales for fp8)
   float v_descale;               // fp8 only, 1 otherwise
+  // dropout (drop_k == 0: none): element kept iff its random byte < drop_k,
+  // kept probabilities scaled by drop_scale = 256 / drop_k
+  uint32_t drop_k, seed_lo, seed_hi, drop_offset;
+  float drop_scale;
 };
 
 // Kernel-side view of one backward call.  Packed varlen calls set
@@ -43,6 +47,8 @@ struct BwdArgs {
   int32_t batch, heads, nq, nk;
   int32_t causal, window, deterministic, grad_f32;
   float scale, scale_log2;
+  uint32_t drop_k, seed_lo, seed_hi, drop_offset;  // dropout, as in FwdArgs
+  float drop_scale;
 };
 
 // Kernel-side view of one merge of partial results (O_p, LSE_p).

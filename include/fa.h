@@ -41,6 +41,20 @@
  *     at most W keys ending at its own position; W = 0 means unlimited.
  *   - A query row that sees no key gets O = 0 and LSE = -inf.
  *   - LSE is the natural-log log-sum-exp of the scaled, masked scores, fp32.
+ *   - Dropout (dropout_p > 0; bf16 only): the attention probabilities are
+ *     dropped after the softmax (LSE is of the undropped softmax), as the
+ *     dropout_p argument of every API example of the MindSpore page and the
+ *     fused softmax/mask/dropout of the ms-swift integration page describe.
+ *     Element (query row i, key j) of head slot b * heads + h (b: batch entry
+ *     or packed sequence; i, j counted within it) draws byte (j & 3) of word
+ *     ((j & 31) >> 3) of Philox4x32-10 (Salmon et al., "Parallel random
+ *     numbers: as easy as 1, 2, 3", SC 2011) with counter (2 (j >> 5) +
+ *     ((j >> 2) & 1), i, slot, dropout_offset) and key (dropout_seed mod
+ *     2^32, dropout_seed >> 32).  It is kept iff that byte < K =
+ *     round(256 (1 - dropout_p)) (at least 1), and kept values are scaled by
+ *     256 / K, so dropout_p is in effect rounded to a multiple of 1/256
+ *     (below 1/512 it is no dropout).  The backward regenerates the same
+ *     mask from the same (seed, offset).
  *   - Errors: a non-FA_OK status is returned and fa_last_error() describes it.
  *     FA_ERR_INVALID_ARGUMENT and FA_ERR_DTYPE_MISMATCH are detected on the
  *     host before anything is launched; kernel faults surface at the caller's
@@ -59,7 +73,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 5
+#define FA_ABI_VERSION 6
 
 typedef enum {
   FA_F32 = 0,       /* IEEE binary32 */
@@ -96,6 +110,9 @@ typedef struct {
   int32_t causal;  /* 0 or 1 */
   int32_t window;  /* 0 = unlimited, W > 0 = sliding window of W keys */
   float q_descale, k_descale, v_descale;
+  float dropout_p;          /* 0 <= p < 1; 0 = no dropout */
+  uint32_t dropout_offset;  /* Philox counter word 3 */
+  uint64_t dropout_seed;    /* Philox key */
 } fa_fwd_params;
 
 /* Packed variable-length forward (self-attention within each sequence).
@@ -118,6 +135,9 @@ typedef struct {
   float softmax_scale;
   int32_t causal, window;
   float q_descale, k_descale, v_descale;
+  float dropout_p;
+  uint32_t dropout_offset;
+  uint64_t dropout_seed;
 } fa_varlen_fwd_params;
 
 /* Dense backward (recomputation from the saved LSE).
@@ -140,6 +160,9 @@ typedef struct {
   int64_t dq_stride[3], dk_stride[3], dv_stride[3];
   float softmax_scale;
   int32_t causal, window, deterministic;
+  float dropout_p;          /* the forward's dropout: same p, seed, offset */
+  uint32_t dropout_offset;
+  uint64_t dropout_seed;
 } fa_bwd_params;
 
 /* Packed variable-length backward: the gradients of fa_varlen_fwd, by the
@@ -166,6 +189,9 @@ typedef struct {
   int64_t dq_stride[2], dk_stride[2], dv_stride[2];
   float softmax_scale;
   int32_t causal, window, deterministic;
+  float dropout_p;
+  uint32_t dropout_offset;
+  uint64_t dropout_seed;
 } fa_varlen_bwd_params;
 
 /* Merge of partial results: attention over disjoint key subsets p, each

@@ -47,10 +47,31 @@ def test_library_exports_every_declared_symbol(lib):
     assert lib.fa_abi_version() == B.ABI_VERSION
 
 
-def test_struct_sizes_match_c_layout():
-    # offsets follow the C rules for these field lists (pointers 8, enums/int32 4, int64 8)
-    assert ctypes.sizeof(B.FwdParams) == 5 * 8 + 7 * 4 + 4 + 12 * 8 + 6 * 4
-    assert B.FwdParams.q_stride.offset == 5 * 8 + 7 * 4 + 4
+STRUCTS = {"fa_fwd_params": "FwdParams", "fa_varlen_fwd_params": "VarlenFwdParams", "fa_bwd_params": "BwdParams",
+           "fa_varlen_bwd_params": "VarlenBwdParams", "fa_merge_params": "MergeParams",
+           "fa_kvcache_params": "KvcacheParams"}
+
+
+def test_struct_layout_matches_the_header(tmp_path):
+    """Every parameter struct of the binding has the size and field offsets
+    that a C compiler gives the declaration in include/fa.h."""
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "fa.h"', "int main(void) {"]
+    for cname, pname in STRUCTS.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for field, _ in getattr(B, pname)._fields_:
+            lines.append(f'printf("{cname} {field} %zu\\n", offsetof({cname}, {field}));')
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    got = {tuple(ln.split()[:2]): int(ln.split()[2]) for ln in out if ln}
+    for cname, pname in STRUCTS.items():
+        cls = getattr(B, pname)
+        assert got[(cname, "size")] == ctypes.sizeof(cls), cname
+        for field, _ in cls._fields_:
+            assert got[(cname, field)] == getattr(cls, field).offset, (cname, field)
 
 
 def _fwd_params(dtype=torch.bfloat16, b=1, n=16, h=2, d=64, causal=True, window=0):
@@ -235,6 +256,26 @@ def test_kvcache_checks(lib):
     p = B.make_kvcache_params(q, pages, pages, q, q, seq, o, lse, causal=True, block_table=table)
     p.cache_len = 321  # more rows than the table can map
     assert lib.fa_check_kvcache(ctypes.byref(p)) == B.FA_ERR_INVALID_ARGUMENT
+
+
+def test_dropout_checks(lib):
+    p, keep = _fwd_params()
+    p.dropout_p = 0.1
+    assert _status(lib, p)[0] == B.FA_OK
+    for bad in (1.0, -0.1, float("nan")):
+        p.dropout_p = bad
+        assert _status(lib, p)[0] == B.FA_ERR_INVALID_ARGUMENT
+    p, keep = _fwd_params(torch.float32)
+    p.dropout_p = 0.1
+    st, err = _status(lib, p)
+    assert st == B.FA_ERR_UNSUPPORTED and "bf16" in err
+    q = torch.zeros(1, 16, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="seed"):
+        B.make_fwd_params(q, q, q, q, None, dropout_p=0.1)
+    g = torch.zeros(1, 16, 2, 64, dtype=torch.float32)
+    lse = torch.zeros(1, 2, 16, dtype=torch.float32)
+    pb = B.make_bwd_params(q, q, q, q, q, lse, g, g, g, dropout_p=0.5, seed=3, offset=2)
+    assert lib.fa_check_bwd(ctypes.byref(pb)) == B.FA_OK and pb.dropout_seed == 3 and pb.dropout_offset == 2
 
 
 def test_python_layer_error_mapping(lib):

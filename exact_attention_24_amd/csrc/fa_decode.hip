@@ -135,21 +135,41 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const uint16_t *kb = (const uint16_t *)a.k_cache + h * a.kc_sh + c * 8;
   const uint16_t *vb = (const uint16_t *)a.v_cache + h * a.vc_sh + c * 8;
   const int jw = wave * KW + g;  // this lane group's first key of a step
-  // rows j >= hi read as zeros (and are masked)
-  auto load_kv = [&](int j, uint4 &kx, uint4 &vx) __attribute__((always_inline)) {
+  // Paged caches: the block-table entries of a step's rows are read one step
+  // before its K/V rows (which are read one step before their arithmetic),
+  // so the table lookup never stalls a K/V load.
+  const int pmask = PAGED ? (1 << a.page_shift) - 1 : 0;
+  const int32_t *tbl = PAGED ? a.block_table + (int64_t)b * a.max_blocks : nullptr;
+  auto table = [&](int j) __attribute__((always_inline)) -> int {
+    return (PAGED && j < hi) ? tbl[j >> a.page_shift] : 0;
+  };
+  // rows j >= hi read as zeros (and are masked); blk: j's table entry (paged)
+  auto load_kv = [&](int j, int blk, uint4 &kx, uint4 &vx) __attribute__((always_inline)) {
     kx = vx = uint4{0u, 0u, 0u, 0u};
     if (j < hi) {
-      kx = *(const uint4 *)(kb + cache_row<PAGED>(a, b, j, a.kc_sb, a.kc_st));
-      vx = *(const uint4 *)(vb + cache_row<PAGED>(a, b, j, a.vc_sb, a.vc_st));
+      if constexpr (PAGED) {
+        kx = *(const uint4 *)(kb + blk * a.kc_sb + (int64_t)(j & pmask) * a.kc_st);
+        vx = *(const uint4 *)(vb + blk * a.vc_sb + (int64_t)(j & pmask) * a.vc_st);
+      } else {
+        kx = *(const uint4 *)(kb + cache_row<false>(a, b, j, a.kc_sb, a.kc_st));
+        vx = *(const uint4 *)(vb + cache_row<false>(a, b, j, a.vc_sb, a.vc_st));
+      }
     }
   };
   uint4 kc[U], vc[U];
+  int tb_next[U];  // table entries of the next step's rows
 #pragma unroll
-  for (int u = 0; u < U; ++u) load_kv(lo + jw + u * G, kc[u], vc[u]);
+  for (int u = 0; u < U; ++u) {
+    load_kv(lo + jw + u * G, table(lo + jw + u * G), kc[u], vc[u]);
+    tb_next[u] = table(lo + KS + jw + u * G);
+  }
   for (int base = lo; base < hi; base += KS) {
     uint4 kn[U], vn[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) load_kv(base + KS + jw + u * G, kn[u], vn[u]);  // in flight during this step
+    for (int u = 0; u < U; ++u) {  // in flight during this step
+      load_kv(base + KS + jw + u * G, tb_next[u], kn[u], vn[u]);
+      tb_next[u] = table(base + 2 * KS + jw + u * G);
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = base + jw + u * G;

@@ -12,8 +12,8 @@
 // tiles that the mask hides entirely are skipped (FA-3 paragraph of the
 // ms-swift integration page).
 //
-// gfx950 mapping of the bf16 kernel (work-group = 8 waves x 32 query rows,
-// key tiles of 64, two waves per SIMD):
+// gfx950 mapping of the bf16 kernels (work-group = 8 waves x 32 query rows,
+// key tiles of 64, two waves per SIMD), common to both:
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims read as
 //     16-byte rows of the K tile in LDS, B = Q^T held in VGPRs for the whole
 //     loop.  The 32x32 accumulator gives every lane ONE query (lane % 32) and
@@ -25,19 +25,17 @@
 //     accumulator's; O^T again gives each lane one query, so the rescale by
 //     alpha = 2^(m_old - m_new) is a per-lane scalar (and is skipped when no
 //     row max of the wave changed).
-//   * The product of tile j-1 is deferred into tile j: the softmax stages of
-//     S(j) are issued between the MFMAs of O += V(j-1)^T P~(j-1)^T, so each
-//     wave keeps the VALU and the matrix cores busy at once.
-//   * K/V tiles stream global -> VGPR -> LDS with 16-byte buffer loads (rows
-//     past the end read as zeros), K one tile ahead of V, rings of two LDS
-//     buffers, one barrier per tile; row pitches chosen so every LDS access
-//     pattern is bank-conflict free.
 //   * Key tiles that no row sees partially run without any mask code; the
 //     edge tiles of the causal diagonal, the window and the key tail take a
 //     masked path.
 //   * Work-group ids are renumbered so each XCD (own L2) processes a
 //     contiguous range of (head, query-tile) items, keeping a head's K/V in one
 //     L2; causal items run heaviest first.
+// fwd_bf16_pp_kernel (no dropout): the two waves of a SIMD take turns, one
+// issuing the MFMAs of a key tile while the other runs its softmax, with
+// K/V staged by LDS DMA into XOR-swizzled tiles.  fwd_bf16_kernel (dropout):
+// each wave issues the softmax of tile j between the P.V MFMAs of tile j-1,
+// with K/V staged through registers into padded tiles.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -430,6 +428,306 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 forward, ping-pong between the two waves of each SIMD (no dropout).
+// A wave alternates two clusters:
+//   M(u): S(u+1) = K(u+1) Q^T, then O = alpha O + V(u)^T P~(u)^T: 32 MFMAs
+//         (d = 128) fed only by their LDS operand reads;
+//   V(u): the online softmax of S(u) into P~(u) (row max, rescale factor,
+//         exponentials, row sum, bf16 packing), and the issue of this wave
+//         group's half of the next K/V tiles as LDS DMA.
+// Waves 0-3 (one per SIMD) run half a step ahead of waves 4-7, and one
+// barrier per half step keeps them there: on every SIMD one wave issues
+// MFMAs back to back while the other works through its VALU cluster.
+// K/V tiles (64 keys) travel HBM -> LDS by buffer_load ... lds, so staging
+// takes neither registers nor LDS store instructions from the softmax wave;
+// the tiles are stored unpadded with 16-byte chunks XOR-swizzled per row,
+// which keeps the row-wise K reads and the transposed V reads conflict free.
+// ---------------------------------------------------------------------------
+constexpr int kRA = 3;  // MFMA operands read this many MFMAs ahead
+template <int D>
+__global__ __launch_bounds__(512, 2) void fwd_bf16_pp_kernel(FwdArgs a) {
+  constexpr int BR = 256, BC = 64;
+  constexpr int TS = BC * D;                  // tile elements
+  constexpr int NKK = D / 16, NDB = D / 32;
+  constexpr int NBLK = TS * 2 / 1024;         // 1 KB DMA blocks per tile
+  constexpr int RPB = 512 / D;                // rows per block
+  constexpr int BPW = NBLK / 8;               // blocks per wave per tile (a group stages half a tile)
+  static_assert(BPW >= 1 && BPW * 8 == NBLK, "block split");
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TS];  // K ring, V ring
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int ql = lane & 31, hf = lane >> 5;
+
+  int b, h, qt;
+  decode_item(a, b, h, qt);
+  int seq0 = 0, nq = a.nq, nk = a.nk;
+  if (a.cu_seqlens) {
+    seq0 = a.cu_seqlens[b];
+    nq = nk = a.cu_seqlens[b + 1] - seq0;
+  }
+  const int q0 = qt * BR;
+  if (q0 >= nq) return;  // uniform for the whole work-group
+  const int off = nk - nq;
+  const int causal = a.causal, window = a.window;
+
+  const uint16_t *qbase = (const uint16_t *)a.q + b * a.q_sb + (int64_t)seq0 * a.q_st + h * a.q_sh;
+  const uint16_t *kbase = (const uint16_t *)a.k + b * a.k_sb + (int64_t)seq0 * a.k_st + h * a.k_sh;
+  const uint16_t *vbase = (const uint16_t *)a.v + b * a.v_sb + (int64_t)seq0 * a.v_st + h * a.v_sh;
+  const __amdgpu_buffer_rsrc_t qrs = slice_rsrc(qbase, slice_bytes(nq, a.q_st, D, 2));
+  const i32x4 kw = buffer_words(kbase, slice_bytes(nk, a.k_st, D, 2));
+  const i32x4 vw = buffer_words(vbase, slice_bytes(nk, a.v_st, D, 2));
+  const uint32_t kst2 = (uint32_t)a.k_st * 2, vst2 = (uint32_t)a.v_st * 2;
+
+  const int p_lo = q0 + off, p_hi = min(q0 + BR, nq) - 1 + off;
+  int kv_lo = 0, kv_hi = nk;
+  if (causal) kv_hi = min(nk, p_hi + 1);
+  if (window > 0) kv_lo = max(0, p_lo - window + 1);
+  const int jt0 = kv_lo / BC;
+  const int jt1 = kv_hi > kv_lo ? (kv_hi + BC - 1) / BC : jt0;
+
+  const int wq0 = q0 + 32 * wave;
+  const bool wave_rows = wq0 < nq;
+  const int wp_lo = wq0 + off, wp_hi = min(wq0 + 31, nq - 1) + off;
+  const int my_q = wq0 + ql;
+  const int my_p = my_q + off;
+  auto active = [&](int jt) __attribute__((always_inline)) {
+    const int k0 = jt * BC;
+    return wave_rows && (!causal || k0 <= wp_hi) && (window <= 0 || k0 + BC - 1 > wp_lo - window);
+  };
+  // tiles a mask may cut for this wave: the window edge, the diagonal, the key tail
+  auto edge = [&](int jt) __attribute__((always_inline)) {
+    const int k0 = jt * BC;
+    return k0 + BC > nk || (causal && k0 + BC - 1 > wp_lo) || (window > 0 && k0 <= wp_hi - window);
+  };
+  const uint32_t lds0 = lds_addr(smem);
+  auto kslot = [&](int jt) __attribute__((always_inline)) { return ((jt - jt0) & 1) * TS; };
+  auto vslot = [&](int jt) __attribute__((always_inline)) { return 2 * TS + ((jt - jt0) & 1) * TS; };
+
+  uint4 qreg[NKK];
+  {
+    const uint32_t qoff = (uint32_t)my_q * (uint32_t)a.q_st * 2 + hf * 16;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qreg[kk] = bload16(qrs, qoff + kk * 32);
+  }
+
+  // DMA: lane l of block q of a tile fills physical chunk l % (D / 8) of row
+  // RPB q + l / (D / 8), i.e. logical chunk (that) ^ swz(row)
+  auto dma_goff = [&](int q, uint32_t st2) __attribute__((always_inline)) {
+    const int r = RPB * q + lane / (D / 8), lc = (lane % (D / 8)) ^ swz<D>(r);
+    return (uint32_t)r * st2 + lc * 16;
+  };
+  uint32_t kgo[BPW], vgo[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int q = (wave & 3) * BPW + i + grp * (NBLK / 2);
+    kgo[i] = dma_goff(q, kst2);
+    vgo[i] = dma_goff(q, vst2);
+  }
+  // this wave's blocks of K(ts + 1) and V(ts)
+  auto dma_half = [&](int ts) __attribute__((always_inline)) {
+    if (ts + 1 < jt1) {
+      const uint32_t gk = (uint32_t)((ts + 1) * BC) * kst2;
+#pragma unroll
+      for (int i = 0; i < BPW; ++i) {
+        const int q = (wave & 3) * BPW + i + grp * (NBLK / 2);
+        dma16_at(kw, lds0 + (uint32_t)(kslot(ts + 1) * 2 + q * 1024), gk + kgo[i]);
+      }
+    }
+    if (ts < jt1) {
+      const uint32_t gv = (uint32_t)(ts * BC) * vst2;
+#pragma unroll
+      for (int i = 0; i < BPW; ++i) {
+        const int q = (wave & 3) * BPW + i + grp * (NBLK / 2);
+        dma16_at(vw, lds0 + (uint32_t)(vslot(ts) * 2 + q * 1024), gv + vgo[i]);
+      }
+    }
+  };
+
+  // per-lane LDS offsets of the MFMA operands in a swizzled tile:
+  // K fragment (kb, kk) at (kbase_off ^ 16 kk) + 32 kb D; V^T fragment
+  // (cc, db, half) at (vt_off[half] ^ 32 db) + 16 cc D
+  const int ksw = swz<D>(ql) ^ hf;
+  const int kbase_off = ql * D + 8 * ksw;
+  const int vt_off0 = tr_off<D>(lane, 0, 0), vt_off1 = tr_off<D>(lane, 0, 1);
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = (f32x16){};
+  f32x16 s[2];
+  s[0] = s[1] = (f32x16){};
+  uint4 pb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pb[i] = (uint4){0u, 0u, 0u, 0u};
+  float m = -INFINITY, l = 0.f, alpha = 1.f;
+  const float c = a.scale_log2;
+
+  // MFMA cluster: S(u+1) = K(u+1) Q^T (kb chains interleaved), then
+  // O = alpha O + V(u)^T P~(u)^T (four independent accumulators in turn)
+  auto m_cluster = [&](int u) __attribute__((always_inline)) {
+    // the MFMA wave issues ahead of its softmax partner on the SIMD (the
+    // arbiter otherwise favours the older wave, i.e. always group 0)
+    __builtin_amdgcn_s_setprio(3);
+    if (u + 1 < jt1 && active(u + 1)) {
+      const uint16_t *ks = smem + kslot(u + 1);
+      auto kread = [&](int i) __attribute__((always_inline)) {
+        const int kb = i & 1, kk = i >> 1;
+        return *(const uint4 *)(ks + ((kbase_off ^ (16 * kk)) + kb * 32 * D));
+      };
+      uint4 kf[2 * NKK];
+#pragma unroll
+      for (int i = 0; i < kRA; ++i) kf[i] = kread(i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 2 * NKK; ++i) {
+        const int kb = i & 1, kk = i >> 1;
+        if (i + kRA < 2 * NKK) kf[i + kRA] = kread(i + kRA);
+        s[kb] = mfma_bf16(kf[i], qreg[kk], kk == 0 ? (f32x16){} : s[kb]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (u >= jt0 && active(u)) {
+      if (__ballot(alpha != 1.f)) {  // rarely taken once the row maxima settle
+        float a_r = alpha;
+        asm volatile("" : "+v"(a_r));
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) acc[i] *= a_r;
+      }
+      const uint16_t *vs = smem + vslot(u);
+      auto vread = [&](int i) __attribute__((always_inline)) {
+        const int cc = i / NDB, db = i % NDB;
+        const uint2 lo = lds_read_tr16(vs + ((vt_off0 ^ (32 * db)) + cc * 16 * D));
+        const uint2 hi = lds_read_tr16(vs + ((vt_off1 ^ (32 * db)) + cc * 16 * D));
+        return (uint4){lo.x, lo.y, hi.x, hi.y};
+      };
+      constexpr int NPV = 4 * NDB;
+      uint4 vf[NPV];
+#pragma unroll
+      for (int i = 0; i < kRA; ++i) vf[i] = vread(i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        if (i + kRA < NPV) vf[i + kRA] = vread(i + kRA);
+        const int cc = i / NDB, db = i % NDB;
+        acc[db] = mfma_bf16(vf[i], pb[cc], acc[db]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // softmax cluster for tile v: P~(v) into pb, the rescale alpha of O, l
+  auto softmax = [&](auto mask_tag, int v) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int k0 = v * BC;
+    if (MASK) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
+          const bool ok = key < nk && (!causal || key <= my_p) && (window <= 0 || key > my_p - window);
+          if (!ok) s[kb][e] = -INFINITY;
+        }
+    }
+    float mp[4];  // four partial maxima: short dependency chains
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mp[j] = fmaxf(s[j >> 1][(j & 1) * 8], s[j >> 1][(j & 1) * 8 + 1]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 2; e < 8; ++e) mp[j] = fmaxf(mp[j], s[j >> 1][(j & 1) * 8 + e]);
+    float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
+    mx = half_swap_max(mx) * c;
+    const bool up = mx > m + kLazy;
+    alpha = up ? fast_exp2(m - mx) : 1.f;
+    m = up ? mx : m;
+    const float m_use = m == -INFINITY ? 0.f : m;
+    float rp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = fast_exp2(__builtin_fmaf(s[kb][e], c, -m_use));
+        s[kb][e] = p;
+        rp[(kb * 16 + e) & 3] += p;
+      }
+    l = l * alpha + ((rp[0] + rp[1]) + (rp[2] + rp[3]));
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const int kb = cc >> 1, r0 = (cc & 1) * 8;
+      pb[cc].x = pack_bf16x2(s[kb][r0 + 0], s[kb][r0 + 1]);
+      pb[cc].y = pack_bf16x2(s[kb][r0 + 2], s[kb][r0 + 3]);
+      pb[cc].z = pack_bf16x2(s[kb][r0 + 4], s[kb][r0 + 5]);
+      pb[cc].w = pack_bf16x2(s[kb][r0 + 6], s[kb][r0 + 7]);
+    }
+  };
+  // softmax cluster at half step hs: issue this wave's DMA blocks of
+  // K(t + 1), V(t) with t = jt0 + hs / 2, then the softmax of S(v)
+  auto v_cluster = [&](int hs, int v) __attribute__((always_inline)) {
+    dma_half(jt0 + (hs >> 1));
+    if (v >= jt0 && v < jt1 && active(v)) {
+      if (edge(v)) softmax(std::true_type(), v);
+      else softmax(std::false_type(), v);
+    }
+  };
+
+  if (jt0 < jt1) {
+    // K(jt0) whole (every wave BPW blocks of each group's half)
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const uint32_t gk = (uint32_t)(jt0 * BC) * kst2;
+      const int q = (wave & 3) * BPW + i + grp * (NBLK / 2);
+      dma16_at(kw, lds0 + (uint32_t)(kslot(jt0) * 2 + q * 1024), gk + kgo[i]);
+    }
+    wait_dma();
+    __syncthreads();
+    // half step 2 i: group 0 runs M(jt0 + i - 1), group 1 the softmax of
+    // tile jt0 + i - 1; half step 2 i + 1: group 0 the softmax of tile
+    // jt0 + i, group 1 M(jt0 + i - 1).  The DMA blocks issued in half steps
+    // 2 i and 2 i + 1 are read from half step 2 i + 2 on: group 0 waits for
+    // its own at the end of its softmax, group 1 at the end of its M.
+    const int n = jt1 - jt0;
+    if (grp == 0) {
+      for (int i = 0; i <= n; ++i) {
+        m_cluster(jt0 + i - 1);
+        __syncthreads();
+        v_cluster(2 * i + 1, jt0 + i);
+        wait_dma();
+        __syncthreads();
+      }
+    } else {
+      for (int i = 0; i <= n; ++i) {
+        v_cluster(2 * i, jt0 + i - 1);
+        __syncthreads();
+        m_cluster(jt0 + i - 1);
+        wait_dma();
+        __syncthreads();
+      }
+    }
+  }
+
+  // epilogue: O = acc / l (bf16, round to nearest even), LSE = (m + log2 l) ln 2
+  const float lt = half_swap_sum(l);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (my_q < nq) {
+    uint16_t *orow = (uint16_t *)a.o + b * a.o_sb + (int64_t)(seq0 + my_q) * a.o_st + h * a.o_sh;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        uint2 w;
+        w.x = pack_bf16x2(acc[db][4 * rb + 0] * inv, acc[db][4 * rb + 1] * inv);
+        w.y = pack_bf16x2(acc[db][4 * rb + 2] * inv, acc[db][4 * rb + 3] * inv);
+        *(uint2 *)(orow + db * 32 + 8 * rb + 4 * hf) = w;
+      }
+    if (hf == 0 && a.lse)
+      a.lse[b * a.lse_sb + h * a.lse_sh + seq0 + my_q] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+  }
+}
+
 // fp32 forward (small workloads): 4 waves x 16 query rows; a query's dot
 // product is split over 4 lanes (one quarter of the head dim each) and
 // combined with two lane exchanges.  Key tiles of 32 in LDS, the same online
@@ -539,8 +837,8 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, int head_dim, hipStream_t s) {
     if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_kernel<128, 8, true>), grid, dim3(512), 0, s, a);
     else hipLaunchKernelGGL((fwd_bf16_kernel<64, 8, true>), grid, dim3(512), 0, s, a);
   } else {
-    if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_kernel<128, 8, false>), grid, dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((fwd_bf16_kernel<64, 8, false>), grid, dim3(512), 0, s, a);
+    if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_pp_kernel<128>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((fwd_bf16_pp_kernel<64>), grid, dim3(512), 0, s, a);
   }
   return hipGetLastError();
 }

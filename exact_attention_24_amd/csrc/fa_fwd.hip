@@ -445,8 +445,20 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
 // which keeps the row-wise K reads and the transposed V reads conflict free.
 // ---------------------------------------------------------------------------
 constexpr int kRA = 3;  // MFMA operands read this many MFMAs ahead
+// row pitch (elements) of the O tile staged in LDS by the epilogue: 16-byte
+// aligned rows for the row-wise read-back
 template <int D>
-__global__ __launch_bounds__(512, 2) void fwd_bf16_pp_kernel(FwdArgs a) {
+constexpr int kOP = D + 8;
+// LDS of the ping-pong kernel: the K and V rings, or the staged O tile
+template <int D>
+constexpr int kPPLds = (4 * 64 * D > 256 * kOP<D>) ? 4 * 64 * D : 256 * kOP<D>;
+// Work-group barrier for LDS reuse only: waits for this wave's LDS accesses,
+// not for its global stores to retire (__syncthreads would wait for both).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// one (batch or sequence b, head h, query tile qt) work item
+template <int D>
+__device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, uint16_t *smem) {
   constexpr int BR = 256, BC = 64;
   constexpr int TS = BC * D;                  // tile elements
   constexpr int NKK = D / 16, NDB = D / 32;
@@ -454,15 +466,12 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_pp_kernel(FwdArgs a) {
   constexpr int RPB = 512 / D;                // rows per block
   constexpr int BPW = NBLK / 8;               // blocks per wave per tile (a group stages half a tile)
   static_assert(BPW >= 1 && BPW * 8 == NBLK, "block split");
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TS];  // K ring, V ring
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;
   const int ql = lane & 31, hf = lane >> 5;
 
-  int b, h, qt;
-  decode_item(a, b, h, qt);
   int seq0 = 0, nq = a.nq, nk = a.nk;
   if (a.cu_seqlens) {
     seq0 = a.cu_seqlens[b];
@@ -709,11 +718,14 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_pp_kernel(FwdArgs a) {
     }
   }
 
-  // epilogue: O = acc / l (bf16, round to nearest even), LSE = (m + log2 l) ln 2
+  // epilogue: O = acc / l (bf16, round to nearest even), LSE = (m + log2 l) ln 2.
+  // O goes through LDS (the K/V tiles are free once the loop's last barrier
+  // has passed) so that it leaves as whole 16-byte-per-lane rows: scattered
+  // 8-byte pieces of 32 rows per store take several times longer to retire.
   const float lt = half_swap_sum(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (my_q < nq) {
-    uint16_t *orow = (uint16_t *)a.o + b * a.o_sb + (int64_t)(seq0 + my_q) * a.o_st + h * a.o_sh;
+  {
+    uint16_t *ot = smem + (32 * wave + ql) * kOP<D>;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -721,10 +733,54 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_pp_kernel(FwdArgs a) {
         uint2 w;
         w.x = pack_bf16x2(acc[db][4 * rb + 0] * inv, acc[db][4 * rb + 1] * inv);
         w.y = pack_bf16x2(acc[db][4 * rb + 2] * inv, acc[db][4 * rb + 3] * inv);
-        *(uint2 *)(orow + db * 32 + 8 * rb + 4 * hf) = w;
+        *(uint2 *)(ot + db * 32 + 8 * rb + 4 * hf) = w;
       }
-    if (hf == 0 && a.lse)
-      a.lse[b * a.lse_sb + h * a.lse_sh + seq0 + my_q] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+  }
+  if (my_q < nq && hf == 0 && a.lse)
+    a.lse[b * a.lse_sb + h * a.lse_sh + seq0 + my_q] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+  lds_barrier();
+  uint16_t *obase = (uint16_t *)a.o + b * a.o_sb + (int64_t)(seq0 + q0) * a.o_st + h * a.o_sh;
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+#pragma unroll
+  for (int i = 0; i < BR * CPR / 512; ++i) {
+    const int idx = tid + i * 512, row = idx / CPR, ch = idx % CPR;
+    const uint4 v = *(const uint4 *)(smem + row * kOP<D> + ch * 8);
+    if (q0 + row < nq) *(uint4 *)(obase + (int64_t)row * a.o_st + ch * 8) = v;
+  }
+}
+
+// Dense calls with at least one unit per work-group run persistently: the
+// grid is a multiple of 8 (one work-group per CU), XCD x = blockIdx % 8 owns
+// the contiguous unit range [x U / 8, (x + 1) U / 8) (a few heads, so their
+// K/V stay in its L2), and its work-groups take every (G / 8)-th unit of it.
+// Under a causal mask a unit pairs query tiles nqt - 1 - i and i, so every
+// unit carries the same number of key tiles; otherwise a unit is one tile.
+// A static schedule has no dispatch gaps between work items (the hardware
+// hands out work-groups in block order over the XCDs, so a CU that frees up
+// early can idle until the next block's XCD has room).
+template <int D>
+__global__ __launch_bounds__(512, 2) void fwd_bf16_pp_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[kPPLds<D>];  // K ring, V ring / staged O
+  if (!a.persist) {
+    int b, h, qt;
+    decode_item(a, b, h, qt);
+    pp_item<D>(a, b, h, qt, smem);
+    return;
+  }
+  const int per = a.causal ? (a.nqt + 1) / 2 : a.nqt;  // units per (batch, head)
+  const int units = a.batch * a.heads * per;
+  const int xcd = blockIdx.x % 8, nx = gridDim.x / 8;
+  const int lo = (int)((int64_t)units * xcd / 8), hi = (int)((int64_t)units * (xcd + 1) / 8);
+  for (int u = lo + (int)(blockIdx.x / 8); u < hi; u += nx) {
+    const int bh = u / per, i = u % per;
+    const int b = bh / a.heads, h = bh % a.heads;
+    const int qt = a.causal ? a.nqt - 1 - i : i;
+    pp_item<D>(a, b, h, qt, smem);
+    lds_barrier();  // the next item's DMA reuses the LDS that the epilogue read
+    if (a.causal && i != qt) {
+      pp_item<D>(a, b, h, i, smem);
+      lds_barrier();
+    }
   }
 }
 
@@ -825,6 +881,21 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
 
 }  // namespace
 
+// Work-groups of a persistent launch: the current device's CU count, rounded
+// down to a multiple of the 8 XCDs (one 512-thread work-group fits per CU);
+// 0 if the count cannot be read.
+int persistent_groups() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = (n / 8) * 8;
+  }
+  return cached[dev];
+}
+
 int fwd_block_rows(int qkv_dtype, int head_dim) {
   (void)head_dim;
   if (qkv_dtype == 0) return 64;  // fp32 kernel: 4 waves x 16 rows
@@ -837,8 +908,14 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, int head_dim, hipStream_t s) {
     if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_kernel<128, 8, true>), grid, dim3(512), 0, s, a);
     else hipLaunchKernelGGL((fwd_bf16_kernel<64, 8, true>), grid, dim3(512), 0, s, a);
   } else {
-    if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_pp_kernel<128>), grid, dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((fwd_bf16_pp_kernel<64>), grid, dim3(512), 0, s, a);
+    FwdArgs p = a;
+    dim3 g = grid;
+    const int cus = persistent_groups();
+    const int64_t units = (int64_t)a.batch * a.heads * (a.causal ? (a.nqt + 1) / 2 : a.nqt);
+    p.persist = !a.cu_seqlens && cus >= 8 && units >= cus;
+    if (p.persist) g = dim3((unsigned)cus);
+    if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_pp_kernel<128>), g, dim3(512), 0, s, p);
+    else hipLaunchKernelGGL((fwd_bf16_pp_kernel<64>), g, dim3(512), 0, s, p);
   }
   return hipGetLastError();
 }

@@ -29,6 +29,7 @@ struct FwdArgs {
   // kept probabilities scaled by drop_scale = 256 / drop_k
   uint32_t drop_k, seed_lo, seed_hi, drop_offset;
   float drop_scale;
+  int32_t persist;               // bf16 forward: persistent launch over a static schedule (set by the launcher)
 };
 
 // Kernel-side view of one backward call.  Packed varlen calls set

@@ -104,6 +104,36 @@ def test_llama_n8192_sampled_rows(name):
         assert_lse_close(lse64[0, h], rl)
 
 
+PERSISTENT = [
+    # shapes with >= 256 work units (one per CU), so the bf16 forward runs its
+    # persistent schedule: (batch, nq, nk, heads, d, causal, window)
+    (2, 1100, 1100, 48, 64, True, 0),     # 5 query tiles: the middle one is unpaired; ragged last tile
+    (3, 1300, 1300, 32, 128, True, 0),    # 6 query tiles, batch 3
+    (2, 1536, 1536, 48, 128, True, 300),  # causal + sliding window
+    (1, 1100, 1500, 64, 128, False, 0),   # non-causal, Nq < Nk
+    (2, 900, 1400, 64, 64, True, 0),      # bottom-right causal, Nq < Nk
+    (1, 1000, 1000, 64, 128, False, 200), # window without causal
+]
+
+
+@pytest.mark.parametrize("b,nq,nk,h,d,causal,window", PERSISTENT)
+def test_bf16_persistent_schedule_sampled_rows(b, nq, nk, h, d, causal, window):
+    print(f"[fwd persistent] b={b} nq={nq} nk={nk} h={h} d={d} causal={causal} window={window}", flush=True)
+    q, _, _ = dense_inputs(b, nq, h, d, "bf16", seed=nq * 7 + h)
+    _, k, v = dense_inputs(b, nk, h, d, "bf16", seed=nk * 7 + h + 1)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = _run(q, k, v, causal, window)
+    q64, k64, v64, o64, lse64 = f64(q), f64(k), f64(v), f64(o), f64(lse)
+    for bi in range(b):
+        for hh in sorted({0, h // 2 + bi, h - 1}):
+            rows = sample_rows(nq, 24, seed=bi * 1000 + hh)
+            rows = np.union1d(rows, [0, nq - 1, min(nq - 1, 255), min(nq - 1, 256)])
+            ro, rl = oracle.attention_fwd(q64[bi, rows, hh], k64[bi, :, hh], v64[bi, :, hh], scale, causal, window,
+                                          q_pos=rows, nq=nq)
+            assert_close(o64[bi, rows, hh], ro, what=f"O batch {bi} head {hh}")
+            assert_lse_close(lse64[bi, hh, rows], rl)
+
+
 def test_causal_row0_is_v0_bitwise():
     """Causal row 0 sees only key 0: P~ = 1, l = 1, so O_0 is exactly V_0."""
     q, k, v = dense_inputs(2, 500, 4, 128, "bf16", seed=3)

@@ -502,7 +502,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 //    dQ is written once, no atomics.
 // ---------------------------------------------------------------------------
 template <int D, bool DROP>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
+__device__ __forceinline__ void dq_item(const BwdArgs &a, int b, int h, int qt) {
   constexpr int NW = 4, T = NW * 64, QW = 64, BR = NW * QW, BC = 64;
   constexpr int DCH = D / 8, TS = BC * D;
   constexpr int PER = BC * DCH / T;  // DMA loads per lane per tile and tensor
@@ -517,9 +517,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   const int ql = lane & 31, hf = lane >> 5;
   const int causal = a.causal, window = a.window;
 
-  const int nqt = (a.nq + BR - 1) / BR;
-  int b, h, qt;
-  fwd_item(blockIdx.x, nqt, a.heads, a.batch, a.cu_seqlens != nullptr, causal, b, h, qt);
   int seq0 = 0, nq = a.nq, nk = a.nk;
   if (a.cu_seqlens) {
     seq0 = a.cu_seqlens[b];
@@ -844,6 +841,63 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     }
   }
 }
+// Work-group barrier for LDS reuse only: waits for this wave's LDS accesses,
+// not for its global stores to retire.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Items of the dQ kernel.  Dense calls with at least one unit per
+// work-group can run persistently: one work-group per CU (grid a multiple of
+// 8), XCD x = blockIdx % 8 owning the contiguous unit range
+// [x U / 8, (x+1) U / 8) and its work-groups every (G / 8)-th unit of it.
+// Under a causal mask a unit pairs tiles i and ntiles - 1 - i, so all units
+// carry the same work; otherwise a unit is one tile.  Without `persist`, one
+// item per work-group in the XCD-aware order of fwd_item.  `heavy_low` says
+// whether low tile indices carry the most work (key tiles) or high ones
+// (query tiles).  The kernel calls its item body from one place, on its own
+// by-value argument block (a reference to it would push it to scratch).
+struct ItemRange {
+  int lo, hi, step, per;
+};
+__device__ __forceinline__ ItemRange item_range(const BwdArgs &a, int ntiles) {
+  if (!a.persist) return {0, 1, 1, 1};
+  const int per = a.causal ? (ntiles + 1) / 2 : ntiles;
+  const int units = a.batch * a.heads * per;
+  const int xcd = blockIdx.x % 8;
+  return {(int)((int64_t)units * xcd / 8) + (int)(blockIdx.x / 8), (int)((int64_t)units * (xcd + 1) / 8),
+          (int)(gridDim.x / 8), per};
+}
+// sub-item j (0, 1) of unit u; false if the unit has no such item
+__device__ __forceinline__ bool item_at(const BwdArgs &a, int ntiles, bool heavy_low, const ItemRange &r, int u,
+                                        int j, int &b, int &h, int &t) {
+  if (!a.persist) {
+    fwd_item(blockIdx.x, ntiles, a.heads, a.batch, a.cu_seqlens != nullptr, a.causal && !heavy_low, b, h, t);
+    return j == 0;
+  }
+  const int bh = u / r.per, i = u % r.per;
+  b = bh / a.heads;
+  h = bh % a.heads;
+  if (!a.causal) {
+    t = i;
+    return j == 0;
+  }
+  const int heavy = heavy_low ? i : ntiles - 1 - i, light = ntiles - 1 - heavy;
+  t = j == 0 ? heavy : light;
+  return j == 0 || heavy != light;
+}
+
+template <int D, bool DROP>
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
+  const int nqt = (a.nq + 255) / 256;  // query tiles of 256; high ones carry the most work under a causal mask
+  const ItemRange r = item_range(a, nqt);
+  for (int u = r.lo; u < r.hi; u += r.step)
+    for (int j = 0; j < 2; ++j) {
+      int b, h, qt;
+      if (!item_at(a, nqt, false, r, u, j, b, h, qt)) break;
+      dq_item<D, DROP>(a, b, h, qt);
+      lds_barrier();
+    }
+}
+
 
 // ---------------------------------------------------------------------------
 // 4. The start of every causal sequence: query rows at positions p with
@@ -1067,15 +1121,28 @@ hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t s) {
     constexpr int RPB = 256 / (D / 8);
     hipLaunchKernelGGL((bwd_dsum_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, a, rows);
   }
+  const int cus = persistent_groups();
+  // grid and flag of a launch over `tiles` tiles per (batch, head)
+  auto plan = [&](int64_t tiles, BwdArgs &p) {
+    const int64_t items = tiles * a.heads * a.batch;
+    const int64_t units = (a.causal ? (tiles + 1) / 2 : tiles) * a.heads * a.batch;
+    p = a;
+    p.persist = !a.cu_seqlens && cus >= 8 && units >= cus;
+    return p.persist ? (int64_t)cus : items;
+  };
+  // dK/dV keeps one work-group per key tile: its items end in 128 KB of
+  // fp32 gradient stores that the next item's DMA wait would drain, and a
+  // persistent schedule measured 9% slower there (dQ: 7-8% faster)
   const int64_t kv_items = (int64_t)((a.nk + 32 * NW_KV - 1) / (32 * NW_KV)) * a.heads * a.batch;
   if (kv_items > 0) {
     if (a.drop_k) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)kv_items), dim3(NW_KV * 64), 0, s, a);
     else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)kv_items), dim3(NW_KV * 64), 0, s, a);
   }
-  const int64_t q_items = (int64_t)((a.nq + 256 - 1) / 256) * a.heads * a.batch;
-  if (q_items > 0) {
-    if (a.drop_k) hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)q_items), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)q_items), dim3(256), 0, s, a);
+  BwdArgs pq;
+  const int64_t q_grid = plan((a.nq + 256 - 1) / 256, pq);
+  if (q_grid > 0) {
+    if (a.drop_k) hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)q_grid), dim3(256), 0, s, pq);
+    else hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)q_grid), dim3(256), 0, s, pq);
   }
   const int64_t start_items = (int64_t)a.batch * a.heads * kStartSplit;
   if (a.causal && start_items > 0 && a.nq > 0 && a.nk > 0)

@@ -50,6 +50,7 @@ struct BwdArgs {
   float scale, scale_log2;
   uint32_t drop_k, seed_lo, seed_hi, drop_offset;  // dropout, as in FwdArgs
   float drop_scale;
+  int32_t persist;   // dK/dV or dQ kernel: persistent launch over a static schedule (set by the launcher)
 };
 
 // Kernel-side view of one merge of partial results (O_p, LSE_p).
@@ -93,6 +94,10 @@ size_t bwd_workspace_bytes(int batch, int heads, int nq, int head_dim, int deter
 hipError_t launch_merge(const MergeArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_kv_append(const DecodeArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int head_dim, hipStream_t s);
+
+// Work-groups of a persistent launch on the current device: its CU count
+// rounded down to a multiple of the 8 XCDs (0 if it cannot be read).
+int persistent_groups();
 
 // Query-tile rows per work-group of each forward kernel (grid sizing).
 int fwd_block_rows(int qkv_dtype, int head_dim);

@@ -67,6 +67,33 @@ def test_bwd_n8192_full_size():
     assert np.abs(dv64.sum(axis=1) - do.sum(axis=1)).max() < 0.05
 
 
+PERSISTENT = [
+    # shapes with >= 256 dQ work units (one per CU), so the dQ kernel runs its
+    # persistent schedule: (batch, nq, nk, heads, d, causal, window)
+    (2, 1100, 1100, 48, 64, True, 0),     # 5 query tiles of 256: the middle one unpaired; ragged tail
+    (1, 1300, 1300, 96, 128, True, 200),  # 6 tiles, causal + window
+    (1, 1100, 1100, 64, 64, False, 0),    # non-causal: one tile per unit
+]
+
+
+@pytest.mark.parametrize("b,nq,nk,h,d,causal,window", PERSISTENT)
+def test_bwd_persistent_dq_whole_heads(b, nq, nk, h, d, causal, window):
+    """dQ, dK, dV of a few whole heads against the oracle."""
+    print(f"[bwd persistent] b={b} nq={nq} h={h} d={d} causal={causal} window={window}", flush=True)
+    q, _, _, do = dense_inputs(b, nq, h, d, "bf16", seed=nq * 5 + h, with_dout=True)
+    _, k, v = dense_inputs(b, nk, h, d, "bf16", seed=nq * 5 + h + 1)
+    dq, dk, dv = _fwd_bwd(q, k, v, do, causal, window)
+    q64, k64, v64, do64 = f64(q), f64(k), f64(v), f64(do)
+    dq64, dk64, dv64 = f64(dq), f64(dk), f64(dv)
+    for bi in range(b):
+        for hh in sorted({0, (h // 2 + 7 * bi) % h, h - 1}):
+            rq, rk, rv = oracle.attention_bwd(q64[bi, :, hh], k64[bi, :, hh], v64[bi, :, hh], do64[bi, :, hh],
+                                              1 / np.sqrt(d), causal, window)
+            assert_close(dq64[bi, :, hh], rq, what=f"dQ batch {bi} head {hh}")
+            assert_close(dk64[bi, :, hh], rk, what=f"dK batch {bi} head {hh}")
+            assert_close(dv64[bi, :, hh], rv, what=f"dV batch {bi} head {hh}")
+
+
 def test_bwd_deterministic_bitwise():
     q, k, v, do = dense_inputs(1, 700, 4, 128, "bf16", seed=21, with_dout=True)
     g1 = _fwd_bwd(q, k, v, do, True, 0)

@@ -841,60 +841,21 @@ __device__ __forceinline__ void dq_item(const BwdArgs &a, int b, int h, int qt) 
     }
   }
 }
-// Work-group barrier for LDS reuse only: waits for this wave's LDS accesses,
-// not for its global stores to retire.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Items of the dQ kernel.  Dense calls with at least one unit per
-// work-group can run persistently: one work-group per CU (grid a multiple of
-// 8), XCD x = blockIdx % 8 owning the contiguous unit range
-// [x U / 8, (x+1) U / 8) and its work-groups every (G / 8)-th unit of it.
-// Under a causal mask a unit pairs tiles i and ntiles - 1 - i, so all units
-// carry the same work; otherwise a unit is one tile.  Without `persist`, one
-// item per work-group in the XCD-aware order of fwd_item.  `heavy_low` says
-// whether low tile indices carry the most work (key tiles) or high ones
-// (query tiles).  The kernel calls its item body from one place, on its own
+// dQ items: query tiles of 256, high ones carry the most work under a causal
+// mask.  Dense calls with at least one unit per CU run persistently (see
+// launch_units); the item body is called from one place, on the kernel's own
 // by-value argument block (a reference to it would push it to scratch).
-struct ItemRange {
-  int lo, hi, step, per;
-};
-__device__ __forceinline__ ItemRange item_range(const BwdArgs &a, int ntiles) {
-  if (!a.persist) return {0, 1, 1, 1};
-  const int per = a.causal ? (ntiles + 1) / 2 : ntiles;
-  const int units = a.batch * a.heads * per;
-  const int xcd = blockIdx.x % 8;
-  return {(int)((int64_t)units * xcd / 8) + (int)(blockIdx.x / 8), (int)((int64_t)units * (xcd + 1) / 8),
-          (int)(gridDim.x / 8), per};
-}
-// sub-item j (0, 1) of unit u; false if the unit has no such item
-__device__ __forceinline__ bool item_at(const BwdArgs &a, int ntiles, bool heavy_low, const ItemRange &r, int u,
-                                        int j, int &b, int &h, int &t) {
-  if (!a.persist) {
-    fwd_item(blockIdx.x, ntiles, a.heads, a.batch, a.cu_seqlens != nullptr, a.causal && !heavy_low, b, h, t);
-    return j == 0;
-  }
-  const int bh = u / r.per, i = u % r.per;
-  b = bh / a.heads;
-  h = bh % a.heads;
-  if (!a.causal) {
-    t = i;
-    return j == 0;
-  }
-  const int heavy = heavy_low ? i : ntiles - 1 - i, light = ntiles - 1 - heavy;
-  t = j == 0 ? heavy : light;
-  return j == 0 || heavy != light;
-}
-
 template <int D, bool DROP>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
-  const int nqt = (a.nq + 255) / 256;  // query tiles of 256; high ones carry the most work under a causal mask
-  const ItemRange r = item_range(a, nqt);
+  const int nqt = (a.nq + 255) / 256;
+  const bool varlen = a.cu_seqlens != nullptr;
+  const UnitRange r = launch_units(a.persist, a.batch, a.heads, nqt, a.causal);
   for (int u = r.lo; u < r.hi; u += r.step)
     for (int j = 0; j < 2; ++j) {
       int b, h, qt;
-      if (!item_at(a, nqt, false, r, u, j, b, h, qt)) break;
+      if (!launch_tile(a.persist, r, u, j, a.batch, a.heads, nqt, varlen, a.causal, false, b, h, qt)) break;
       dq_item<D, DROP>(a, b, h, qt);
-      lds_barrier();
+      lds_barrier();  // the next item's DMA reuses the LDS tiles
     }
 }
 

@@ -198,6 +198,55 @@ __device__ __forceinline__ void fwd_item(int bid, int nqt, int heads, int batch,
   qt = causal ? nqt - 1 - t : t;
 }
 
+// ---------------------------------------------------------------------------
+// Static schedule of a persistent launch (one work-group per CU, the grid a
+// multiple of the 8 XCDs).  Work is cut into units of one (batch, head) and
+// either one tile or, under a causal mask, the pair of tiles i and n - 1 - i,
+// which together carry as much work as any other pair.  XCD x = blockIdx % 8
+// owns the contiguous unit range [x U / 8, (x + 1) U / 8) (a few heads, so
+// their K/V stay in its L2) and its work-groups take every (G / 8)-th unit.
+// A static schedule has no dispatch gaps: the hardware hands out work-groups
+// in block order over the XCDs, so with one work-group per item a CU that
+// frees up early can idle until the next block's XCD has room.
+// Without `persist` the same loop runs the one item of fwd_item(blockIdx).
+// ---------------------------------------------------------------------------
+struct UnitRange {
+  int lo, hi, step, per;  // units [lo, hi) by step; units per (batch, head)
+};
+__device__ __forceinline__ UnitRange launch_units(bool persist, int batch, int heads, int ntiles, bool pair) {
+  if (!persist) return {0, 1, 1, 1};
+  const int per = pair ? (ntiles + 1) / 2 : ntiles;
+  const int units = batch * heads * per;
+  const int xcd = blockIdx.x % 8;
+  return {(int)((int64_t)units * xcd / 8) + (int)(blockIdx.x / 8), (int)((int64_t)units * (xcd + 1) / 8),
+          (int)(gridDim.x / 8), per};
+}
+// tile j (0, 1) of unit u, the heavier one first; false if there is none.
+// heavy_low: low tile indices carry the most work (key tiles under a causal
+// mask) rather than high ones (query tiles).
+__device__ __forceinline__ bool launch_tile(bool persist, const UnitRange &r, int u, int j, int batch, int heads,
+                                            int ntiles, bool varlen, bool causal, bool heavy_low, int &b, int &h,
+                                            int &t) {
+  if (!persist) {
+    fwd_item(blockIdx.x, ntiles, heads, batch, varlen, causal && !heavy_low, b, h, t);
+    return j == 0;
+  }
+  const int bh = u / r.per, i = u % r.per;
+  b = bh / heads;
+  h = bh % heads;
+  if (!causal) {
+    t = i;
+    return j == 0;
+  }
+  const int heavy = heavy_low ? i : ntiles - 1 - i, light = ntiles - 1 - heavy;
+  t = j == 0 ? heavy : light;
+  return j == 0 || heavy != light;
+}
+
+// Work-group barrier for LDS reuse only: waits for this wave's LDS accesses,
+// not for its global stores to retire (__syncthreads would wait for both).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Write a unit of 4 rows x 8 bf16 columns (r[i] = row i) transposed: column
 // `col0 + e` gets the 4 values at positions pos..pos+3 of its row (pitch
 // `pitch` elements) in the tile at `t`.

@@ -79,21 +79,25 @@ __device__ __forceinline__ int pkey(int e, int hf) {
 // FP8 forward, 8 waves of 32 query rows, two waves per SIMD, with the P.V
 // product of tile j-1 issued next to the softmax stages of tile j.
 // ---------------------------------------------------------------------------
+// row pitch (elements) of the bf16 O tile staged in LDS by the epilogue
+template <int D>
+constexpr int kFp8OP = D + 8;
+
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdArgs a) {
+__device__ __forceinline__ void fp8_item(const FwdArgs &a, int b, int h, int qt) {
   constexpr int BC = 64, BR = 32 * NW, T = NW * 64;
   constexpr int KPB = D + 16;          // K tile row pitch (bytes): 16 rows of a b128 read hit distinct banks
   constexpr int KSB = BC * KPB, VSB = BC * D;
   constexpr int DCH = D / 16;          // 16-byte chunks per row
   constexpr int NCH = (BC * DCH + T - 1) / T;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * KSB + 2 * VSB];
+  constexpr int OSB = BR * kFp8OP<D> * 2;  // staged O tile (bytes)
+  // K and V rings; the epilogue reuses the space for the O tile
+  __shared__ __attribute__((aligned(16))) uint8_t smem[(2 * KSB + 2 * VSB > OSB) ? 2 * KSB + 2 * VSB : OSB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int ql = lane & 31, hf = lane >> 5;
 
-  int b, h, qt;
-  fwd_item(blockIdx.x, a.nqt, a.heads, a.batch, a.cu_seqlens != nullptr, a.causal, b, h, qt);
   int seq0 = 0, nq = a.nq, nk = a.nk;
   if (a.cu_seqlens) {
     seq0 = a.cu_seqlens[b];
@@ -353,11 +357,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdArgs a) {
     }
   }
 
-  // note: l sums the fp32 P~ (before quantisation), as the softmax denominator
+  // note: l sums the fp32 P~ (before quantisation), as the softmax denominator.
+  // O goes through LDS (free once every wave is past its last product) so
+  // that it leaves as whole 16-byte-per-lane rows.
   const float lt = half_swap_sum(l);
   const float inv = lt > 0.f ? a.v_descale / lt : 0.f;
-  if (my_q < nq) {
-    uint16_t *orow = (uint16_t *)a.o + b * a.o_sb + (int64_t)(seq0 + my_q) * a.o_st + h * a.o_sh;
+  lds_barrier();
+  {
+    uint16_t *ot = (uint16_t *)smem + (32 * wave + ql) * kFp8OP<D>;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -365,21 +372,51 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdArgs a) {
         uint2 w;
         w.x = pack_bf16x2(acc[db][4 * rb + 0] * inv, acc[db][4 * rb + 1] * inv);
         w.y = pack_bf16x2(acc[db][4 * rb + 2] * inv, acc[db][4 * rb + 3] * inv);
-        *(uint2 *)(orow + db * 32 + 8 * rb + 4 * hf) = w;
+        *(uint2 *)(ot + db * 32 + 8 * rb + 4 * hf) = w;
       }
-    if (hf == 0 && a.lse)
-      a.lse[b * a.lse_sb + h * a.lse_sh + seq0 + my_q] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
   }
+  if (my_q < nq && hf == 0 && a.lse)
+    a.lse[b * a.lse_sb + h * a.lse_sh + seq0 + my_q] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+  lds_barrier();
+  uint16_t *obase = (uint16_t *)a.o + b * a.o_sb + (int64_t)(seq0 + q0) * a.o_st + h * a.o_sh;
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+#pragma unroll
+  for (int i = 0; i < BR * CPR / T; ++i) {
+    const int idx = tid + i * T, row = idx / CPR, ch = idx % CPR;
+    const uint4 v = *(const uint4 *)((const uint16_t *)smem + row * kFp8OP<D> + ch * 8);
+    if (q0 + row < nq) *(uint4 *)(obase + (int64_t)row * a.o_st + ch * 8) = v;
+  }
+}
+
+// Dense calls with at least one unit per CU run persistently (launch_units);
+// the item body is called from one place, on the kernel's by-value arguments.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdArgs a) {
+  const UnitRange r = launch_units(a.persist, a.batch, a.heads, a.nqt, a.causal);
+  for (int u = r.lo; u < r.hi; u += r.step)
+    for (int j = 0; j < 2; ++j) {
+      int b, h, qt;
+      if (!launch_tile(a.persist, r, u, j, a.batch, a.heads, a.nqt, a.cu_seqlens != nullptr, a.causal, false, b, h,
+                       qt))
+        break;
+      fp8_item<D, NW>(a, b, h, qt);
+      lds_barrier();  // the next item stages its tiles into the same LDS
+    }
 }
 
 }  // namespace
 
 hipError_t launch_fwd_fp8(const FwdArgs &a, int head_dim, hipStream_t s) {
-  const dim3 grid((unsigned)(a.nqt * a.heads * a.batch));
+  FwdArgs p = a;
+  dim3 grid((unsigned)(a.nqt * a.heads * a.batch));
+  const int cus = persistent_groups();
+  const int64_t units = (int64_t)a.batch * a.heads * (a.causal ? (a.nqt + 1) / 2 : a.nqt);
+  p.persist = !a.cu_seqlens && cus >= 8 && units >= cus;
+  if (p.persist) grid = dim3((unsigned)cus);
   if (head_dim == 128)
-    hipLaunchKernelGGL((fwd_fp8_kernel<128, 8>), grid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL((fwd_fp8_kernel<128, 8>), grid, dim3(512), 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_fp8_kernel<64, 8>), grid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL((fwd_fp8_kernel<64, 8>), grid, dim3(512), 0, s, p);
   return hipGetLastError();
 }
 

@@ -452,10 +452,6 @@ constexpr int kOP = D + 8;
 // LDS of the ping-pong kernel: the K and V rings, or the staged O tile
 template <int D>
 constexpr int kPPLds = (4 * 64 * D > 256 * kOP<D>) ? 4 * 64 * D : 256 * kOP<D>;
-// Work-group barrier for LDS reuse only: waits for this wave's LDS accesses,
-// not for its global stores to retire (__syncthreads would wait for both).
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 // one (batch or sequence b, head h, query tile qt) work item
 template <int D>
 __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, uint16_t *smem) {

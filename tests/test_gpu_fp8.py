@@ -64,6 +64,29 @@ def test_fp8_n8192_sampled_rows(causal):
     assert_close(o64[0, :, 7], ro, max_abs=FP8_MAX_ABS, mean_abs=None, what="O fp8 full head 7")
 
 
+@pytest.mark.parametrize("b,n,h,d,causal,window", [
+    # >= 256 work units (one per CU): the persistent schedule
+    (2, 1100, 48, 128, True, 0),     # 5 query tiles: the middle one unpaired; ragged tail
+    (2, 1536, 48, 64, True, 300),    # causal + window, d64
+    (1, 1100, 64, 128, False, 0),    # non-causal
+])
+def test_fp8_persistent_schedule_sampled_rows(b, n, h, d, causal, window):
+    print(f"[fp8 persistent] b={b} n={n} h={h} d={d} causal={causal} window={window}", flush=True)
+    q, k, v = dense_inputs(b, n, h, d, "bf16", seed=n + 3 * h)
+    (q8, sq), (k8, sk), (v8, sv) = quantize_e4m3(q), quantize_e4m3(k), quantize_e4m3(v)
+    o, lse = fa_fwd(q8.to(DEV), k8.to(DEV), v8.to(DEV), causal=causal, window=window, descale=(sq, sk, sv))
+    torch.cuda.synchronize()
+    qd, kd, vd = _deq(q8, sq), _deq(k8, sk), _deq(v8, sv)
+    o64, lse64 = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    for bi in range(b):
+        for hh in sorted({0, (h // 2 + 5 * bi) % h, h - 1}):
+            rows = np.union1d(sample_rows(n, 24, seed=bi * 100 + hh), [0, 255, 256, n - 1])
+            ro, rl = oracle.attention_fwd(qd[bi, rows, hh], kd[bi, :, hh], vd[bi, :, hh], 1 / np.sqrt(d), causal, window,
+                                          q_pos=rows, nq=n)
+            assert_close(o64[bi, rows, hh], ro, max_abs=FP8_MAX_ABS, mean_abs=None, what=f"O fp8 batch {bi} head {hh}")
+            assert_lse_close(lse64[bi, hh, rows], rl, tol=2e-3)
+
+
 def test_fp8_causal_row0():
     """Row 0 sees only key 0: P~ = 1 exactly in e4m3, so O_0 = s_v * code(V_0) rounded to bf16."""
     q, k, v = dense_inputs(1, 100, 2, 128, "bf16", seed=5)

@@ -117,7 +117,7 @@ constexpr float kLazy = 8.f;
 // staged one tile ahead of V (LDS rings of two for each).
 // ---------------------------------------------------------------------------
 template <int D, int NW, bool DROP>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
+__device__ __forceinline__ void drop_item(const FwdArgs &a, int b, int h, int qt) {
   constexpr int T = NW * 64, BR = NW * 32;
   using St = KvStage<D, T>;
   constexpr int BC = St::BC, KP = St::KP, VP = St::VP, KS = St::KS, VS = St::VS;
@@ -129,8 +129,6 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int ql = lane & 31, hf = lane >> 5;
   const int vtr_off = (4 * hf + (lane & 15) / 4) * VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  int b, h, qt;
-  decode_item(a, b, h, qt);
   int seq0 = 0, nq = a.nq, nk = a.nk;
   if (a.cu_seqlens) {
     seq0 = a.cu_seqlens[b];
@@ -409,11 +407,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
     pv_prev(vbuf(jt1 - 1));
   }
 
-  // epilogue: O = acc / l (bf16, round to nearest even), LSE = (m + log2 l) ln 2
+  // epilogue: O = acc / l (bf16, round to nearest even), LSE = (m + log2 l) ln 2,
+  // O through LDS (free once every wave is past its last product) as whole rows
   const float lt = half_swap_sum(l);
   const float inv = lt > 0.f ? (DROP ? a.drop_scale : 1.f) / lt : 0.f;
-  if (my_q < nq) {
-    uint16_t *orow = (uint16_t *)a.o + b * a.o_sb + (int64_t)(seq0 + my_q) * a.o_st + h * a.o_sh;
+  constexpr int OP = D + 8;
+  static_assert(BR * OP <= 2 * KS + 2 * VS, "the O tile fits the K/V buffers");
+  lds_barrier();
+  {
+    uint16_t *ot = smem + (32 * wave + ql) * OP;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -421,11 +423,36 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
         uint2 w;
         w.x = pack_bf16x2(acc[db][4 * rb + 0] * inv, acc[db][4 * rb + 1] * inv);
         w.y = pack_bf16x2(acc[db][4 * rb + 2] * inv, acc[db][4 * rb + 3] * inv);
-        *(uint2 *)(orow + db * 32 + 8 * rb + 4 * hf) = w;
+        *(uint2 *)(ot + db * 32 + 8 * rb + 4 * hf) = w;
       }
-    if (hf == 0 && a.lse)
-      a.lse[b * a.lse_sb + h * a.lse_sh + seq0 + my_q] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
   }
+  if (my_q < nq && hf == 0 && a.lse)
+    a.lse[b * a.lse_sb + h * a.lse_sh + seq0 + my_q] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+  lds_barrier();
+  uint16_t *obase = (uint16_t *)a.o + b * a.o_sb + (int64_t)(seq0 + q0) * a.o_st + h * a.o_sh;
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+#pragma unroll
+  for (int i = 0; i < BR * CPR / T; ++i) {
+    const int idx = tid + i * T, row = idx / CPR, ch = idx % CPR;
+    const uint4 v = *(const uint4 *)(smem + row * OP + ch * 8);
+    if (q0 + row < nq) *(uint4 *)(obase + (int64_t)row * a.o_st + ch * 8) = v;
+  }
+}
+
+// Calls with dropout; dense ones with at least one unit per CU run
+// persistently on the schedule of launch_units.
+template <int D, int NW, bool DROP>
+__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
+  const UnitRange r = launch_units(a.persist, a.batch, a.heads, a.nqt, a.causal);
+  for (int u = r.lo; u < r.hi; u += r.step)
+    for (int j = 0; j < 2; ++j) {
+      int b, h, qt;
+      if (!launch_tile(a.persist, r, u, j, a.batch, a.heads, a.nqt, a.cu_seqlens != nullptr, a.causal, false, b, h,
+                       qt))
+        break;
+      drop_item<D, NW, DROP>(a, b, h, qt);
+      lds_barrier();  // the next item stages its tiles into the same LDS
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -745,39 +772,22 @@ __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, 
   }
 }
 
-// Dense calls with at least one unit per work-group run persistently: the
-// grid is a multiple of 8 (one work-group per CU), XCD x = blockIdx % 8 owns
-// the contiguous unit range [x U / 8, (x + 1) U / 8) (a few heads, so their
-// K/V stay in its L2), and its work-groups take every (G / 8)-th unit of it.
-// Under a causal mask a unit pairs query tiles nqt - 1 - i and i, so every
-// unit carries the same number of key tiles; otherwise a unit is one tile.
-// A static schedule has no dispatch gaps between work items (the hardware
-// hands out work-groups in block order over the XCDs, so a CU that frees up
-// early can idle until the next block's XCD has room).
+// Dense calls with at least one unit per CU run persistently on the static
+// schedule of launch_units (paired causal query tiles, XCD-contiguous heads);
+// the item body is called from one place, on the kernel's by-value arguments.
 template <int D>
 __global__ __launch_bounds__(512, 2) void fwd_bf16_pp_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[kPPLds<D>];  // K ring, V ring / staged O
-  if (!a.persist) {
-    int b, h, qt;
-    decode_item(a, b, h, qt);
-    pp_item<D>(a, b, h, qt, smem);
-    return;
-  }
-  const int per = a.causal ? (a.nqt + 1) / 2 : a.nqt;  // units per (batch, head)
-  const int units = a.batch * a.heads * per;
-  const int xcd = blockIdx.x % 8, nx = gridDim.x / 8;
-  const int lo = (int)((int64_t)units * xcd / 8), hi = (int)((int64_t)units * (xcd + 1) / 8);
-  for (int u = lo + (int)(blockIdx.x / 8); u < hi; u += nx) {
-    const int bh = u / per, i = u % per;
-    const int b = bh / a.heads, h = bh % a.heads;
-    const int qt = a.causal ? a.nqt - 1 - i : i;
-    pp_item<D>(a, b, h, qt, smem);
-    lds_barrier();  // the next item's DMA reuses the LDS that the epilogue read
-    if (a.causal && i != qt) {
-      pp_item<D>(a, b, h, i, smem);
-      lds_barrier();
+  const UnitRange r = launch_units(a.persist, a.batch, a.heads, a.nqt, a.causal);
+  for (int u = r.lo; u < r.hi; u += r.step)
+    for (int j = 0; j < 2; ++j) {
+      int b, h, qt;
+      if (!launch_tile(a.persist, r, u, j, a.batch, a.heads, a.nqt, a.cu_seqlens != nullptr, a.causal, false, b, h,
+                       qt))
+        break;
+      pp_item<D>(a, b, h, qt, smem);
+      lds_barrier();  // the next item's DMA reuses the LDS that the epilogue read
     }
-  }
 }
 
 // fp32 forward (small workloads): 4 waves x 16 query rows; a query's dot
@@ -899,17 +909,16 @@ int fwd_block_rows(int qkv_dtype, int head_dim) {
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, int head_dim, hipStream_t s) {
-  const dim3 grid((unsigned)(a.nqt * a.heads * a.batch));
+  FwdArgs p = a;
+  dim3 g((unsigned)(a.nqt * a.heads * a.batch));
+  const int cus = persistent_groups();
+  const int64_t units = (int64_t)a.batch * a.heads * (a.causal ? (a.nqt + 1) / 2 : a.nqt);
+  p.persist = !a.cu_seqlens && cus >= 8 && units >= cus;
+  if (p.persist) g = dim3((unsigned)cus);
   if (a.drop_k) {
-    if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_kernel<128, 8, true>), grid, dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((fwd_bf16_kernel<64, 8, true>), grid, dim3(512), 0, s, a);
+    if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_kernel<128, 8, true>), g, dim3(512), 0, s, p);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<64, 8, true>), g, dim3(512), 0, s, p);
   } else {
-    FwdArgs p = a;
-    dim3 g = grid;
-    const int cus = persistent_groups();
-    const int64_t units = (int64_t)a.batch * a.heads * (a.causal ? (a.nqt + 1) / 2 : a.nqt);
-    p.persist = !a.cu_seqlens && cus >= 8 && units >= cus;
-    if (p.persist) g = dim3((unsigned)cus);
     if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_pp_kernel<128>), g, dim3(512), 0, s, p);
     else hipLaunchKernelGGL((fwd_bf16_pp_kernel<64>), g, dim3(512), 0, s, p);
   }

@@ -107,6 +107,37 @@ def test_dropout_random_inputs(b, nq, nk, h, d, causal, window, p):
     assert_close(f64(dv), rv, what="dV")
 
 
+def test_dropout_persistent_schedule():
+    """B2 N1100 H48 d64 causal, p = 0.1: enough work units that the forward
+    and the dQ kernel run their persistent schedules (5 query tiles, the
+    middle one unpaired).  Sampled forward rows and whole-head gradients of
+    a few (batch, head) slots against the oracle's own Philox mask."""
+    b, n, h, d, p = 2, 1100, 48, 64, 0.1
+    q, k, v, do = dense_inputs(b, n, h, d, "bf16", seed=55, with_dout=True)
+    seed, off = 909, 3
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    o, lse = fa_fwd(qd, kd, vd, causal=True, dropout_p=p, seed=seed, offset=off)
+    dq, dk, dv = fa_bwd(dod, qd, kd, vd, o, lse, causal=True, dropout_p=p, seed=seed, offset=off)
+    torch.cuda.synchronize()
+    q64, k64, v64, do64 = f64(q), f64(k), f64(v), f64(do)
+    o64, l64, dq64, dk64, dv64 = f64(o), f64(lse), f64(dq), f64(dk), f64(dv)
+    sc = 1 / np.sqrt(d)
+    for bi, hh in ((0, 0), (0, 29), (1, 7), (1, h - 1)):
+        slot = bi * h + hh
+        rows = np.union1d(sample_rows(n, 32, seed=slot), [255, 256, 1023, 1024])
+        drop = oracle.dropout_keep(slot, rows, n, seed, off, p)
+        ro, rl = oracle.attention_fwd(q64[bi, rows, hh], k64[bi, :, hh], v64[bi, :, hh], sc, True, 0, q_pos=rows, nq=n,
+                                      drop=drop)
+        assert_close(o64[bi, rows, hh], ro, what=f"O slot {slot}")
+        assert_lse_close(l64[bi, hh, rows], rl)
+        drop = oracle.dropout_keep(slot, range(n), n, seed, off, p)
+        rq, rk, rv = oracle.attention_bwd(q64[bi, :, hh], k64[bi, :, hh], v64[bi, :, hh], do64[bi, :, hh], sc, True, 0,
+                                          drop=drop)
+        assert_close(dq64[bi, :, hh], rq, what=f"dQ slot {slot}")
+        assert_close(dk64[bi, :, hh], rk, what=f"dK slot {slot}")
+        assert_close(dv64[bi, :, hh], rv, what=f"dV slot {slot}")
+
+
 def test_dropout_varlen():
     lengths = [300, 1, 77, 513, 0]
     q, k, v, cu, do = varlen_inputs(lengths, 2, 128, "bf16", seed=31, with_dout=True)

@@ -775,9 +775,77 @@ __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, 
 // Dense calls with at least one unit per CU run persistently on the static
 // schedule of launch_units (paired causal query tiles, XCD-contiguous heads);
 // the item body is called from one place, on the kernel's by-value arguments.
+// Packed varlen calls with up to kVarlenSeqs sequences run persistently
+// too.  The host does not know the sequence lengths, so every work-group
+// derives the same schedule from cu_seqlens: units are (sequence, head, one
+// query tile, or a causal pair nqt_s - 1 - i, i when there is no window),
+// sequences ranked longest first, heavy tiles first within a sequence; unit k goes to slot k mod 2G, or 2G - 1 - (k mod 2G) on the way back
+// (a snake over decreasing unit sizes, close to longest-processing-time
+// first), and slots are numbered XCD-major so that consecutive units of one
+// (sequence, head) share an XCD's L2.
+constexpr int kVarlenSeqs = 512;
+template <int D>
+__device__ __forceinline__ void pp_varlen_persistent(const FwdArgs &a, uint16_t *smem) {
+  __shared__ int s_key[kVarlenSeqs];        // query tiles of sequence i
+  __shared__ int s_order[kVarlenSeqs];      // sequences, longest first
+  __shared__ int s_first[kVarlenSeqs + 1];  // first unit of each ranked sequence
+  const int nseq = a.batch, tid = threadIdx.x;
+  // a causal pair (nqt - 1 - i, i) carries as much work as any other pair of
+  // its sequence only without a window; with one, units are single tiles
+  const bool pair = a.causal && a.window <= 0;
+  // (a decreasing cu_seqlens gives a sequence no units, as the item itself would skip it)
+  for (int i = tid; i < nseq; i += blockDim.x) s_key[i] = max(0, a.cu_seqlens[i + 1] - a.cu_seqlens[i] + 255) / 256;
+  __syncthreads();
+  for (int i = tid; i < nseq; i += blockDim.x) {
+    const int ki = s_key[i];
+    int rank = 0;
+    for (int j = 0; j < nseq; ++j) {
+      const int kj = s_key[j];
+      rank += kj > ki || (kj == ki && j < i);
+    }
+    s_order[rank] = i;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int r = 0; r < nseq; ++r) {
+      s_first[r] = acc;
+      const int nt = s_key[s_order[r]];
+      acc += a.heads * (pair ? (nt + 1) / 2 : nt);
+    }
+    s_first[nseq] = acc;
+  }
+  __syncthreads();
+  const int units = s_first[nseq], G = gridDim.x;
+  const int slot = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+  // e / 2: the outward or the return slot of this lap; e % 2: the tile of a pair
+  for (int k0 = 0; k0 < units; k0 += 2 * G)
+    for (int e = 0; e < 4; ++e) {
+      const int k = k0 + ((e >> 1) == 0 ? slot : 2 * G - 1 - slot);
+      if (k >= units) continue;
+      int lo = 0, hi = nseq;  // the ranked sequence r with s_first[r] <= k < s_first[r + 1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_first[mid] <= k) lo = mid;
+        else hi = mid;
+      }
+      const int sq = s_order[lo], nt = s_key[sq];
+      const int per = pair ? (nt + 1) / 2 : nt;
+      const int local = k - s_first[lo], h = local / per, i = local % per;
+      const int heavy = a.causal ? nt - 1 - i : i;  // high query tiles first under a causal mask
+      if ((e & 1) && (!pair || heavy == i)) continue;  // no second tile in this unit
+      pp_item<D>(a, sq, h, (e & 1) ? i : heavy, smem);
+      lds_barrier();  // the next item's DMA reuses the LDS that the epilogue read
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(512, 2) void fwd_bf16_pp_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[kPPLds<D>];  // K ring, V ring / staged O
+  if (a.persist == 2) {
+    pp_varlen_persistent<D>(a, smem);
+    return;
+  }
   const UnitRange r = launch_units(a.persist, a.batch, a.heads, a.nqt, a.causal);
   for (int u = r.lo; u < r.hi; u += r.step)
     for (int j = 0; j < 2; ++j) {
@@ -919,6 +987,11 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, int head_dim, hipStream_t s) {
     if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_kernel<128, 8, true>), g, dim3(512), 0, s, p);
     else hipLaunchKernelGGL((fwd_bf16_kernel<64, 8, true>), g, dim3(512), 0, s, p);
   } else {
+    // packed calls: persistent with a schedule derived on the device
+    if (a.cu_seqlens && cus >= 8 && a.batch <= kVarlenSeqs) {
+      p.persist = 2;
+      g = dim3((unsigned)cus);
+    }
     if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_pp_kernel<128>), g, dim3(512), 0, s, p);
     else hipLaunchKernelGGL((fwd_bf16_pp_kernel<64>), g, dim3(512), 0, s, p);
   }

@@ -29,7 +29,7 @@ struct FwdArgs {
   // kept probabilities scaled by drop_scale = 256 / drop_k
   uint32_t drop_k, seed_lo, seed_hi, drop_offset;
   float drop_scale;
-  int32_t persist;               // bf16 forward: persistent launch over a static schedule (set by the launcher)
+  int32_t persist;               // persistent launch (set by the launcher): 1 dense schedule, 2 packed varlen schedule
 };
 
 // Kernel-side view of one backward call.  Packed varlen calls set

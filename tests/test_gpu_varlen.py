@@ -37,6 +37,19 @@ def test_varlen_small_elementwise(lengths, h, d, causal, window, dt):
     assert_lse_close(f64(lse), rl)
 
 
+def test_varlen_many_sequences_elementwise():
+    """600 short sequences (more than one packed call schedules on the device,
+    so the one-item-per-work-group launch runs), some empty, causal and not."""
+    rng = np.random.default_rng(600)
+    lengths = [int(x) for x in rng.integers(0, 40, size=600)]
+    q, k, v, cu = varlen_inputs(lengths, 2, 64, "bf16", seed=600)
+    for causal in (True, False):
+        o, lse = _run(q, k, v, cu, causal, 0)
+        ro, rl = oracle.varlen_fwd(f64(q), f64(k), f64(v), cu.numpy(), 1 / np.sqrt(64), causal, 0)
+        assert_close(f64(o), ro, what=f"O causal={causal}")
+        assert_lse_close(f64(lse), rl)
+
+
 def test_varlen_equals_dense_per_sequence_bitwise():
     lengths = [300, 1, 513, 64]
     q, k, v, cu = varlen_inputs(lengths, 4, 128, "bf16", seed=9)

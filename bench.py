@@ -384,7 +384,8 @@ def main():
         torch.cuda.synchronize()
         log("[bench] calibration copy of 1 GiB done")
 
-    sha = src_hash(src)
+    # the kernel's code depends on its source file and the shared device headers
+    sha = src_hash(src, "fa_device.h", "fa_internal.h")
     rows = {} if (args.no_rows or not headline) else extra_rows(torch, fa, max(5, min(args.steps, 20)))
     if rows:
         log(f"[bench] rows: {json.dumps(rows)}")

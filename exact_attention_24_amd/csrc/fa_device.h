@@ -129,7 +129,16 @@ __device__ __forceinline__ void dma16(i32x4 r, const uint16_t *lds_wave, uint32_
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait for this wave's LDS DMA.  The builtin (not inline asm) lets the
+// compiler's own load tracking see every vector load complete here: with an
+// asm wait, register loads issued before it (the Q fragments) stayed
+// "pending" in that tracking across the main loop, and the compiler waited
+// for them inside the loop, which at run time also waited for the DMA of the
+// next tiles in flight.  The empty asm keeps LDS reads from moving above it.
+__device__ __forceinline__ void wait_dma() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0; expcnt, lgkmcnt unchanged (7, 15)
+  asm volatile("" ::: "memory");
+}
 // same, with the wave-uniform LDS byte address given directly
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"

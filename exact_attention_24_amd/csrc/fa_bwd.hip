@@ -507,7 +507,6 @@ __device__ __forceinline__ void dq_item(const BwdArgs &a, int b, int h, int qt) 
   constexpr int DCH = D / 8, TS = BC * D;
   constexpr int PER = BC * DCH / T;  // DMA loads per lane per tile and tensor
   constexpr int NK = D / 16;         // d-steps of S and dP (fragments per sub-tile and tensor)
-  constexpr int NA = 2 * NK;         // phase-A fragments per sub-tile (K, V interleaved)
   constexpr int NF = (D / 32) * 2;   // phase-B K^T fragments per sub-tile
   constexpr int RING = 6;
   __shared__ __attribute__((aligned(16))) uint16_t smem[6 * TS];  // K x3, V x3

@@ -47,17 +47,6 @@ __device__ __forceinline__ uint32_t u16_at(const uint4 &v, int e) {
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
-// Position of row group g (4 consecutive rows of a tile) inside a transposed
-// tile that serves as the A operand of a product whose B operand comes
-// straight from a 32x32 MFMA accumulator: within each group of 16 rows the
-// accumulator lists rows 0-3, 8-11 for lanes 0-31 and rows 4-7, 12-15 for
-// lanes 32-63, so groups 1 and 2 trade places.
-__device__ __forceinline__ int vt_group_pos(int g) {
-  const int gi = g & 3;
-  const int sw = gi == 1 ? 2 : gi == 2 ? 1 : gi;
-  return (g >> 2) * 16 + sw * 4;
-}
-
 // Combine a per-lane value with the one in lane l ^ 32 (the other half of a
 // 32x32 accumulator column): v_permlane32_swap exchanges the halves, and the
 // pair {own, other} comes back in some order, which max and + ignore.
@@ -110,25 +99,13 @@ __device__ __forceinline__ int tr_off(int lane, int db, int half) {
   return swz_off<D>(row, chunk) + 4 * (lane & 1);
 }
 
-// LDS DMA of 16 bytes per lane: the 16 bytes at byte offset `off` of the
-// buffer described by `r` land at lds_wave + 16 * lane (lds_wave must be
-// wave-uniform); offsets past the end of the buffer deliver zeros.  Issued
-// from inline assembly so the compiler does not wait for its completion
-// before unrelated LDS reads; callers wait with wait_dma() and a barrier
-// before anything reads the destination.
+// Buffer resource words for LDS DMA: `bytes` bytes from `base`, raw
+// (stride 0), so offsets at or past `bytes` read as zeros.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4 buffer_words(const void *base, uint32_t bytes) {
   const uint64_t p = (uint64_t)base;
   return (i32x4){(int)(uint32_t)p, (int)((p >> 32) & 0xffff), (int)bytes, 0x00020000};
 }
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(i32x4 r, const uint16_t *lds_wave, uint32_t off) {
-  const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t *)lds_wave;
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(off), "s"(r)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
 // Wait for this wave's LDS DMA.  The builtin (not inline asm) lets the
 // compiler's own load tracking see every vector load complete here: with an
 // asm wait, register loads issued before it (the Q fragments) stayed
@@ -139,7 +116,12 @@ __device__ __forceinline__ void wait_dma() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0; expcnt, lgkmcnt unchanged (7, 15)
   asm volatile("" ::: "memory");
 }
-// same, with the wave-uniform LDS byte address given directly
+// LDS DMA of 16 bytes per lane: the 16 bytes at byte offset `off` of the
+// buffer described by `r` land at LDS byte address lds_byte + 16 * lane
+// (lds_byte must be wave-uniform); offsets past the end of the buffer
+// deliver zeros.  Issued from inline assembly so the compiler does not wait
+// for its completion before unrelated LDS reads; callers wait with
+// wait_dma() and a barrier before anything reads the destination.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16_at(i32x4 r, uint32_t lds_byte, uint32_t off) {
@@ -173,7 +155,6 @@ __device__ __forceinline__ void mfma_drain2_v(f32x16 &x, f32x16 &y) {
   asm volatile("s_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
 }
 __device__ __forceinline__ void mfma_drain_a(f32x16 &x) { asm volatile("s_nop 7\n\ts_nop 7" : "+a"(x)); }
-__device__ __forceinline__ void valu_to_mfma_a(f32x16 &x) { asm volatile("s_nop 1" : "+a"(x)); }
 
 // XCD-aware renumbering of the linear block id: the hardware hands
 // consecutive block ids to the 8 XCDs in turn, so XCD x sees ids x, x+8, ...;
@@ -255,20 +236,6 @@ __device__ __forceinline__ bool launch_tile(bool persist, const UnitRange &r, in
 // Work-group barrier for LDS reuse only: waits for this wave's LDS accesses,
 // not for its global stores to retire (__syncthreads would wait for both).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Write a unit of 4 rows x 8 bf16 columns (r[i] = row i) transposed: column
-// `col0 + e` gets the 4 values at positions pos..pos+3 of its row (pitch
-// `pitch` elements) in the tile at `t`.
-__device__ __forceinline__ void store_transposed_4x8(uint16_t *t, int pitch, int col0, int pos,
-                                                     const uint4 (&r)[4]) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    uint2 w;
-    w.x = u16_at(r[0], e) | (u16_at(r[1], e) << 16);
-    w.y = u16_at(r[2], e) | (u16_at(r[3], e) << 16);
-    *(uint2 *)(t + (col0 + e) * pitch + pos) = w;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Dropout randomness: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel

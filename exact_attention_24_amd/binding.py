@@ -191,6 +191,19 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _same_gpu(ref, **tensors):
+    """Every tensor the kernels read or write must live on ref's GPU: a host
+    pointer handed to a kernel would fault the device, not raise.  Checked by
+    each launching entry point before anything is allocated or launched (the
+    make_*_params builders stay usable on host tensors, for the host-only
+    fa_check_* validators)."""
+    if not ref.is_cuda:
+        raise ValueError(f"tensors must be on a GPU (got {ref.device})")
+    for name, t in tensors.items():
+        if t is not None and (not t.is_cuda or t.device != ref.device):
+            raise ValueError(f"{name} must be on {ref.device} (got {t.device})")
+
+
 def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
@@ -267,6 +280,7 @@ def fa_fwd(q, k, v, causal=False, window=0, softmax_scale=None, out=None, lse=No
     if lse is None and return_lse:
         lse = torch.empty((b, h, nq), dtype=torch.float32, device=q.device)
     p = make_fwd_params(q, k, v, out, lse, causal, window, softmax_scale, descale, dropout_p, seed, offset)
+    _same_gpu(q, k=k, v=v, out=out, lse=lse)
     _raise(lib().fa_fwd(ctypes.byref(p), _stream()))
     return (out, lse) if return_lse else out
 
@@ -317,6 +331,7 @@ def fa_varlen_fwd(q, k, v, cu_seqlens, max_seqlen, causal=False, window=0, softm
         lse = torch.empty((h, total), dtype=torch.float32, device=q.device)
     p = make_varlen_params(q, k, v, out, lse, cu_seqlens, max_seqlen, causal, window, softmax_scale, descale,
                            dropout_p, seed, offset)
+    _same_gpu(q, k=k, v=v, out=out, lse=lse, cu_seqlens=cu_seqlens)
     _raise(lib().fa_varlen_fwd(ctypes.byref(p), _stream()))
     return (out, lse) if return_lse else out
 
@@ -371,6 +386,7 @@ def fa_bwd(dout, q, k, v, o, lse, causal=False, window=0, softmax_scale=None, de
         dv = torch.empty(v.shape, dtype=grad_dtype, device=q.device)
     p = make_bwd_params(dout, q, k, v, o, lse, dq, dk, dv, causal, window, softmax_scale, deterministic,
                         dropout_p, seed, offset)
+    _same_gpu(q, k=k, v=v, o=o, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv)
     _raise(lib().fa_check_bwd(ctypes.byref(p)))
     nbytes = fa_bwd_workspace_bytes(p)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
@@ -431,6 +447,7 @@ def fa_varlen_bwd(dout, q, k, v, o, lse, cu_seqlens, max_seqlen, causal=False, w
         dv = torch.empty(v.shape, dtype=grad_dtype, device=q.device)
     p = make_varlen_bwd_params(dout, q, k, v, o, lse, dq, dk, dv, cu_seqlens, max_seqlen, causal, window,
                                softmax_scale, deterministic, dropout_p, seed, offset)
+    _same_gpu(q, k=k, v=v, o=o, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv, cu_seqlens=cu_seqlens)
     _raise(lib().fa_check_varlen_bwd(ctypes.byref(p)))
     nbytes = fa_varlen_bwd_workspace_bytes(p)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
@@ -476,6 +493,7 @@ def fa_merge(o_parts, lse_parts, out=None, lse=None, out_dtype=None, return_lse=
     if lse is None and return_lse:
         lse = torch.empty((b, h, n), dtype=torch.float32, device=o_parts.device)
     p = make_merge_params(o_parts, lse_parts, out, lse)
+    _same_gpu(o_parts, lse_parts=lse_parts, out=out, lse=lse)
     _raise(lib().fa_merge(ctypes.byref(p), _stream()))
     return (out, lse) if return_lse else out
 
@@ -562,6 +580,8 @@ def fa_fwd_kvcache(q, k_cache, v_cache, k=None, v=None, cache_seqlens=0, causal=
         lse = torch.empty((b, h, nq), dtype=torch.float32, device=q.device)
     p = make_kvcache_params(q, k_cache, v_cache, k, v, cache_seqlens, out, lse, causal, window, softmax_scale,
                             num_splits, block_table)
+    _same_gpu(q, k_cache=k_cache, v_cache=v_cache, k=k, v=v, cache_seqlens=cache_seqlens, out=out, lse=lse,
+              block_table=block_table)
     _raise(lib().fa_check_kvcache(ctypes.byref(p)))
     nbytes = fa_kvcache_workspace_bytes(p)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)

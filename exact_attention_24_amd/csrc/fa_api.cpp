@@ -145,6 +145,12 @@ fa_status check_dropout(float p, fa_dtype qkv) {
   return FA_OK;
 }
 
+// Lazy running max of the forward kernels: 8 (log2 units), or exact where
+// every row sees at most 64 keys (causal mask with a window of at most 64):
+// the weights of such rows can sit on a few keys, whose unnormalised
+// probabilities are then kept at 1 rather than rounded from up to 2^8.
+float lazy_threshold(int causal, int window) { return causal && window > 0 && window <= 64 ? 0.f : 8.f; }
+
 template <class Args>
 void set_dropout(Args &a, float p, uint64_t seed, uint32_t offset) {
   const long kthr = std::max(1L, std::lround(256.0 * (1.0 - (double)p)));
@@ -275,7 +281,9 @@ fa_status fa_check_bwd(const fa_bwd_params *p) {
   if ((st = check_tensor("dk", p->dk, p->dk_stride, 3, gb, k_empty, nk, hd)) != FA_OK) return st;
   if ((st = check_tensor("dv", p->dv, p->dv_stride, 3, gb, k_empty, nk, hd)) != FA_OK) return st;
   if (!q_empty && !p->lse) return fail(FA_ERR_INVALID_ARGUMENT, "lse is NULL");
-  if (ceil_div(std::max(nq, nk), 128) * (int64_t)p->heads * p->batch > INT32_MAX)
+  if (ceil_div(std::max(nq, nk), 128) * (int64_t)p->heads * p->batch > INT32_MAX ||
+      (fa::bwd_band(p->causal, p->window) &&
+       ceil_div(std::max(nq, nk), 32) * (int64_t)p->heads * p->batch * 256 > (int64_t)UINT32_MAX))
     return fail(FA_ERR_INVALID_ARGUMENT, "problem too large for one launch");
   return ok();
 }
@@ -305,7 +313,9 @@ fa_status fa_check_varlen_bwd(const fa_varlen_bwd_params *p) {
   if ((st = check_tensor("dk", p->dk, p->dk_stride, 2, gb, empty, tt, hd)) != FA_OK) return st;
   if ((st = check_tensor("dv", p->dv, p->dv_stride, 2, gb, empty, tt, hd)) != FA_OK) return st;
   if (!empty && !p->lse) return fail(FA_ERR_INVALID_ARGUMENT, "lse is NULL");
-  if (ceil_div(p->max_seqlen, 128) * (int64_t)p->heads * p->num_seqs > INT32_MAX)
+  if (ceil_div(p->max_seqlen, 128) * (int64_t)p->heads * p->num_seqs > INT32_MAX ||
+      (fa::bwd_band(p->causal, p->window) &&
+       ceil_div(p->max_seqlen, 32) * (int64_t)p->heads * p->num_seqs * 256 > (int64_t)UINT32_MAX))
     return fail(FA_ERR_INVALID_ARGUMENT, "problem too large for one launch");
   return ok();
 }
@@ -327,6 +337,7 @@ fa_status fa_fwd(const fa_fwd_params *p, void *stream) {
   a.causal = p->causal; a.window = p->window;
   a.scale_log2 = p->softmax_scale * kLog2e * p->q_descale * p->k_descale;
   a.v_descale = p->v_descale;
+  a.lazy = lazy_threshold(p->causal, p->window);
   set_dropout(a, p->dropout_p, p->dropout_seed, p->dropout_offset);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   switch (p->qkv_dtype) {
@@ -353,6 +364,7 @@ fa_status fa_varlen_fwd(const fa_varlen_fwd_params *p, void *stream) {
   a.causal = p->causal; a.window = p->window;
   a.scale_log2 = p->softmax_scale * kLog2e * p->q_descale * p->k_descale;
   a.v_descale = p->v_descale;
+  a.lazy = lazy_threshold(p->causal, p->window);
   set_dropout(a, p->dropout_p, p->dropout_seed, p->dropout_offset);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   switch (p->qkv_dtype) {

@@ -1071,9 +1071,314 @@ __global__ __launch_bounds__(256) void bwd_start_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 5. Causal mask with a sliding window of at most kBandMax keys: every query
+//    row then sees at most kBandMax keys, all among the kBandMax - 1
+//    positions before it.  Such rows' probabilities can sit on a few keys,
+//    where the bf16 P and dS operands of the MFMA kernels (and a D taken
+//    from the bf16 O) cost most of the accuracy the gradients have elsewhere,
+//    as at the causal start rows.  These calls run two exact fp32 kernels
+//    instead of kernels 1-4:
+//      bwd_band_dq_kernel    32 query rows against the aligned slab of 128
+//                            keys (four 32-key blocks) that holds all their
+//                            visible keys: each row's softmax over its keys,
+//                            D_i = sum_j P_ij dP_ij, dS = P (dP - D), dQ; the
+//                            row's D and log-sum-exp go to the workspace.
+//      bwd_band_dkdv_kernel  32 keys against the 128 query rows from their
+//                            first position on (all rows that can see them):
+//                            P from that log-sum-exp, dS with that D, dK, dV.
+//    S and dP come from MFMA on the bf16 operands (exact products, fp32
+//    sums); everything after them is fp32, and no output is shared between
+//    work-groups.
+// ---------------------------------------------------------------------------
+constexpr int kBandMax = 64;
+constexpr int kBandRows = 32;   // query rows (dQ kernel) or keys (dK/dV kernel) per work-group
+constexpr int kBandSlab = 128;  // keys (dQ kernel) or query rows (dK/dV kernel) staged against them
+
+// bf16 x 4 (8 bytes) to fp32
+__device__ __forceinline__ void band_bf4(uint2 w, float (&x)[4]) {
+  x[0] = bf16_to_f32(w.x & 0xffffu);
+  x[1] = bf16_to_f32(w.x >> 16);
+  x[2] = bf16_to_f32(w.y & 0xffffu);
+  x[3] = bf16_to_f32(w.y >> 16);
+}
+
+// S = A B^T and dP = C E^T of one 32 x 32 block on MFMA: rows 32 ra.. of the
+// row-major LDS tiles a (for S) and c (for dP), columns 32 rb.. from the
+// tiles b and e; results into s_out / dp_out [row][col] (pitch P floats).
+template <int D, int PITCH, int P>
+__device__ __forceinline__ void band_block(const uint16_t *a, const uint16_t *bt, const uint16_t *c,
+                                           const uint16_t *e, int ra, int rb, float *s_out, float *dp_out,
+                                           int lane) {
+  const int l32 = lane & 31, hf = lane >> 5;
+  f32x16 sacc = {}, dacc = {};
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const int col = kk * 16 + hf * 8;
+    sacc = mfma_bf16(*(const uint4 *)(a + (32 * ra + l32) * PITCH + col),
+                     *(const uint4 *)(bt + (32 * rb + l32) * PITCH + col), sacc);
+    dacc = mfma_bf16(*(const uint4 *)(c + (32 * ra + l32) * PITCH + col),
+                     *(const uint4 *)(e + (32 * rb + l32) * PITCH + col), dacc);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 32 * ra + 8 * (i / 4) + 4 * hf + i % 4;
+    s_out[r * P + 32 * rb + l32] = sacc[i];
+    dp_out[r * P + 32 * rb + l32] = dacc[i];
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_band_dq_kernel(BwdArgs a) {
+  constexpr int R = kBandRows, K = kBandSlab, PITCH = D + 8, DCH = D / 8, SP = K + 1;
+  constexpr int G = D / 4, RG = 256 / G, RPT = R / RG;  // dQ: 4 dims x RPT rows per thread
+  static_assert(RPT * RG == R, "row split");
+  __shared__ __attribute__((aligned(16))) uint16_t qs[R * PITCH], dos[R * PITCH], ks[K * PITCH], vs[K * PITCH];
+  __shared__ float ss[R * SP], dps[R * SP];  // S; dP then dS
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nqt = (a.nq + R - 1) / R;
+  const int qt = blockIdx.x % nqt, bh = blockIdx.x / nqt;
+  const int b = bh / a.heads, h = bh % a.heads;
+  int seq0 = 0, nq = a.nq, nk = a.nk;
+  if (a.cu_seqlens) {
+    seq0 = a.cu_seqlens[b];
+    nq = nk = a.cu_seqlens[b + 1] - seq0;
+  }
+  const int q0 = qt * R;
+  if (q0 >= nq) return;  // uniform
+  const int off = nk - nq, window = a.window;
+  const int p0 = q0 + off;                   // key position of row q0
+  const int ks0 = (p0 - (kBandMax - 1)) & ~31;  // slab [ks0, ks0 + K): 32-aligned, holds [p0 - 63, p0 + 31]
+  const float scale = a.scale;
+
+  const uint16_t *qg = (const uint16_t *)a.q + b * a.q_sb + (int64_t)seq0 * a.q_st + h * a.q_sh;
+  const uint16_t *dog = (const uint16_t *)a.dout + b * a.do_sb + (int64_t)seq0 * a.do_st + h * a.do_sh;
+  const uint16_t *kg = (const uint16_t *)a.k + b * a.k_sb + (int64_t)seq0 * a.k_st + h * a.k_sh;
+  const uint16_t *vg = (const uint16_t *)a.v + b * a.v_sb + (int64_t)seq0 * a.v_st + h * a.v_sh;
+  for (int idx = tid; idx < R * DCH; idx += 256) {
+    const int r = idx / DCH, ch = idx % DCH;
+    uint4 q4 = {0u, 0u, 0u, 0u}, o4 = q4;
+    if (q0 + r < nq) {
+      q4 = *(const uint4 *)(qg + (int64_t)(q0 + r) * a.q_st + ch * 8);
+      o4 = *(const uint4 *)(dog + (int64_t)(q0 + r) * a.do_st + ch * 8);
+    }
+    *(uint4 *)(qs + r * PITCH + ch * 8) = q4;
+    *(uint4 *)(dos + r * PITCH + ch * 8) = o4;
+  }
+  for (int idx = tid; idx < K * DCH; idx += 256) {
+    const int c = idx / DCH, ch = idx % DCH, j = ks0 + c;
+    uint4 k4 = {0u, 0u, 0u, 0u}, v4 = k4;
+    if (j >= 0 && j < nk) {
+      k4 = *(const uint4 *)(kg + (int64_t)j * a.k_st + ch * 8);
+      v4 = *(const uint4 *)(vg + (int64_t)j * a.v_st + ch * 8);
+    }
+    *(uint4 *)(ks + c * PITCH + ch * 8) = k4;
+    *(uint4 *)(vs + c * PITCH + ch * 8) = v4;
+  }
+  __syncthreads();
+  // wave w: rows 0..31 against keys 32 w..32 w + 31
+  band_block<D, PITCH, SP>(qs, ks, dos, vs, 0, wave, ss, dps, lane);
+  __syncthreads();
+
+  // row r, Philox call `call` of it: the 16 keys 32 kb + 8 (e / 4) + 4 hq + e % 4
+  // (e < 16) of slab block kb, whose random bytes that one call gives
+  {
+    const int r = tid >> 3, call = tid & 7, kb = call >> 1, hq = call & 1;
+    const int q = q0 + r, p = q + off;
+    const bool row_ok = q < nq;
+    float sv[16], dp[16], kf[16];
+    float m = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int c = 32 * kb + 8 * (e >> 2) + 4 * hq + (e & 3), j = ks0 + c;
+      const bool vis = row_ok && j >= 0 && j < nk && j <= p && j > p - window;
+      sv[e] = vis ? ss[r * SP + c] * scale : -INFINITY;
+      dp[e] = dps[r * SP + c];
+      kf[e] = 1.f;
+      m = fmaxf(m, sv[e]);
+    }
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    m = fmaxf(m, __shfl_xor(m, 4));
+    float l = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      sv[e] = sv[e] == -INFINITY ? 0.f : expf(sv[e] - m);
+      l += sv[e];
+    }
+    l += __shfl_xor(l, 1);
+    l += __shfl_xor(l, 2);
+    l += __shfl_xor(l, 4);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    if (a.drop_k && row_ok) {
+      const uint32_t kbg = (uint32_t)((ks0 >> 5) + kb);  // global 32-key block (used only where keys exist)
+      const Philox x = philox10(2u * kbg + (uint32_t)hq, (uint32_t)q, (uint32_t)(b * a.heads + h), a.drop_offset,
+                                a.seed_lo, a.seed_hi);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) kf[e] = drop_keep(x, e, a.drop_k) ? a.drop_scale : 0.f;
+    }
+    float dd = 0.f;  // D = sum_j P_j kf_j dP_j
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      sv[e] *= inv;
+      dd = __builtin_fmaf(sv[e] * kf[e], dp[e], dd);
+    }
+    dd += __shfl_xor(dd, 1);
+    dd += __shfl_xor(dd, 2);
+    dd += __shfl_xor(dd, 4);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int c = 32 * kb + 8 * (e >> 2) + 4 * hq + (e & 3);
+      dps[r * SP + c] = sv[e] * __builtin_fmaf(kf[e], dp[e], -dd);  // 0 where P = 0
+    }
+    if (row_ok && call == 0) {
+      const int64_t lr = b * a.lse_sb + h * a.lse_sh + seq0 + q;
+      a.dpsum[lr] = dd;
+      a.lse2[lr] = l > 0.f ? m + logf(l) : INFINITY;  // natural log of the scaled scores' exponent sum
+    }
+  }
+  __syncthreads();
+
+  // dQ = scale dS K over the keys any of the rows can see
+  const int c_lo = max(0, p0 - window + 1 - ks0), c_hi = min(K, p0 + R - ks0);
+  const int d0 = 4 * (tid % G), tg = tid / G;
+  float acc[RPT][4] = {};
+  for (int c = c_lo; c < c_hi; ++c) {
+    float kx[4];
+    band_bf4(*(const uint2 *)(ks + c * PITCH + d0), kx);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const float ds = dps[(tg + RG * i) * SP + c];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) acc[i][x] = __builtin_fmaf(ds, kx[x], acc[i][x]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int q = q0 + tg + RG * i;
+    if (q < nq)
+      store_grad4(a.dq, b * a.dq_sb + (int64_t)(seq0 + q) * a.dq_st + h * a.dq_sh + d0, a.grad_f32,
+                  scale * acc[i][0], scale * acc[i][1], scale * acc[i][2], scale * acc[i][3]);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_band_dkdv_kernel(BwdArgs a) {
+  constexpr int KB = kBandRows, RS = kBandSlab, PITCH = D + 8, DCH = D / 8, SP = KB + 1;
+  constexpr int G = D / 4, KG = 256 / G, KPT = KB / KG;  // dK, dV: 4 dims x KPT keys per thread
+  static_assert(KPT * KG == KB, "key split");
+  __shared__ __attribute__((aligned(16))) uint16_t ks[KB * PITCH], vs[KB * PITCH], qs[RS * PITCH], dos[RS * PITCH];
+  __shared__ float ss[RS * SP], dps[RS * SP];  // S then P kf; dP then dS
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nkt = (a.nk + KB - 1) / KB;
+  const int kt = blockIdx.x % nkt, bh = blockIdx.x / nkt;
+  const int b = bh / a.heads, h = bh % a.heads;
+  int seq0 = 0, nq = a.nq, nk = a.nk;
+  if (a.cu_seqlens) {
+    seq0 = a.cu_seqlens[b];
+    nq = nk = a.cu_seqlens[b + 1] - seq0;
+  }
+  const int k0 = kt * KB;
+  if (k0 >= nk) return;  // uniform
+  const int off = nk - nq, window = a.window;
+  const int qr0 = k0 - off;  // query row at key position k0: slab rows qr0 .. qr0 + RS - 1
+  const float scale = a.scale;
+
+  const uint16_t *qg = (const uint16_t *)a.q + b * a.q_sb + (int64_t)seq0 * a.q_st + h * a.q_sh;
+  const uint16_t *dog = (const uint16_t *)a.dout + b * a.do_sb + (int64_t)seq0 * a.do_st + h * a.do_sh;
+  const uint16_t *kg = (const uint16_t *)a.k + b * a.k_sb + (int64_t)seq0 * a.k_st + h * a.k_sh;
+  const uint16_t *vg = (const uint16_t *)a.v + b * a.v_sb + (int64_t)seq0 * a.v_st + h * a.v_sh;
+  for (int idx = tid; idx < KB * DCH; idx += 256) {
+    const int c = idx / DCH, ch = idx % DCH;
+    uint4 k4 = {0u, 0u, 0u, 0u}, v4 = k4;
+    if (k0 + c < nk) {
+      k4 = *(const uint4 *)(kg + (int64_t)(k0 + c) * a.k_st + ch * 8);
+      v4 = *(const uint4 *)(vg + (int64_t)(k0 + c) * a.v_st + ch * 8);
+    }
+    *(uint4 *)(ks + c * PITCH + ch * 8) = k4;
+    *(uint4 *)(vs + c * PITCH + ch * 8) = v4;
+  }
+  for (int idx = tid; idx < RS * DCH; idx += 256) {
+    const int r = idx / DCH, ch = idx % DCH, q = qr0 + r;
+    uint4 q4 = {0u, 0u, 0u, 0u}, o4 = q4;
+    if (q >= 0 && q < nq) {
+      q4 = *(const uint4 *)(qg + (int64_t)q * a.q_st + ch * 8);
+      o4 = *(const uint4 *)(dog + (int64_t)q * a.do_st + ch * 8);
+    }
+    *(uint4 *)(qs + r * PITCH + ch * 8) = q4;
+    *(uint4 *)(dos + r * PITCH + ch * 8) = o4;
+  }
+  __syncthreads();
+  // wave w: slab rows 32 w..32 w + 31 against the 32 keys
+  band_block<D, PITCH, SP>(qs, ks, dos, vs, wave, 0, ss, dps, lane);
+  __syncthreads();
+
+  // slab row r, Philox call hq of it: keys 8 (e / 4) + 4 hq + e % 4 (e < 16)
+  {
+    const int r = tid >> 1, hq = tid & 1;
+    const int q = qr0 + r, p = k0 + r;
+    const bool row_ok = q >= 0 && q < nq;
+    const int64_t lr = b * a.lse_sb + h * a.lse_sh + seq0 + q;
+    const float lse = row_ok ? a.lse2[lr] : INFINITY, dd = row_ok ? a.dpsum[lr] : 0.f;
+    Philox x = {{0u, 0u, 0u, 0u}};
+    if (a.drop_k && row_ok)
+      x = philox10(2u * (uint32_t)kt + (uint32_t)hq, (uint32_t)q, (uint32_t)(b * a.heads + h), a.drop_offset,
+                   a.seed_lo, a.seed_hi);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int c = 8 * (e >> 2) + 4 * hq + (e & 3), j = k0 + c;
+      const bool vis = row_ok && j < nk && j <= p && j > p - window;
+      const float pr = vis ? expf(ss[r * SP + c] * scale - lse) : 0.f;
+      const float kf = a.drop_k ? (drop_keep(x, e, a.drop_k) ? a.drop_scale : 0.f) : 1.f;
+      const float dp = dps[r * SP + c];
+      ss[r * SP + c] = pr * kf;
+      dps[r * SP + c] = pr * __builtin_fmaf(kf, dp, -dd);
+    }
+  }
+  __syncthreads();
+
+  // dV = (P kf)^T dO and dK = scale dS^T Q over the rows that can see a key here
+  const int r_lo = max(0, -qr0), r_hi = min(min(RS, KB - 1 + window), nq - qr0);
+  const int d0 = 4 * (tid % G), kgp = tid / G;
+  float gk[KPT][4] = {}, gv[KPT][4] = {};
+  for (int r = r_lo; r < r_hi; ++r) {
+    float qx[4], ox[4];
+    band_bf4(*(const uint2 *)(qs + r * PITCH + d0), qx);
+    band_bf4(*(const uint2 *)(dos + r * PITCH + d0), ox);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = kgp + KG * i;
+      const float ds = dps[r * SP + c], pk = ss[r * SP + c];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        gk[i][x] = __builtin_fmaf(ds, qx[x], gk[i][x]);
+        gv[i][x] = __builtin_fmaf(pk, ox[x], gv[i][x]);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int j = k0 + kgp + KG * i;
+    if (j < nk) {
+      store_grad4(a.dk, b * a.dk_sb + (int64_t)(seq0 + j) * a.dk_st + h * a.dk_sh + d0, a.grad_f32,
+                  scale * gk[i][0], scale * gk[i][1], scale * gk[i][2], scale * gk[i][3]);
+      store_grad4(a.dv, b * a.dv_sb + (int64_t)(seq0 + j) * a.dv_st + h * a.dv_sh + d0, a.grad_f32, gv[i][0],
+                  gv[i][1], gv[i][2], gv[i][3]);
+    }
+  }
+}
+
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t s) {
   constexpr int NW_KV = 4;
+  if (bwd_band(a.causal, a.window)) {
+    const int64_t bh = (int64_t)a.batch * a.heads;
+    const int64_t q_items = bh * ((a.nq + kBandRows - 1) / kBandRows);
+    const int64_t k_items = bh * ((a.nk + kBandRows - 1) / kBandRows);
+    if (q_items > 0) hipLaunchKernelGGL((bwd_band_dq_kernel<D>), dim3((unsigned)q_items), dim3(256), 0, s, a);
+    if (k_items > 0) hipLaunchKernelGGL((bwd_band_dkdv_kernel<D>), dim3((unsigned)k_items), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   // D and lse2 of every row: [batch, heads, nq], or heads x total_tokens
   // rows for a packed call (its lse layout)
   const int64_t rows = a.cu_seqlens ? (int64_t)a.heads * a.lse_sh : (int64_t)a.batch * a.heads * a.nq;
@@ -1111,6 +1416,8 @@ hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t s) {
 }
 
 }  // namespace
+
+bool bwd_band(int causal, int window) { return causal && window > 0 && window <= kBandMax; }
 
 size_t bwd_workspace_bytes(int batch, int heads, int nq, int head_dim, int deterministic) {
   (void)head_dim;

@@ -286,8 +286,8 @@ __device__ __forceinline__ void fp8_item(const FwdArgs &a, int b, int h, int qt)
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
           mx = half_swap_max(mx) * c;
           // the running max moves only when a row max jumps by more than
-          // 2^8 (P~ <= 256 stays inside e4m3's range of 448)
-          const bool up = mx > m + 8.f;
+          // a.lazy <= 8 (P~ <= 256 stays inside e4m3's range of 448)
+          const bool up = mx > m + a.lazy;
           alpha = up ? fast_exp2(m - mx) : 1.f;
           m = up ? mx : m;
           m_use = m == -INFINITY ? 0.f : m;

@@ -101,11 +101,13 @@ struct KvStage {
 };
 
 // The running row max only moves when a tile's row max exceeds it by more
-// than kLazy (log2 units): P~ = 2^(s - m) then stays <= 2^kLazy, far inside
+// than a.lazy (log2 units): P~ = 2^(s - m) then stays <= 2^a.lazy, far inside
 // fp32 and bf16 range, and the accumulators are rescaled only when a row max
 // jumps that far (with inputs of unit scale, only on the first tile).  The
-// result is exact either way: O and LSE are formed with the same m.
-constexpr float kLazy = 8.f;
+// result is exact either way: O and LSE are formed with the same m.  The
+// launcher sets a.lazy = 8, or 0 (an exact running max) where every row sees
+// at most 64 keys: those rows' weights can sit on a few keys, and with an
+// exact max the largest P~ is 1, which bf16 holds without rounding.
 
 // ---------------------------------------------------------------------------
 // bf16 forward with the P.V product deferred by one key tile.  8 waves of 32
@@ -193,7 +195,7 @@ __device__ __forceinline__ void drop_item(const FwdArgs &a, int b, int h, int qt
   float m = -INFINITY, l = 0.f;
   const float c = a.scale_log2;
   f32x16 s[2];
-  uint4 pb_prev[4];        // P~ of the previous tile (B operands)
+  uint4 pb_prev[4] = {};   // P~ of the previous tile (B operands)
   float alpha_prev = 1.f;  // accumulator rescale that goes with it
   bool has_prev = false;
 
@@ -244,7 +246,7 @@ __device__ __forceinline__ void drop_item(const FwdArgs &a, int b, int h, int qt
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
     mx = half_swap_max(mx) * c;
-    const bool up = mx > m + kLazy;
+    const bool up = mx > m + a.lazy;
     const float alpha = up ? fast_exp2(m - mx) : 1.f;
     m = up ? mx : m;
     const float m_use = m == -INFINITY ? 0.f : m;
@@ -285,7 +287,10 @@ __device__ __forceinline__ void drop_item(const FwdArgs &a, int b, int h, int qt
     const bool more_k = jt + 1 < jt1;
     if (!MASK || more_k) st.load_k(krs, k0 + BC, tid, kst2);
     st.load_v(vrs, k0, tid, vst2);
-    uint4 pb[4];
+    // zero unless this wave's softmax writes it: a wave that sits out a
+    // masked tile hands P~ = 0 to the next interior tile's product, which
+    // runs without a has_prev check
+    uint4 pb[4] = {};
     float alpha = 1.f;
     if (!MASK) {
       // interior tile: the wave sees the whole tile and the previous one.
@@ -331,7 +336,7 @@ __device__ __forceinline__ void drop_item(const FwdArgs &a, int b, int h, int qt
 #pragma unroll
           for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[1][e]);
           mx = half_swap_max(mx) * c;
-          const bool up = mx > m + kLazy;
+          const bool up = mx > m + a.lazy;
           alpha = up ? fast_exp2(m - mx) : 1.f;
           m = up ? mx : m;
           m_use = m == -INFINITY ? 0.f : m;
@@ -673,7 +678,7 @@ __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, 
       for (int e = 2; e < 8; ++e) mp[j] = fmaxf(mp[j], s[j >> 1][(j & 1) * 8 + e]);
     float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
     mx = half_swap_max(mx) * c;
-    const bool up = mx > m + kLazy;
+    const bool up = mx > m + a.lazy;
     alpha = up ? fast_exp2(m - mx) : 1.f;
     m = up ? mx : m;
     const float m_use = m == -INFINITY ? 0.f : m;

@@ -29,6 +29,9 @@ struct FwdArgs {
   // kept probabilities scaled by drop_scale = 256 / drop_k
   uint32_t drop_k, seed_lo, seed_hi, drop_offset;
   float drop_scale;
+  // the running row max moves only when a tile's max exceeds it by more than
+  // this (base-2 units); 0 keeps it exact
+  float lazy;
   int32_t persist;               // persistent launch (set by the launcher): 1 dense schedule, 2 packed varlen schedule
 };
 
@@ -91,6 +94,10 @@ hipError_t launch_fwd_f32(const FwdArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_fwd_fp8(const FwdArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs &a, int head_dim, hipStream_t s);
 size_t bwd_workspace_bytes(int batch, int heads, int nq, int head_dim, int deterministic);
+// Backward calls that run the exact fp32 kernels of a narrow causal window
+// (every row sees at most 64 keys); their launches take one work-group per
+// 32 query rows and per 32 keys of each (batch, head).
+bool bwd_band(int causal, int window);
 hipError_t launch_merge(const MergeArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_kv_append(const DecodeArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int head_dim, hipStream_t s);

@@ -140,6 +140,40 @@ def kvcache_inputs(batch, cache_len, heads, head_dim, nq, seed=0):
     return q, kc, vc, kn, vn
 
 
+def spike_keys(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float, every: int = 1024,
+               phase: int = 300, group: int = 8, level: float = 9.0, voff: float = 0.3, rest: float = 0.1):
+    """Inputs whose row maximum of the logits jumps in the middle of the key loop.
+
+    q, k, v: [..., seqlen, heads, d] (token axis -3).  Every query gets first
+    coordinate 1 and its other coordinates scaled by ``rest``; every key gets
+    first coordinate 0 except the spike keys, groups of ``group`` consecutive
+    keys starting at phase (mod every), which get level / (scale log2 e).  A
+    spike key's logit then exceeds the others' by about ``level`` in base-2
+    units (the rest spread by about rest sqrt(d) scale log2 e around 0), so a
+    row's running maximum rises by more than 8 when the row reaches its first
+    spike group after its first key tile.  A group's weight (group 2^level)
+    is of the order of that of the ~1000 ordinary keys before it, and no key
+    carries much of a row's weight.  V rows of ordinary keys are shifted by
+    +voff, those of spike keys by -voff (alternating in sign along the head
+    dimension), so the output depends strongly on how the weights before and
+    after the jump are combined.  Returns new q, k, v of the input dtypes."""
+    qf, kf, vf = q.float().clone(), k.float().clone(), v.float().clone()
+    qf[..., 1:] *= rest
+    qf[..., 0] = 1.0
+    n = kf.shape[-3]
+    j = torch.arange(n)
+    hit = ((j - phase) % every) < group
+    amp = torch.where(hit, level / (scale * 1.4426950408889634), 0.0)
+    sign = torch.where(hit, -voff, voff)
+    shape = [1] * (kf.dim() - 1)
+    shape[-2] = n
+    kf[..., 0] = amp.reshape(shape).expand(kf.shape[:-1])
+    d = vf.shape[-1]
+    pattern = torch.where(torch.arange(d) % 2 == 0, 1.0, -1.0)
+    vf += sign.reshape(shape + [1]) * pattern
+    return qf.to(q.dtype), kf.to(k.dtype), vf.to(v.dtype)
+
+
 def quantize_e4m3(x: torch.Tensor):
     """Per-tensor e4m3 quantisation done by the caller before the fp8 forward.
 

@@ -293,3 +293,18 @@ def test_launch_without_gpu_fails_loudly(lib):
     st = lib.fa_fwd(ctypes.byref(p), None)
     assert st == B.FA_ERR_HIP
     assert lib.fa_last_error()
+
+
+def test_host_tensors_are_refused_before_any_launch(lib):
+    """A host tensor handed to a launching call raises ValueError instead of
+    reaching a kernel as a host pointer."""
+    q = torch.zeros(40, 2, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 40], dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU|must be on"):
+        B.fa_varlen_fwd(q, q, q, cu, 40, causal=True)
+    q4 = torch.zeros(1, 1, 2, 64, dtype=torch.bfloat16)
+    kc = torch.zeros(1, 16, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU|must be on"):
+        B.fa_fwd_kvcache(q4, kc, kc, cache_seqlens=torch.tensor([3], dtype=torch.int32))
+    with pytest.raises(ValueError, match="GPU|must be on"):
+        B.fa_fwd(q4, kc, kc)

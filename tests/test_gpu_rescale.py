@@ -1,0 +1,223 @@
+"""GPU parity on inputs that make the online softmax rescale a non-zero accumulator.
+
+The blocks of a row are combined by rescaling what was accumulated so far
+whenever a later block raises the row maximum ("FlashAttention优化Transformer
+显存与计算效率", section 2.2.2).  With i.i.d. N(0, 1) inputs the kernels' lazy
+maximum (it moves only when a tile's maximum exceeds it by more than 8 in
+base-2 units) settles on the first tile, so that branch would never run.
+Here the spike keys of ``spike_keys`` raise a row's maximum by about 9 in the
+middle of the key loop, with the keys before the jump still carrying a large
+share of the weights and value rows that pull the output the other way; each
+forward kernel (ping-pong, persistent ping-pong, dropout, fp8, packed varlen)
+and the decode kernel is checked element by element against the oracle.
+The partial-result merge is checked with more parts than one batch of 8.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_24_amd import fa_fwd, fa_fwd_kvcache, fa_merge, fa_varlen_fwd
+from exact_attention_24_amd.inputs import (cu_seqlens_of, dense_inputs, kvcache_inputs, quantize_e4m3, spike_keys,
+                                           varlen_inputs)
+from tests.parity import FP8_MAX_ABS, assert_close, assert_lse_close, f64, sample_rows
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _spiked(b, nq, nk, h, d, seed):
+    q, _, _ = dense_inputs(b, nq, h, d, "bf16", seed=seed)
+    _, k, v = dense_inputs(b, nk, h, d, "bf16", seed=seed + 1)
+    return spike_keys(q, k, v, 1 / np.sqrt(d))
+
+
+def _rose(q, k, scale, causal, window, rows=None):
+    """Fraction of checked rows whose maximum logit (base 2) over all visible
+    keys exceeds the one over their first visible key tile of 64 by more than
+    8: the rows on which the rescale must run (a check on the inputs only)."""
+    q, k = np.asarray(q, np.float64), np.asarray(k, np.float64)
+    nq, nk = q.shape[0], k.shape[0]
+    rows = np.arange(nq) if rows is None else rows
+    s = scale * 1.4426950408889634 * (q[rows] @ k.T)
+    ok = oracle.visible(rows, nk, causal, window, offset=nk - nq)
+    s = np.where(ok, s, -np.inf)
+    first = np.argmax(ok, axis=1) // 64 * 64
+    cnt = 0
+    for a, r in enumerate(rows):
+        if not ok[a].any():
+            continue
+        m_all = s[a].max()
+        m_first = s[a, first[a]:first[a] + 64].max()
+        cnt += m_all > m_first + 8
+    return cnt / max(1, len(rows))
+
+
+FWD = [
+    # (batch, nq, nk, heads, d, causal, window)
+    (1, 1100, 1100, 2, 128, True, 0),
+    (1, 1100, 1100, 2, 64, False, 0),
+    (2, 900, 900, 2, 128, True, 700),
+    (1, 700, 1300, 2, 128, True, 0),   # Nq < Nk, bottom-right causal
+    (1, 1000, 1000, 3, 64, False, 600),
+]
+
+
+@pytest.mark.parametrize("b,nq,nk,h,d,causal,window", FWD)
+def test_bf16_forward_rescale(b, nq, nk, h, d, causal, window):
+    print(f"[rescale bf16] b={b} nq={nq} nk={nk} h={h} d={d} causal={causal} window={window}", flush=True)
+    q, k, v = _spiked(b, nq, nk, h, d, seed=nq + nk + d)
+    scale = 1 / np.sqrt(d)
+    assert _rose(f64(q[0, :, 0]), f64(k[0, :, 0]), scale, causal, window) > 0.5
+    o, lse = fa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, window=window)
+    torch.cuda.synchronize()
+    ro, rl = oracle.mha_fwd(f64(q), f64(k), f64(v), scale, causal, window)
+    assert_close(f64(o), ro)
+    assert_lse_close(f64(lse), rl)
+
+
+@pytest.mark.parametrize("b,n,h,d,causal,window", [
+    (2, 1100, 48, 128, True, 0),    # persistent schedule, paired causal tiles
+    (1, 1300, 64, 64, False, 0),
+    (2, 1536, 48, 128, True, 500),
+])
+def test_bf16_persistent_forward_rescale(b, n, h, d, causal, window):
+    print(f"[rescale bf16 persistent] b={b} n={n} h={h} d={d} causal={causal} window={window}", flush=True)
+    q, k, v = _spiked(b, n, n, h, d, seed=n + h)
+    scale = 1 / np.sqrt(d)
+    o, lse = fa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, window=window)
+    torch.cuda.synchronize()
+    q64, k64, v64, o64, l64 = f64(q), f64(k), f64(v), f64(o), f64(lse)
+    for bi in range(b):
+        for hh in sorted({0, (h // 2 + 5 * bi) % h, h - 1}):
+            rows = np.union1d(sample_rows(n, 32, seed=bi * 10 + hh), [0, 255, 256, 511, 512, n - 1])
+            assert _rose(q64[bi, :, hh], k64[bi, :, hh], scale, causal, window, rows) > 0.2
+            ro, rl = oracle.attention_fwd(q64[bi, rows, hh], k64[bi, :, hh], v64[bi, :, hh], scale, causal, window,
+                                          q_pos=rows, nq=n)
+            assert_close(o64[bi, rows, hh], ro, what=f"O batch {bi} head {hh}")
+            assert_lse_close(l64[bi, hh, rows], rl)
+
+
+@pytest.mark.parametrize("n,causal,window,p", [(1100, True, 0, 0.2), (900, False, 300, 0.1), (700, True, 500, 0.3)])
+def test_dropout_forward_rescale(n, causal, window, p):
+    """V is halved: kept probabilities are scaled by 1 / (1 - p), and a row
+    with few keys (causal row 0 returns V_0 / (1 - p)) would otherwise reach
+    |O| >= 4, where half a bf16 ulp alone exceeds the 1e-2 bound."""
+    print(f"[rescale dropout] n={n} causal={causal} window={window} p={p}", flush=True)
+    q, k, v = _spiked(1, n, n, 2, 128, seed=n * 3)
+    v = (v.float() * 0.5).to(v.dtype)
+    seed, off = 0xABCDEF + n, 11
+    o, lse = fa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, window=window, dropout_p=p, seed=seed,
+                    offset=off)
+    torch.cuda.synchronize()
+    ro, rl = oracle.mha_fwd(f64(q), f64(k), f64(v), 1 / np.sqrt(128), causal, window, dropout=(p, seed, off))
+    assert_close(f64(o), ro)
+    assert_lse_close(f64(lse), rl)
+
+
+def _deq(t, s):
+    return oracle.fp8_dequant(t.view(torch.uint8).numpy(), s)
+
+
+@pytest.mark.parametrize("b,n,h,d,causal,window", [
+    (1, 1100, 2, 128, True, 0),
+    (1, 900, 2, 64, False, 400),
+    (2, 1100, 48, 128, True, 0),   # persistent schedule
+])
+def test_fp8_forward_rescale(b, n, h, d, causal, window):
+    """P~ <= 2^8 stays inside e4m3's range (448) only because the running
+    maximum moves when a tile's maximum exceeds it by more than 8."""
+    print(f"[rescale fp8] b={b} n={n} h={h} d={d} causal={causal} window={window}", flush=True)
+    q, k, v = _spiked(b, n, n, h, d, seed=n + 7 * h)
+    (q8, sq), (k8, sk), (v8, sv) = quantize_e4m3(q), quantize_e4m3(k), quantize_e4m3(v)
+    o, lse = fa_fwd(q8.to(DEV), k8.to(DEV), v8.to(DEV), causal=causal, window=window, descale=(sq, sk, sv))
+    torch.cuda.synchronize()
+    qd, kd, vd = _deq(q8, sq), _deq(k8, sk), _deq(v8, sv)
+    o64, l64 = f64(o), f64(lse)
+    for bi in range(b):
+        for hh in sorted({0, h - 1}):
+            ro, rl = oracle.attention_fwd(qd[bi, :, hh], kd[bi, :, hh], vd[bi, :, hh], 1 / np.sqrt(d), causal, window)
+            assert _rose(qd[bi, :, hh], kd[bi, :, hh], 1 / np.sqrt(d), causal, window) > 0.5
+            assert_close(o64[bi, :, hh], ro, max_abs=FP8_MAX_ABS, mean_abs=None, what=f"O fp8 batch {bi} head {hh}")
+            assert_lse_close(l64[bi, hh], rl, tol=2e-3)
+
+
+@pytest.mark.parametrize("lengths,causal,window", [
+    ([1100, 70, 900, 1300], True, 0),
+    ([1100, 70, 900, 1300], True, 600),
+    ([800, 1200, 5], False, 0),
+])
+def test_varlen_forward_rescale(lengths, causal, window):
+    print(f"[rescale varlen] lengths={lengths} causal={causal} window={window}", flush=True)
+    h, d = 3, 128
+    q, k, v, cu = varlen_inputs(lengths, h, d, "bf16", seed=sum(lengths))
+    q, k, v = spike_keys(q, k, v, 1 / np.sqrt(d))
+    o, lse = fa_varlen_fwd(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), max(lengths), causal=causal, window=window)
+    torch.cuda.synchronize()
+    ro, rl = oracle.varlen_fwd(f64(q), f64(k), f64(v), cu.numpy(), 1 / np.sqrt(d), causal, window)
+    assert_close(f64(o), ro)
+    assert_lse_close(f64(lse), rl)
+
+
+# ---------------------------------------------------------------------------
+# merge of more parts than one batch of 8, and the decode's default split
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n_p,pdt,odt", [
+    (9, torch.float32, torch.bfloat16),
+    (16, torch.float32, torch.float32),
+    (64, torch.bfloat16, torch.bfloat16),
+])
+def test_merge_more_than_eight_parts(n_p, pdt, odt):
+    """LSE_p grows with p on half the rows, so the maximum moves from batch to
+    batch and the running sums are rescaled."""
+    print(f"[merge many] parts={n_p} {pdt}->{odt}", flush=True)
+    b, n, h, d = 2, 97, 3, 128
+    g = torch.Generator().manual_seed(n_p)
+    o_p = (0.5 * torch.randn(n_p, b, n, h, d, generator=g)).to(pdt)
+    lse_p = 3.0 * torch.randn(n_p, b, h, n, generator=g)
+    ramp = torch.linspace(0.0, 12.0, n_p)[:, None, None, None]
+    lse_p[:, :, :, ::2] += ramp
+    dead = torch.rand(n_p, b, h, n, generator=g) < 0.1
+    dead[:, 0, 0, 5] = True  # one row without any key
+    lse_p[dead] = float("-inf")
+    o_p.permute(0, 1, 3, 2, 4)[dead] = float("nan")
+    o, lse = fa_merge(o_p.to(DEV), lse_p.to(DEV), out_dtype=odt)
+    torch.cuda.synchronize()
+    ro, rl = oracle.merge_partials(np.nan_to_num(f64(o_p), nan=0.0), f64(lse_p).transpose(0, 1, 3, 2))
+    if odt == torch.float32:
+        assert_close(f64(o), ro, max_abs=1e-5, mean_abs=1e-5)
+    else:
+        assert_close(f64(o), ro)
+    assert_lse_close(f64(lse), rl.transpose(0, 2, 1))
+
+
+@pytest.mark.parametrize("spiked", [False, True])
+def test_kvcache_default_split_b1_h8_8k(spiked):
+    """B1 H8 d128 with 8191 cached keys + 1 new: the default choice cuts each
+    (batch, head) into 16 key splits, joined by the merge over two batches of
+    8 parts; with spike keys the per-split running maxima move as well."""
+    b, h, d, lmax = 1, 8, 128, 8192
+    q, kc, vc, kn, vn = kvcache_inputs(b, lmax, h, d, 1, seed=88 + spiked)
+    if spiked:
+        q, kc, vc = spike_keys(q, kc, vc, 1 / np.sqrt(d), phase=700)
+    print(f"[kvcache default split] spiked={spiked}", flush=True)
+    kcd, vcd = kc.to(DEV), vc.to(DEV)
+    o, lse = fa_fwd_kvcache(q.to(DEV), kcd, vcd, kn.to(DEV), vn.to(DEV), cache_seqlens=lmax - 1, causal=True)
+    torch.cuda.synchronize()
+    ro, rl, _, _ = oracle.kvcache_fwd(f64(q), f64(kc), f64(vc), [lmax - 1], 1 / np.sqrt(d), True, 0, f64(kn), f64(vn))
+    assert_close(f64(o), ro)
+    assert_lse_close(f64(lse), rl)
+
+
+def test_dropout_single_row_wave_at_window_edge():
+    """nq = nk = 289, causal, window 97: the last wave holds one row, and the
+    window edge falls on the last key of a tile, so that wave sits out a
+    masked tile just before an interior one."""
+    q, k, v = dense_inputs(1, 289, 2, 128, "bf16", seed=289)
+    seed, off = 4242, 1
+    o, lse = fa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, window=97, dropout_p=0.2, seed=seed, offset=off)
+    torch.cuda.synchronize()
+    ro, rl = oracle.mha_fwd(f64(q), f64(k), f64(v), 1 / np.sqrt(128), True, 97, dropout=(0.2, seed, off))
+    assert_close(f64(o), ro)
+    assert_lse_close(f64(lse), rl)

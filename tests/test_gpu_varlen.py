@@ -82,3 +82,10 @@ def test_varlen_32k_window4096_sampled():
                                           q_pos=rows, nq=n)
             assert_close(o64[a + rows, h], ro, what=f"O seq {s} head {h}")
             assert_lse_close(l64[h, a + rows], rl)
+
+
+def test_host_cu_seqlens_is_refused():
+    """cu_seqlens left on the host raises before anything is launched."""
+    q, k, v, cu = varlen_inputs([30, 10], 2, 64, "bf16", seed=1)
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        fa_varlen_fwd(q.to(DEV), k.to(DEV), v.to(DEV), cu, 30, causal=True)

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 FA_F32, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_DTYPE_MISMATCH, FA_ERR_UNSUPPORTED, FA_ERR_HIP = range(5)
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 _I64x4 = ctypes.c_int64 * 4
 _I64x3 = ctypes.c_int64 * 3
@@ -118,7 +118,7 @@ class KvcacheParams(ctypes.Structure):
 EXPORTS = ("fa_abi_version", "fa_last_error", "fa_check_fwd", "fa_check_varlen_fwd", "fa_check_bwd",
            "fa_check_varlen_bwd", "fa_fwd", "fa_varlen_fwd", "fa_bwd_workspace_bytes", "fa_bwd",
            "fa_varlen_bwd_workspace_bytes", "fa_varlen_bwd", "fa_check_merge", "fa_merge",
-           "fa_check_kvcache", "fa_kvcache_workspace_bytes", "fa_fwd_kvcache")
+           "fa_check_kvcache", "fa_kvcache_workspace_bytes", "fa_fwd_kvcache", "fa_bwd_noalloc")
 
 _lib = None
 
@@ -147,6 +147,8 @@ def lib():
     L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.fa_bwd.argtypes = [ctypes.POINTER(BwdParams), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     L.fa_bwd.restype = ctypes.c_int
+    L.fa_bwd_noalloc.argtypes = [ctypes.POINTER(BwdParams), ctypes.c_void_p]
+    L.fa_bwd_noalloc.restype = ctypes.c_int
     L.fa_varlen_bwd_workspace_bytes.argtypes = [ctypes.POINTER(VarlenBwdParams)]
     L.fa_varlen_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.fa_varlen_bwd.argtypes = [ctypes.POINTER(VarlenBwdParams), ctypes.c_void_p, ctypes.c_size_t,
@@ -391,6 +393,17 @@ def fa_bwd(dout, q, k, v, o, lse, causal=False, window=0, softmax_scale=None, de
     nbytes = fa_bwd_workspace_bytes(p)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     _raise(lib().fa_bwd(ctypes.byref(p), ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(nbytes), _stream()))
+    return dq, dk, dv
+
+
+def fa_bwd_noalloc(dout, q, k, v, o, lse, dq, dk, dv, causal=False, window=0, softmax_scale=None,
+                   deterministic=False, dropout_p=0.0, seed=None, offset=0):
+    """fa_bwd with the caller's dq, dk, dv and no allocation at all: the
+    library's static device scratch replaces the workspace."""
+    p = make_bwd_params(dout, q, k, v, o, lse, dq, dk, dv, causal, window, softmax_scale, deterministic,
+                        dropout_p, seed, offset)
+    _same_gpu(q, k=k, v=v, o=o, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv)
+    _raise(lib().fa_bwd_noalloc(ctypes.byref(p), _stream()))
     return dq, dk, dv
 
 

@@ -414,6 +414,23 @@ fa_status fa_bwd(const fa_bwd_params *p, void *workspace, size_t workspace_bytes
   return launched(fa::launch_bwd_bf16(a, p->head_dim, reinterpret_cast<hipStream_t>(stream)));
 }
 
+fa_status fa_bwd_noalloc(const fa_bwd_params *p, void *stream) {
+  fa_status st = fa_check_bwd(p);
+  if (st != FA_OK) return st;
+  const size_t need = fa::bwd_workspace_bytes(p->batch, p->heads, p->seqlen_q, p->head_dim, p->deterministic);
+  if (need > fa::kBwdScratchBytes)
+    return fail(FA_ERR_INVALID_ARGUMENT,
+                "fa_bwd_noalloc: this call needs %zu bytes of scratch, more than the library's static %zu "
+                "(8 bytes per row of batch x heads x seqlen_q); use fa_bwd with a workspace",
+                need, (size_t)fa::kBwdScratchBytes);
+  if ((int64_t)p->batch * p->heads * (p->seqlen_q + (int64_t)p->seqlen_k) == 0) return ok();
+  if ((st = check_device()) != FA_OK) return st;
+  void *ws = nullptr;
+  const hipError_t e = fa::bwd_scratch(&ws);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "device scratch lookup failed: %s", hipGetErrorString(e));
+  return fa_bwd(p, ws, fa::kBwdScratchBytes, stream);
+}
+
 size_t fa_varlen_bwd_workspace_bytes(const fa_varlen_bwd_params *p) {
   if (fa_check_varlen_bwd(p) != FA_OK) return 0;
   return fa::bwd_workspace_bytes(1, p->heads, p->total_tokens, p->head_dim, p->deterministic);

@@ -30,10 +30,39 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
+
+// Workspace of fa_bwd_noalloc, for callers that cannot allocate: D and
+// LSE log2(e) of every query row (8 bytes per row of batch x heads x
+// seqlen_q) live in this array, one copy per device, held until the process
+// ends.  Host code must not pass `scratch` itself to a kernel (on the host
+// it names a stand-in, not device memory): bwd_scratch() looks up the
+// device address once per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[kBwdScratchBytes];
+
+hipError_t bwd_scratch(void **ptr) {
+  static std::mutex mu;
+  static void *addr[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
 namespace {
 
 using namespace dev;

@@ -94,6 +94,10 @@ hipError_t launch_fwd_f32(const FwdArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_fwd_fp8(const FwdArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs &a, int head_dim, hipStream_t s);
 size_t bwd_workspace_bytes(int batch, int heads, int nq, int head_dim, int deterministic);
+// Device scratch that replaces the backward's workspace in fa_bwd_noalloc
+// (one static copy per device); bwd_scratch() gives this device's address.
+constexpr size_t kBwdScratchBytes = (size_t)8 << 20;
+hipError_t bwd_scratch(void **ptr);
 // Backward calls that run the exact fp32 kernels of a narrow causal window
 // (every row sees at most 64 keys); their launches take one work-group per
 // 32 query rows and per 32 keys of each (batch, head).

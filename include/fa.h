@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 6
+#define FA_ABI_VERSION 7
 
 typedef enum {
   FA_F32 = 0,       /* IEEE binary32 */
@@ -286,6 +286,20 @@ size_t fa_bwd_workspace_bytes(const fa_bwd_params *p);
 
 /* Enqueue the backward: writes dq, dk, dv. */
 fa_status fa_bwd(const fa_bwd_params *p, void *workspace, size_t workspace_bytes, void *stream);
+
+/* fa_bwd without any allocation, for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that
+ * forbid allocation): the same kernels and results as fa_bwd, with the
+ * workspace taken from a static device array of FA_BWD_SCRATCH_BYTES that
+ * the library holds on each device it runs on until the process ends.  The
+ * caller passes every input and output as for fa_bwd.  Calls that need more
+ * than FA_BWD_SCRATCH_BYTES (8 bytes per row of batch x heads x seqlen_q,
+ * i.e. more than 2^20 such rows) return FA_ERR_INVALID_ARGUMENT before
+ * anything is launched.  Nothing in the array has to start at any value
+ * (every call writes what it reads), but all calls on one device share it:
+ * calls that overlap in time on one device (different streams) race. */
+#define FA_BWD_SCRATCH_BYTES ((size_t)8 << 20)
+fa_status fa_bwd_noalloc(const fa_bwd_params *p, void *stream);
 
 /* Bytes of device workspace fa_varlen_bwd needs (0 on invalid parameters). */
 size_t fa_varlen_bwd_workspace_bytes(const fa_varlen_bwd_params *p);

@@ -97,6 +97,7 @@ __all__ = [
     "varlen_fwd",
     "varlen_bwd",
     "philox4x32",
+    "dropout_index",
     "dropout_bytes",
     "dropout_keep",
     "merge_partials",
@@ -263,18 +264,29 @@ def philox4x32(counter, key, rounds=10):
     return np.stack([c0, c1, c2, c3], axis=-1).astype(np.uint32)
 
 
-def dropout_bytes(slot, q_rows, nk, seed, offset):
-    """Random bytes [len(q_rows), nk] of head slot ``slot`` (see the module
-    docstring for the element -> (counter, word, byte) map)."""
+def dropout_index(slot, q_rows, nk, offset):
+    """Where the random byte of each element (query row i, key j) of head slot
+    ``slot`` comes from: (counter [len(q_rows), nk, 4], word [len(q_rows), nk],
+    byte [len(q_rows), nk]) -- the Philox counter (2 (j div 32) + (j div 4)
+    mod 2, i, slot, offset), word (j mod 32) div 8 of its output, byte j mod 4
+    of that word (see the module docstring)."""
     i = np.asarray(q_rows, dtype=np.uint64)[:, None]
     j = np.arange(nk, dtype=np.uint64)[None, :]
     ctr = np.stack(np.broadcast_arrays(2 * (j >> np.uint64(5)) + ((j >> np.uint64(2)) & np.uint64(1)), i,
                                        np.uint64(slot), np.uint64(offset & 0xFFFFFFFF)), axis=-1)
+    shape = ctr.shape[:2]
+    word = np.broadcast_to(((j & np.uint64(31)) >> np.uint64(3)).astype(np.int64), shape)
+    byte = np.broadcast_to((j & np.uint64(3)).astype(np.int64), shape)
+    return ctr, word, byte
+
+
+def dropout_bytes(slot, q_rows, nk, seed, offset):
+    """Random bytes [len(q_rows), nk] of head slot ``slot``: byte ``byte`` of
+    word ``word`` of Philox4x32-10 at ``counter`` (dropout_index)."""
+    ctr, word, byte = dropout_index(slot, q_rows, nk, offset)
     words = philox4x32(ctr, (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF))   # [rows, nk, 4]
-    widx = np.broadcast_to(((j & np.uint64(31)) >> np.uint64(3)).astype(np.int64), words.shape[:2])
-    w = np.take_along_axis(words, widx[..., None], axis=-1)[..., 0]
-    shift = (np.uint32(8) * (j & np.uint64(3)).astype(np.uint32))
-    return ((w >> shift) & np.uint32(0xFF)).astype(np.uint8)
+    w = np.take_along_axis(words, word[..., None], axis=-1)[..., 0]
+    return ((w >> (np.uint32(8) * byte.astype(np.uint32))) & np.uint32(0xFF)).astype(np.uint8)
 
 
 def dropout_keep(slot, q_rows, nk, seed, offset, p):

@@ -113,6 +113,18 @@ def _bwd_mask_only_in_dv(q, k, v, dout, scale, causal=False, window=0, drop=None
     return dq, dk, dv
 
 
+_ORIG_DROPOUT_INDEX = oa.dropout_index
+
+
+def _dropout_index_shares_bytes(slot, q_rows, nk, offset):
+    """Word (j mod 16) div 4 instead of (j mod 32) div 8: keys j and j + 16 of
+    the first half of every 32-key block then draw the same byte, which leaves
+    every marginal statistic of the bytes intact."""
+    ctr, word, byte = _ORIG_DROPOUT_INDEX(slot, q_rows, nk, offset)
+    j = np.arange(nk)
+    return ctr, np.broadcast_to((j % 16) // 4, word.shape), byte
+
+
 _ORIG_MERGE = oa.merge_partials
 _ORIG_KVCACHE = oa.kvcache_fwd
 
@@ -129,6 +141,9 @@ MUTATIONS = [
      lambda: pins.test_merge_of_key_chunks_equals_full_attention(False, 0, [0, 7, 19, 40])),
     ("philox4x32", _philox_no_key_bump, lambda: pins.test_philox_known_answers()),
     ("attention_bwd", _bwd_mask_only_in_dv, lambda: pins.test_dropout_backward_finite_differences(True, 0)),
+    ("dropout_index", _dropout_index_shares_bytes, lambda: pins.test_dropout_map_is_injective()),
+    ("dropout_index", _dropout_index_shares_bytes, lambda: pins.test_dropout_bytes_pairwise_independent()),
+    ("dropout_index", _dropout_index_shares_bytes, lambda: pins.test_dropout_bytes_map_and_uniformity()),
     ("paged_gather", _paged_gather_swaps_index, lambda: pins.test_paged_kvcache_equals_contiguous(4)),
     ("kvcache_fwd", _kvcache_forgets_new_keys,
      lambda: pins.test_kvcache_decode_equals_rows_of_the_full_sequence(1, True, 0)),

@@ -540,6 +540,49 @@ def test_dropout_bytes_map_and_uniformity():
     assert chi2 < 255 + 6 * math.sqrt(2 * 255)
 
 
+def test_dropout_map_is_injective():
+    """No two elements share a random byte: over a 64 x 4096 block of two
+    head slots and two offsets, every element has its own (counter, word,
+    byte) triple."""
+    rows = np.arange(64)
+    seen = []
+    for slot in (3, 4):
+        for off in (1, 2):
+            ctr, word, byte = oracle.dropout_index(slot, rows, 4096, off)
+            assert ctr.shape == (64, 4096, 4) and word.shape == byte.shape == (64, 4096)
+            assert ((0 <= word) & (word < 4)).all() and ((0 <= byte) & (byte < 4)).all()
+            seen.append(np.concatenate([ctr.reshape(-1, 4), word.reshape(-1, 1), byte.reshape(-1, 1)], axis=1))
+    triples = np.concatenate(seen).astype(np.uint64)
+    assert np.unique(triples, axis=0).shape[0] == triples.shape[0]
+
+
+def test_dropout_bytes_pairwise_independent():
+    """Pairs of elements draw independent bytes: for every lag along the keys
+    (1..63, which spans the 32-key blocks the map is built from) and along the
+    rows (1..15), and between two head slots and two offsets, equal bytes occur
+    at the rate 1/256 and the keep flags (p = 0.5) are uncorrelated, each
+    within 5 sigma.  Two elements mapped to one byte would be equal always."""
+    b = oracle.dropout_bytes(3, range(64), 4096, 0xFEEDF00D, 1).astype(np.int64)
+    other = {"slot": oracle.dropout_bytes(4, range(64), 4096, 0xFEEDF00D, 1).astype(np.int64),
+             "offset": oracle.dropout_bytes(3, range(64), 4096, 0xFEEDF00D, 2).astype(np.int64)}
+
+    def check(x, y, what):
+        n = x.size
+        eq = (x == y).mean()
+        sd = math.sqrt((1 / 256) * (255 / 256) / n)
+        assert abs(eq - 1 / 256) < 5 * sd, f"{what}: equal-byte rate {eq:.5f}"
+        kx, ky = (x < 128).astype(np.float64), (y < 128).astype(np.float64)
+        corr = ((kx - kx.mean()) * (ky - ky.mean())).mean() / (kx.std() * ky.std())
+        assert abs(corr) < 5 / math.sqrt(n), f"{what}: keep-flag correlation {corr:.4f}"
+
+    for lag in range(1, 64):
+        check(b[:, :-lag], b[:, lag:], f"key lag {lag}")
+    for lag in range(1, 16):
+        check(b[:-lag], b[lag:], f"row lag {lag}")
+    for what, o in other.items():
+        check(b, o, what)
+
+
 @pytest.mark.parametrize("p", [0.1, 0.5, 0.9])
 def test_dropout_keep_rate_and_scale(p):
     keep, s = oracle.dropout_keep(2, range(256), 1024, 7, 3, p)

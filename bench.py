@@ -21,8 +21,8 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
-import math
 import os
+import re
 import sys
 import time
 
@@ -98,10 +98,31 @@ def traffic_from_profile(kernel_sha):
     return t.get("traffic_bytes_per_launch")
 
 
+def cpu_info():
+    """The host the oracle runs on: CPU model, CPUs in this process's
+    affinity mask, and the BLAS thread count (the threads its matmuls use)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((p.get("num_threads") or 0) for p in threadpool_info()) or None
+    except Exception:
+        pass
+    return {"cpu_model": model, "affinity_cpus": len(os.sched_getaffinity(0)), "blas_threads": blas}
+
+
 def cpu_baseline(budget_s=15.0):
     """The fp64 oracle on a bounded sample of the same workload: whole heads of
     the causal N=8192 d=128 forward, one after another, until budget_s."""
-    import numpy as np
+    import numpy as np  # noqa: F401
     import oracle
     from exact_attention_24_amd.inputs import WORKLOADS, workload_inputs
 
@@ -113,17 +134,255 @@ def cpu_baseline(budget_s=15.0):
         oracle.attention_fwd(q[0, :, heads], k[0, :, heads], v[0, :, heads], w.scale, True, 0)
         heads += 1
     el = time.perf_counter() - t0
-    threads = None
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads") or 0) for p in threadpool_info()) or None
-    except Exception:
-        pass
-    cores = threads or len(os.sched_getaffinity(0))
+    info = cpu_info()
     flops = fwd_flops(1, heads, w.seqlen, w.head_dim, True)
-    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": info["blas_threads"] or 1,
+            "kind": "oracle",
             "sample": f"{heads} of 32 heads of the B1 H32 N8192 d128 causal forward, fp64 NumPy, {el:.1f} s",
-            "seconds": round(el, 2)}
+            "seconds": round(el, 2), **info}
+
+
+def counters_from_profile(name, sha):
+    """MFMA-busy % per kernel from a committed SQ counter summary, if it was
+    taken on the current kernel source (its sha line); else None."""
+    try:
+        with open(os.path.join(ROOT, "profiles", name)) as f:
+            text = f.read()
+    except OSError:
+        return None
+    if f"sha {sha}" not in text:
+        return None
+    out, kernel = {}, None
+    for ln in text.splitlines():
+        if ln.startswith("fa::"):
+            kernel = ln.strip()
+        m = re.search(r"MFMA_busy_pct=([0-9.]+)", ln)
+        if m and kernel:
+            out[kernel] = float(m.group(1))
+    return out or None
+
+
+def _errors(got, ref):
+    import numpy as np
+    d = np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64))
+    return float(d.max()), float(d.mean())
+
+
+def _oracle_timed(fn):
+    t0 = time.perf_counter()
+    r = fn()
+    return r, time.perf_counter() - t0
+
+
+def config_rows(torch, fa, steps, headline_cpu):
+    """One record per configuration of the hot path, plus the extra rows:
+    flops and compulsory HBM bytes per call, median and minimum call time
+    (HIP events on the launch stream), TFLOP/s and % of peak, bytes / time,
+    MFMA busy % from the committed counter summary of the same kernel source
+    (null when there is none), max / mean abs error against the fp64 oracle
+    on sampled rows, and the oracle timed on a bounded sample of the config."""
+    import numpy as np
+    import oracle
+    from exact_attention_24_amd.inputs import WORKLOADS, workload_inputs
+
+    rows = {}
+    f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()  # noqa: E731
+
+    def timed(fn):
+        _, ms = time_calls(fn, 2, steps, torch)
+        ms = sorted(ms)
+        return ms[len(ms) // 2], ms[0]
+
+    def mfma_row(name, fn, flops, nbytes, peak, err, oracle_s, oracle_flops, sample, counters=None, extra=None):
+        med, mn = timed(fn)
+        r = {"flops": flops, "bytes": nbytes, "median_us": round(med * 1e3, 1), "min_us": round(mn * 1e3, 1),
+             "tflops": round(flops / med / 1e9, 1), "pct_peak": round(100 * flops / med / 1e9 / peak, 2),
+             "gbs": round(nbytes / med / 1e6, 1), "mfma_busy_pct": counters,
+             "err_max": None if err is None else float(f"{err[0]:.3e}"),
+             "err_mean": None if err is None else float(f"{err[1]:.3e}"),
+             "oracle": None if oracle_s is None else {"seconds": round(oracle_s, 3), "sample": sample,
+                                                       "gflops": round(oracle_flops / oracle_s / 1e9, 3)}}
+        if extra:
+            r.update(extra)
+        rows[name] = r
+        log(f"[bench] {name}: {json.dumps(r)}")
+
+    def hbm_row(name, fn, nbytes):
+        med, mn = timed(fn)
+        rows[name] = {"bytes": nbytes, "median_us": round(med * 1e3, 1), "min_us": round(mn * 1e3, 1),
+                      "gbs": round(nbytes / med / 1e6, 1), "pct_hbm_peak": round(100 * nbytes / med / 1e6 / PEAK_HBM_GBS, 2)}
+        log(f"[bench] {name}: {json.dumps(rows[name])}")
+
+    fsha = src_hash("fa_fwd.hip", "fa_device.h", "fa_internal.h")
+    bsha = src_hash("fa_bwd.hip", "fa_device.h", "fa_internal.h")
+    psha = src_hash("fa_fp8.hip", "fa_device.h", "fa_internal.h")
+
+    # configuration 1: B1 H1 N256 d64 fp32, non-causal (whole output checked)
+    w = WORKLOADS["tiny_fp32"]
+    t = workload_inputs("tiny_fp32")
+    q, k, v = (t[x].cuda() for x in ("q", "k", "v"))
+    o, _ = fa.fa_fwd(q, k, v, causal=False)
+    (ro, _), secs = _oracle_timed(lambda: oracle.mha_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), w.scale, False, 0))
+    F = fwd_flops(1, 1, 256, 64, False)
+    mfma_row("cfg1_fwd_fp32_b1_h1_n256_d64", lambda: fa.fa_fwd(q, k, v, causal=False), F,
+             4 * (4 * 256 * 64) + 4 * 256, 157.3, _errors(f64(o), ro), secs, F, "the whole config",
+             extra={"note": "fp32 FMA kernel; peak is the fp32 vector rate 157.3 TFLOP/s; launch-bound"})
+
+    # configuration 2: B2 H16 N1024 d64 bf16 causal (whole output checked)
+    w = WORKLOADS["b2_h16_n1024"]
+    t = workload_inputs("b2_h16_n1024")
+    q, k, v = (t[x].cuda() for x in ("q", "k", "v"))
+    o, _ = fa.fa_fwd(q, k, v, causal=True)
+    (ro, _), secs = _oracle_timed(lambda: oracle.mha_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), w.scale, True, 0))
+    F = fwd_flops(2, 16, 1024, 64, True)
+    mfma_row("cfg2_fwd_bf16_b2_h16_n1024_d64_causal", lambda: fa.fa_fwd(q, k, v, causal=True), F,
+             2 * (4 * 2 * 1024 * 16 * 64) + 4 * 2 * 16 * 1024, PEAK_BF16_TFLOPS, _errors(f64(o), ro), secs, F,
+             "the whole config")
+
+    # configuration 3: B1 H32 N8192 d128 bf16, causal (headline) and non-causal
+    w = WORKLOADS["llama_n8192"]
+    t = workload_inputs("llama_n8192")
+    q, k, v = (t[x].cuda() for x in ("q", "k", "v"))
+    qh, kh, vh = f64(t["q"]), f64(t["k"]), f64(t["v"])
+    nbytes = 2 * (4 * 8192 * 32 * 128) + 4 * 32 * 8192
+    srows = np.unique(np.concatenate([[0, 1, 63, 64, 255, 256, 8191], np.random.default_rng(3).choice(8192, 25, False)]))
+    for causal in (True, False):
+        o, _ = fa.fa_fwd(q, k, v, causal=causal)
+        o64 = f64(o)
+        errs = []
+        for h in (0, 11, 22, 31):
+            ro, _ = oracle.attention_fwd(qh[0, srows, h], kh[0, :, h], vh[0, :, h], w.scale, causal, 0, q_pos=srows,
+                                         nq=8192)
+            errs.append(_errors(o64[0, srows, h], ro))
+        err = (max(e[0] for e in errs), float(np.mean([e[1] for e in errs])))
+        F = fwd_flops(1, 32, 8192, 128, causal)
+        if causal and headline_cpu:
+            secs, nh = headline_cpu["seconds"], int(headline_cpu["sample"].split()[0])
+        else:
+            _, secs = _oracle_timed(lambda: oracle.attention_fwd(qh[0, :, 0], kh[0, :, 0], vh[0, :, 0], w.scale, causal,
+                                                                 0))
+            nh = 1
+        name = "cfg3_fwd_bf16_b1_h32_n8192_d128_" + ("causal" if causal else "noncausal")
+        prof = "fwd_bf16_n8192_d128_causal.sq_counters.txt" if causal else "fwd_bf16_n8192_d128_noncausal.sq_counters.txt"
+        mfma_row(name, lambda c=causal: fa.fa_fwd(q, k, v, causal=c), F, nbytes, PEAK_BF16_TFLOPS, err, secs,
+                 fwd_flops(1, nh, 8192, 128, causal), f"{nh} of 32 heads, fp64", counters_from_profile(prof, fsha))
+    # the same causal call with the inputs evicted from the 256 MB last-level
+    # cache (MALL) before every call: two input sets (402 MB) in turn
+    t2 = workload_inputs("llama_n8192_noncausal")
+    q2, k2, v2 = (x.cuda() * 1 for x in (t2["q"], t2["k"], t2["v"]))
+    sets = [(q, k, v), (q2, k2, v2)]
+    state = {"i": 0}
+
+    def alternate():
+        qq, kk, vv = sets[state["i"] & 1]
+        state["i"] += 1
+        fa.fa_fwd(qq, kk, vv, causal=True)
+
+    med, mn = timed(alternate)
+    F = fwd_flops(1, 32, 8192, 128, True)
+    rows["cfg3_fwd_causal_two_input_sets"] = {
+        "median_us": round(med * 1e3, 1), "min_us": round(mn * 1e3, 1), "tflops": round(F / med / 1e9, 1),
+        "note": "Q/K/V of one call are 201 MB and stay resident in the 256 MB MALL between repeated calls; "
+                "alternating two input sets (402 MB) makes every call read them from HBM"}
+    log(f"[bench] cfg3_fwd_causal_two_input_sets: {json.dumps(rows['cfg3_fwd_causal_two_input_sets'])}")
+    del q2, k2, v2, sets
+
+    # configuration 5 (fp8): the same shape in e4m3 with per-tensor scales, causal
+    t8 = workload_inputs("fp8_n8192")
+    q8, k8, v8 = (t8[x].cuda() for x in ("q8", "k8", "v8"))
+    ds = (t8["q_scale"], t8["k_scale"], t8["v_scale"])
+    o, _ = fa.fa_fwd(q8, k8, v8, causal=True, descale=ds)
+    o64 = f64(o)
+    deq = [oracle.fp8_dequant(t8[x].view(torch.uint8).numpy(), sc) for x, sc in zip(("q8", "k8", "v8"), ds)]
+    errs = []
+    for h in (0, 11, 22, 31):
+        ro, _ = oracle.attention_fwd(deq[0][0, srows, h], deq[1][0, :, h], deq[2][0, :, h], w.scale, True, 0,
+                                     q_pos=srows, nq=8192)
+        errs.append(_errors(o64[0, srows, h], ro))
+    err = (max(e[0] for e in errs), float(np.mean([e[1] for e in errs])))
+    _, secs = _oracle_timed(lambda: oracle.attention_fwd(deq[0][0, :, 0], deq[1][0, :, 0], deq[2][0, :, 0], w.scale,
+                                                         True, 0))
+    F = fwd_flops(1, 32, 8192, 128, True)
+    mfma_row("cfg5_fwd_fp8_b1_h32_n8192_d128_causal", lambda: fa.fa_fwd(q8, k8, v8, causal=True, descale=ds), F,
+             3 * 8192 * 32 * 128 + 2 * 8192 * 32 * 128 + 4 * 32 * 8192, PEAK_FP8_TFLOPS, err, secs,
+             fwd_flops(1, 1, 8192, 128, True), "1 of 32 heads, fp64 on the dequantised inputs",
+             counters_from_profile("fwd_fp8_n8192_d128_causal.sq_counters.txt", psha))
+    del q8, k8, v8, deq
+
+    # configuration 5 (backward): B1 H32 N8192 d128 bf16 causal, fp32 gradients
+    w = WORKLOADS["bwd_n8192"]
+    t = workload_inputs("bwd_n8192")
+    qb, kb, vb, dob = (t[x].cuda() for x in ("q", "k", "v", "dout"))
+    o, lse = fa.fa_fwd(qb, kb, vb, causal=True)
+    dq, dk, dv = (torch.empty(x.shape, dtype=torch.float32, device="cuda") for x in (qb, kb, vb))
+    bwd = lambda: fa.fa_bwd(dob, qb, kb, vb, o, lse, causal=True, dq=dq, dk=dk, dv=dv)  # noqa: E731
+    bwd()
+    g64 = [f64(x)[0, :, 0] for x in (dq, dk, dv)]
+    ref, secs = _oracle_timed(lambda: oracle.attention_bwd(*(f64(t[x])[0, :, 0] for x in ("q", "k", "v", "dout")),
+                                                           w.scale, True, 0))
+    errs = [_errors(g, r) for g, r in zip(g64, ref)]
+    err = (max(e[0] for e in errs), float(np.mean([e[1] for e in errs])))
+    F = 2.5 * fwd_flops(1, 32, 8192, 128, True)
+    mfma_row("cfg5_bwd_bf16_b1_h32_n8192_d128_causal", bwd, F,
+             5 * 2 * 8192 * 32 * 128 + 4 * 32 * 8192 + 3 * 4 * 8192 * 32 * 128, PEAK_BF16_TFLOPS, err, secs,
+             2.5 * fwd_flops(1, 1, 8192, 128, True), "head 0 of 32 (all its dQ, dK, dV), fp64",
+             counters_from_profile("bwd_bf16_n8192_d128_causal.sq_counters.txt", bsha))
+    # dropout (p = 0.1) forward and backward at the same shape
+    kw = dict(causal=True, dropout_p=0.1, seed=1234, offset=0)
+    od, lsed = fa.fa_fwd(qb, kb, vb, **kw)
+    F = fwd_flops(1, 32, 8192, 128, True)
+    mfma_row("fwd_bf16_n8192_causal_dropout0.1", lambda: fa.fa_fwd(qb, kb, vb, **kw), F,
+             2 * (4 * 8192 * 32 * 128) + 4 * 32 * 8192, PEAK_BF16_TFLOPS, None, None, 0, None)
+    mfma_row("bwd_bf16_n8192_causal_dropout0.1",
+             lambda: fa.fa_bwd(dob, qb, kb, vb, od, lsed, dq=dq, dk=dk, dv=dv, **kw), 2.5 * F,
+             5 * 2 * 8192 * 32 * 128 + 4 * 32 * 8192 + 3 * 4 * 8192 * 32 * 128, PEAK_BF16_TFLOPS, None, None, 0,
+             None)
+    del qb, kb, vb, dob, o, lse, od, lsed, dq, dk, dv
+
+    # configuration 4: packed varlen, 32768 tokens, H28 d128, causal + window 4096; and its backward
+    w = WORKLOADS["varlen_32k"]
+    t = workload_inputs("varlen_bwd_32k")
+    q, k, v, do, cu = (t[x].cuda() for x in ("q", "k", "v", "dout", "cu_seqlens"))
+    mx = max(t["lengths"])
+    o, lse = fa.fa_varlen_fwd(q, k, v, cu, mx, causal=True, window=w.window)
+    o64 = f64(o)
+    cuh = t["cu_seqlens"].numpy()
+    qh, kh, vh = f64(t["q"]), f64(t["k"]), f64(t["v"])
+    errs, osecs = [], 0.0
+    for s_ in range(len(t["lengths"])):
+        a_, b_ = int(cuh[s_]), int(cuh[s_ + 1])
+        rr = np.unique(np.concatenate([[0, b_ - a_ - 1], np.random.default_rng(s_).choice(b_ - a_, 6, False)]))
+        for h in (0, 27):
+            ro, _ = oracle.attention_fwd(qh[a_ + rr, h], kh[a_:b_, h], vh[a_:b_, h], w.scale, True, w.window,
+                                         q_pos=rr, nq=b_ - a_)
+            errs.append(_errors(o64[a_ + rr, h], ro))
+        _, sec = _oracle_timed(lambda: oracle.attention_fwd(qh[a_:b_, 0], kh[a_:b_, 0], vh[a_:b_, 0], w.scale, True,
+                                                            w.window))
+        osecs += sec
+    err = (max(e[0] for e in errs), float(np.mean([e[1] for e in errs])))
+    pairs = visible_pairs_varlen(t["lengths"], True, w.window)
+    F = 4.0 * w.head_dim * w.heads * pairs
+    mfma_row("cfg4_varlen_fwd_bf16_32k_h28_d128_causal_w4096",
+             lambda: fa.fa_varlen_fwd(q, k, v, cu, mx, causal=True, window=w.window), F,
+             2 * (4 * 32768 * 28 * 128) + 4 * 28 * 32768, PEAK_BF16_TFLOPS, err, osecs, 4.0 * 128 * pairs,
+             "head 0 of 28, all sequences, fp64", counters_from_profile("varlen_fwd_bf16_32k_h28_w4096.sq_counters.txt", fsha),
+             extra={"lengths": t["lengths"]})
+    dq, dk, dv = (torch.empty(x.shape, dtype=torch.float32, device="cuda") for x in (q, k, v))
+    mfma_row("varlen_bwd_bf16_32k_h28_d128_causal_w4096",
+             lambda: fa.fa_varlen_bwd(do, q, k, v, o, lse, cu, mx, causal=True, window=w.window, dq=dq, dk=dk, dv=dv),
+             2.5 * F, 5 * 2 * 32768 * 28 * 128 + 4 * 28 * 32768 + 3 * 4 * 32768 * 28 * 128, PEAK_BF16_TFLOPS, None,
+             None, 0, None, counters_from_profile("varlen_bwd_bf16_32k_h28_w4096.sq_counters.txt", bsha))
+    del q, k, v, do, o, lse, dq, dk, dv
+
+    # HBM-bound rows: partial-result merge, KV-cache decode steps
+    o_p, lse_p, out, lse, nbytes = merge_inputs(torch)
+    hbm_row("merge_8parts_f32_b1_n8192_h32_d128", lambda: fa.fa_merge(o_p, lse_p, out=out, lse=lse), nbytes)
+    del o_p, lse_p, out, lse
+    fn, nbytes = kvcache_step(torch, fa)
+    hbm_row("kvcache_decode_b8_h32_d128_8k", fn, nbytes)
+    fn, nbytes = kvcache_step(torch, fa, page=256)
+    hbm_row("kvcache_paged256_decode_b8_h32_d128_8k", fn, nbytes)
+    return rows
 
 
 MERGE_PARTS = 8
@@ -168,109 +427,6 @@ def kvcache_step(torch, fa, page=0):
     fn = lambda: fa.fa_fwd_kvcache(q, kc, vc, kn, vn, cache_seqlens=seq, causal=True, out=out, lse=lse,
                                    block_table=table)
     return fn, nbytes
-
-
-def extra_rows(torch, fa, steps):
-    """Timings of the other hot-path rows (median per call, HIP events)."""
-    from exact_attention_24_amd.inputs import WORKLOADS, workload_inputs
-    rows = {}
-
-    def med(xs):
-        xs = sorted(xs)
-        return xs[len(xs) // 2]
-
-    # non-causal forward
-    t = {k_: v_.cuda() for k_, v_ in workload_inputs("llama_n8192").items()}
-    _, ms = time_calls(lambda: fa.fa_fwd(t["q"], t["k"], t["v"], causal=False), 2, steps, torch)
-    f = fwd_flops(1, 32, 8192, 128, False)
-    rows["fwd_noncausal_n8192"] = {"ms": round(med(ms), 4), "tflops": round(f / med(ms) / 1e9, 1)}
-    # backward
-    try:
-        w = WORKLOADS["bwd_n8192"]
-        t = {k_: v_.cuda() for k_, v_ in workload_inputs("bwd_n8192").items() if hasattr(v_, "cuda")}
-        o, lse = fa.fa_fwd(t["q"], t["k"], t["v"], causal=True)
-        _, ms = time_calls(lambda: fa.fa_bwd(t["dout"], t["q"], t["k"], t["v"], o, lse, causal=True), 2, steps,
-                           torch)
-        f = 2.5 * fwd_flops(1, 32, 8192, 128, True)
-        rows["bwd_causal_n8192"] = {"ms": round(med(ms), 4), "tflops": round(f / med(ms) / 1e9, 1)}
-    except Exception as e:  # not available in this build
-        rows["bwd_causal_n8192"] = {"error": str(e)[:120]}
-    # dropout (p = 0.1) forward and backward at the same shape
-    try:
-        t = {k_: v_.cuda() for k_, v_ in workload_inputs("bwd_n8192").items() if hasattr(v_, "cuda")}
-        kw = dict(causal=True, dropout_p=0.1, seed=1234, offset=0)
-        _, ms = time_calls(lambda: fa.fa_fwd(t["q"], t["k"], t["v"], **kw), 2, steps, torch)
-        f = fwd_flops(1, 32, 8192, 128, True)
-        rows["fwd_causal_dropout0.1_n8192"] = {"ms": round(med(ms), 4), "tflops": round(f / med(ms) / 1e9, 1)}
-        o, lse = fa.fa_fwd(t["q"], t["k"], t["v"], **kw)
-        _, ms = time_calls(lambda: fa.fa_bwd(t["dout"], t["q"], t["k"], t["v"], o, lse, **kw), 2, steps, torch)
-        rows["bwd_causal_dropout0.1_n8192"] = {"ms": round(med(ms), 4), "tflops": round(2.5 * f / med(ms) / 1e9, 1)}
-    except Exception as e:
-        rows["fwd_causal_dropout0.1_n8192"] = {"error": str(e)[:120]}
-    # varlen
-    try:
-        w = WORKLOADS["varlen_32k"]
-        t = workload_inputs("varlen_32k")
-        q, k, v, cu = (t[x].cuda() for x in ("q", "k", "v", "cu_seqlens"))
-        mx = max(t["lengths"])
-        _, ms = time_calls(lambda: fa.fa_varlen_fwd(q, k, v, cu, mx, causal=True, window=w.window), 2, steps,
-                           torch)
-        f = 4.0 * w.head_dim * w.heads * visible_pairs_varlen(t["lengths"], True, w.window)
-        rows["varlen_32k_w4096"] = {"ms": round(med(ms), 4), "tflops": round(f / med(ms) / 1e9, 1)}
-    except Exception as e:
-        rows["varlen_32k_w4096"] = {"error": str(e)[:120]}
-    # varlen backward
-    try:
-        w = WORKLOADS["varlen_bwd_32k"]
-        t = workload_inputs("varlen_bwd_32k")
-        q, k, v, do, cu = (t[x].cuda() for x in ("q", "k", "v", "dout", "cu_seqlens"))
-        mx = max(t["lengths"])
-        o, lse = fa.fa_varlen_fwd(q, k, v, cu, mx, causal=True, window=w.window)
-        _, ms = time_calls(lambda: fa.fa_varlen_bwd(do, q, k, v, o, lse, cu, mx, causal=True, window=w.window),
-                           2, steps, torch)
-        f = 2.5 * 4.0 * w.head_dim * w.heads * visible_pairs_varlen(t["lengths"], True, w.window)
-        rows["varlen_bwd_32k_w4096"] = {"ms": round(med(ms), 4), "tflops": round(f / med(ms) / 1e9, 1)}
-    except Exception as e:
-        rows["varlen_bwd_32k_w4096"] = {"error": str(e)[:120]}
-    # merge of partial results
-    try:
-        o_p, lse_p, out, lse, nbytes = merge_inputs(torch)
-        _, ms = time_calls(lambda: fa.fa_merge(o_p, lse_p, out=out, lse=lse), 2, steps, torch)
-        gbs = nbytes / med(ms) / 1e6
-        rows["merge_8parts_n8192"] = {"ms": round(med(ms), 4), "GB/s": round(gbs, 1),
-                                      "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
-        del o_p, lse_p, out, lse
-    except Exception as e:
-        rows["merge_8parts_n8192"] = {"error": str(e)[:120]}
-    # KV-cache decode step
-    try:
-        fn, nbytes = kvcache_step(torch, fa)
-        _, ms = time_calls(fn, 2, steps, torch)
-        gbs = nbytes / med(ms) / 1e6
-        rows["kvcache_decode_b8_h32_8k"] = {"ms": round(med(ms), 4), "GB/s": round(gbs, 1),
-                                            "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
-    except Exception as e:
-        rows["kvcache_decode_b8_h32_8k"] = {"error": str(e)[:120]}
-    try:
-        fn, nbytes = kvcache_step(torch, fa, page=256)
-        _, ms = time_calls(fn, 2, steps, torch)
-        gbs = nbytes / med(ms) / 1e6
-        rows["kvcache_paged256_decode_b8_h32_8k"] = {"ms": round(med(ms), 4), "GB/s": round(gbs, 1),
-                                                     "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
-    except Exception as e:
-        rows["kvcache_paged256_decode_b8_h32_8k"] = {"error": str(e)[:120]}
-    # fp8 forward
-    try:
-        t = workload_inputs("fp8_n8192")
-        q8, k8, v8 = (t[x].cuda() for x in ("q8", "k8", "v8"))
-        ds = (t["q_scale"], t["k_scale"], t["v_scale"])
-        _, ms = time_calls(lambda: fa.fa_fwd(q8, k8, v8, causal=True, descale=ds), 2, steps, torch)
-        f = fwd_flops(1, 32, 8192, 128, True)
-        rows["fp8_fwd_causal_n8192"] = {"ms": round(med(ms), 4), "tflops": round(f / med(ms) / 1e9, 1),
-                                        "frac_fp8_peak": round(f / med(ms) / 1e9 / PEAK_FP8_TFLOPS, 4)}
-    except Exception as e:
-        rows["fp8_fwd_causal_n8192"] = {"error": str(e)[:120]}
-    return rows
 
 
 WORKLOAD_CHOICES = ("fwd_causal", "fwd_noncausal", "bwd", "varlen", "varlen_bwd", "fp8", "merge", "kvcache")
@@ -386,10 +542,8 @@ def main():
 
     # the kernel's code depends on its source file and the shared device headers
     sha = src_hash(src, "fa_device.h", "fa_internal.h")
-    rows = {} if (args.no_rows or not headline) else extra_rows(torch, fa, max(5, min(args.steps, 20)))
-    if rows:
-        log(f"[bench] rows: {json.dumps(rows)}")
     cpu = None if (args.no_cpu_baseline or not headline) else cpu_baseline(args.cpu_budget)
+    rows = {} if (args.no_rows or not headline) else config_rows(torch, fa, max(5, min(args.steps, 20)), cpu)
 
     out = {
         "metric": "attention fwd TFLOP/s + % MFMA peak, bf16 causal N=8192 d=128, 1 GPU" if headline else
@@ -405,7 +559,9 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic: seeded i.i.d. N(0,1) inputs (see exact_attention_24_amd/inputs.py)",
-        "config": {"workload": desc, "parallelism": "none (1 GPU)"},
+        "config": {"workload": desc, "parallelism": "none (1 GPU)",
+                   "inputs": "resident in HBM; the 201 MB of Q/K/V also stay in the 256 MB MALL between calls "
+                             "(rows.cfg3_fwd_causal_two_input_sets times the same call with them evicted)"},
         "pct_mfma_peak" if unit == "TFLOP/s" else "pct_hbm_peak": round(100 * value / peak, 2),
         "roofline": {"bound": "mfma" if unit == "TFLOP/s" else "hbm", "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),

@@ -226,8 +226,7 @@ fa_status fa_check_fwd(const fa_fwd_params *p) {
   if ((st = check_tensor("k", p->k, p->k_stride, 3, eb, k_empty, p->seqlen_k, hd)) != FA_OK) return st;
   if ((st = check_tensor("v", p->v, p->v_stride, 3, eb, k_empty, p->seqlen_k, hd)) != FA_OK) return st;
   if ((st = check_tensor("o", p->o, p->o_stride, 3, ob, q_empty, p->seqlen_q, hd)) != FA_OK) return st;
-  const int64_t items = ceil_div(p->seqlen_q, fa::fwd_block_rows(p->qkv_dtype, p->head_dim)) *
-                        (int64_t)p->heads * p->batch;
+  const int64_t items = ceil_div(p->seqlen_q, fa::kFwdMinBlockRows) * (int64_t)p->heads * p->batch;
   if (items > INT32_MAX) return fail(FA_ERR_INVALID_ARGUMENT, "problem too large for one launch");
   return ok();
 }
@@ -252,8 +251,7 @@ fa_status fa_check_varlen_fwd(const fa_varlen_fwd_params *p) {
   if ((st = check_tensor("k", p->k, p->k_stride, 2, eb, empty, tt, hd)) != FA_OK) return st;
   if ((st = check_tensor("v", p->v, p->v_stride, 2, eb, empty, tt, hd)) != FA_OK) return st;
   if ((st = check_tensor("o", p->o, p->o_stride, 2, ob, empty, tt, hd)) != FA_OK) return st;
-  const int64_t items = ceil_div(p->max_seqlen, fa::fwd_block_rows(p->qkv_dtype, p->head_dim)) *
-                        (int64_t)p->heads * p->num_seqs;
+  const int64_t items = ceil_div(p->max_seqlen, fa::kFwdMinBlockRows) * (int64_t)p->heads * p->num_seqs;
   if (items > INT32_MAX) return fail(FA_ERR_INVALID_ARGUMENT, "problem too large for one launch");
   return ok();
 }
@@ -333,7 +331,9 @@ fa_status fa_fwd(const fa_fwd_params *p, void *stream) {
   a.o_sb = p->o_stride[0]; a.o_st = p->o_stride[1]; a.o_sh = p->o_stride[2];
   a.lse_sb = (int64_t)p->heads * p->seqlen_q; a.lse_sh = p->seqlen_q;
   a.batch = p->batch; a.heads = p->heads; a.nq = p->seqlen_q; a.nk = p->seqlen_k;
-  a.nqt = (int32_t)ceil_div(p->seqlen_q, fa::fwd_block_rows(p->qkv_dtype, p->head_dim));
+  a.br = fa::fwd_block_rows(p->qkv_dtype, p->head_dim, (int64_t)p->batch * p->heads, p->seqlen_q, p->causal,
+                            false, fa::persistent_groups());
+  a.nqt = (int32_t)ceil_div(p->seqlen_q, a.br);
   a.causal = p->causal; a.window = p->window;
   a.scale_log2 = p->softmax_scale * kLog2e * p->q_descale * p->k_descale;
   a.v_descale = p->v_descale;
@@ -360,7 +360,9 @@ fa_status fa_varlen_fwd(const fa_varlen_fwd_params *p, void *stream) {
   a.o_sb = 0; a.o_st = p->o_stride[0]; a.o_sh = p->o_stride[1];
   a.lse_sb = 0; a.lse_sh = p->total_tokens;
   a.batch = p->num_seqs; a.heads = p->heads; a.nq = p->max_seqlen; a.nk = p->max_seqlen;
-  a.nqt = (int32_t)ceil_div(p->max_seqlen, fa::fwd_block_rows(p->qkv_dtype, p->head_dim));
+  a.br = fa::fwd_block_rows(p->qkv_dtype, p->head_dim, (int64_t)p->num_seqs * p->heads, p->max_seqlen, p->causal,
+                            true, fa::persistent_groups());
+  a.nqt = (int32_t)ceil_div(p->max_seqlen, a.br);
   a.causal = p->causal; a.window = p->window;
   a.scale_log2 = p->softmax_scale * kLog2e * p->q_descale * p->k_descale;
   a.v_descale = p->v_descale;

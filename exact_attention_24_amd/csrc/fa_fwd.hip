@@ -975,10 +975,25 @@ int persistent_groups() {
   return cached[dev];
 }
 
-int fwd_block_rows(int qkv_dtype, int head_dim) {
+int fwd_block_rows(int qkv_dtype, int head_dim, int64_t batch_heads, int64_t nq, bool causal, bool varlen,
+                   int cus) {
   (void)head_dim;
   if (qkv_dtype == 0) return 64;  // fp32 kernel: 4 waves x 16 rows
-  return 256;                     // bf16 and fp8 kernels: 8 waves x 32 rows
+  if (qkv_dtype != 1) return 256;  // fp8 kernel
+  const int64_t want = cus > 0 ? cus : 256;
+  // 256 rows where that launch runs persistently (dense causal calls pair
+  // their tiles, so they need twice the tiles): below that, CUs idle behind
+  // the longest work-groups, and 128-row tiles measured faster
+  const int64_t t256 = (nq + 255) / 256;
+  if (batch_heads * (causal && !varlen ? (t256 + 1) / 2 : t256) >= want) return 256;
+  if (batch_heads * ((nq + 127) / 128) >= want) return 128;
+  return 64;
+}
+
+template <int D, int NW>
+void launch_drop_kernel(const FwdArgs &p, dim3 g, hipStream_t s) {
+  if (p.drop_k) hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, true>), g, dim3(NW * 64), 0, s, p);
+  else hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, false>), g, dim3(NW * 64), 0, s, p);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, int head_dim, hipStream_t s) {
@@ -988,7 +1003,16 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, int head_dim, hipStream_t s) {
   const int64_t units = (int64_t)a.batch * a.heads * (a.causal ? (a.nqt + 1) / 2 : a.nqt);
   p.persist = !a.cu_seqlens && cus >= 8 && units >= cus;
   if (p.persist) g = dim3((unsigned)cus);
-  if (a.drop_k) {
+  if (a.br < 256) {
+    // short sequences: 4 or 2 waves of 32 rows per work-group, one work item each
+    if (a.br == 128) {
+      if (head_dim == 128) launch_drop_kernel<128, 4>(p, g, s);
+      else launch_drop_kernel<64, 4>(p, g, s);
+    } else {
+      if (head_dim == 128) launch_drop_kernel<128, 2>(p, g, s);
+      else launch_drop_kernel<64, 2>(p, g, s);
+    }
+  } else if (a.drop_k) {
     if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_kernel<128, 8, true>), g, dim3(512), 0, s, p);
     else hipLaunchKernelGGL((fwd_bf16_kernel<64, 8, true>), g, dim3(512), 0, s, p);
   } else {

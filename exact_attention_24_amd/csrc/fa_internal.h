@@ -22,6 +22,7 @@ struct FwdArgs {
   int64_t lse_sb, lse_sh;     // lse element strides: batch, head (token stride 1)
   int32_t batch, heads, nq, nk;  // varlen: nq = nk = max_seqlen (grid sizing only)
   int32_t nqt;                   // query tiles per (batch, head)
+  int32_t br;                    // query rows per tile (fwd_block_rows)
   int32_t causal, window;
   float scale_log2;              // softmax_scale * log2(e) (* q, k descales for fp8)
   float v_descale;               // fp8 only, 1 otherwise
@@ -110,7 +111,16 @@ hipError_t launch_decode(const DecodeArgs &a, int head_dim, hipStream_t s);
 // rounded down to a multiple of the 8 XCDs (0 if it cannot be read).
 int persistent_groups();
 
-// Query-tile rows per work-group of each forward kernel (grid sizing).
-int fwd_block_rows(int qkv_dtype, int head_dim);
+// Query rows per work-group of the forward for a call (the tile table):
+// bf16 calls take 256 rows (the ping-pong kernel) when that launch has at
+// least one unit of work per CU (a causal dense unit is a pair of tiles),
+// else 128 rows (4 waves) if that gives one work-group per CU, else 64 (2
+// waves), so that short sequences still spread over the chip; packed calls
+// count sequences x heads tiles of max_seqlen rows.  fp8 takes 256, fp32
+// 64.  `cus` is the device's CU count (0: unknown).
+int fwd_block_rows(int qkv_dtype, int head_dim, int64_t batch_heads, int64_t nq, bool causal, bool varlen,
+                   int cus);
+// Smallest tile any call may take (bounds of the host checks).
+constexpr int kFwdMinBlockRows = 64;
 
 }  // namespace fa

@@ -871,20 +871,35 @@ __device__ __forceinline__ void dq_item(const BwdArgs &a, int b, int h, int qt) 
 }
 // dQ items: query tiles of 256, high ones carry the most work under a causal
 // mask.  Dense calls with at least one unit per CU run persistently (see
-// launch_units); the item body is called from one place, on the kernel's own
-// by-value argument block (a reference to it would push it to scratch).
+// launch_units), packed calls with up to kPackedSeqs sequences on the
+// schedule built from cu_seqlens (persist 2); the item body is called from one
+// place, on the kernel's own by-value argument block (a reference to it would
+// push it to scratch).
 template <int D, bool DROP>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
+  __shared__ int s_key[kPackedSeqs], s_order[kPackedSeqs], s_first[kPackedSeqs + 1];
   const int nqt = (a.nq + 255) / 256;
   const bool varlen = a.cu_seqlens != nullptr;
-  const UnitRange r = launch_units(a.persist, a.batch, a.heads, nqt, a.causal);
-  for (int u = r.lo; u < r.hi; u += r.step)
-    for (int j = 0; j < 2; ++j) {
-      int b, h, qt;
-      if (!launch_tile(a.persist, r, u, j, a.batch, a.heads, nqt, varlen, a.causal, false, b, h, qt)) break;
-      dq_item<D, DROP>(a, b, h, qt);
-      lds_barrier();  // the next item's DMA reuses the LDS tiles
+  const bool packed = a.persist == 2;
+  // a causal pair carries equal work only without a window
+  PackedSchedule ps{s_key, s_order, s_first, a.batch, a.heads, 0, a.causal && a.window <= 0};
+  if (packed) packed_schedule_build(ps, a.cu_seqlens, 256);
+  const UnitRange r = launch_units(a.persist == 1, a.batch, a.heads, nqt, a.causal);
+  for (int i = 0;; ++i) {
+    int b, h, qt;
+    if (packed) {
+      const int st = packed_schedule_item(ps, i, a.causal, false, b, h, qt);
+      if (st < 0) break;
+      if (st == 0) continue;
+    } else {
+      const int u = r.lo + (i >> 1) * r.step;
+      if (u >= r.hi) break;
+      if (!launch_tile(a.persist == 1, r, u, i & 1, a.batch, a.heads, nqt, varlen, a.causal, false, b, h, qt))
+        continue;
     }
+    dq_item<D, DROP>(a, b, h, qt);
+    lds_barrier();  // the next item's DMA reuses the LDS tiles
+  }
 }
 
 
@@ -1433,7 +1448,11 @@ hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t s) {
     else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)kv_items), dim3(NW_KV * 64), 0, s, a);
   }
   BwdArgs pq;
-  const int64_t q_grid = plan((a.nq + 256 - 1) / 256, pq);
+  int64_t q_grid = plan((a.nq + 256 - 1) / 256, pq);
+  if (a.cu_seqlens && cus >= 8 && a.batch <= kPackedSeqs && q_grid > 0) {  // packed: schedule from cu_seqlens
+    pq.persist = 2;
+    q_grid = cus;
+  }
   if (q_grid > 0) {
     if (a.drop_k) hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)q_grid), dim3(256), 0, s, pq);
     else hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)q_grid), dim3(256), 0, s, pq);

@@ -233,6 +233,86 @@ __device__ __forceinline__ bool launch_tile(bool persist, const UnitRange &r, in
   return j == 0 || heavy != light;
 }
 
+// ---------------------------------------------------------------------------
+// Persistent schedule of a packed (cu_seqlens) call, derived on the device.
+// The host does not know the sequence lengths, so every work-group builds the
+// same tables in LDS: tiles of `rows` rows per sequence, sequences ranked
+// longest first, and the first unit of each ranked sequence.  A unit is one
+// (sequence, head, tile), or under `pair` the two tiles n - 1 - i and i of a
+// sequence, which together carry as much work as any other pair.  Unit k goes
+// to slot k mod 2G, or 2G - 1 - (k mod 2G) on the way back (a snake over
+// decreasing unit sizes, close to longest-processing-time first); slots are
+// numbered XCD-major (slot = (block % 8) G / 8 + block / 8), so consecutive
+// units of one (sequence, head) share an XCD's L2.
+// ---------------------------------------------------------------------------
+constexpr int kPackedSeqs = 512;  // packed calls with more sequences take one work-group per item
+struct PackedSchedule {
+  int *key;    // [kPackedSeqs] tiles of sequence i
+  int *order;  // [kPackedSeqs] sequences, longest first
+  int *first;  // [kPackedSeqs + 1] first unit of each ranked sequence
+  int nseq, heads, units;
+  bool pair;
+};
+// All threads of the work-group; ends with a barrier.
+__device__ __forceinline__ void packed_schedule_build(PackedSchedule &ps, const int32_t *cu, int rows) {
+  const int tid = threadIdx.x, nseq = ps.nseq;
+  for (int i = tid; i < nseq; i += blockDim.x) ps.key[i] = max(0, cu[i + 1] - cu[i] + rows - 1) / rows;
+  __syncthreads();
+  for (int i = tid; i < nseq; i += blockDim.x) {
+    const int ki = ps.key[i];
+    int rank = 0;
+    for (int j = 0; j < nseq; ++j) {
+      const int kj = ps.key[j];
+      rank += kj > ki || (kj == ki && j < i);
+    }
+    ps.order[rank] = i;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int r = 0; r < nseq; ++r) {
+      ps.first[r] = acc;
+      const int nt = ps.key[ps.order[r]];
+      acc += ps.heads * (ps.pair ? (nt + 1) / 2 : nt);
+    }
+    ps.first[nseq] = acc;
+  }
+  __syncthreads();
+  ps.units = ps.first[nseq];
+}
+// Item i (0, 1, ...) of this work-group: 1 and (seq, head, tile) for an
+// item, 0 for a slot with nothing to do, -1 when the work-group is done.
+// heavy_low: low tile indices carry the most work (key tiles under a causal
+// mask) rather than high ones (query tiles); the heavier tile of a pair or
+// the sequence's heaviest tiles come first.
+__device__ __forceinline__ int packed_schedule_item(const PackedSchedule &ps, int i, bool causal, bool heavy_low,
+                                                    int &seq, int &h, int &tile) {
+  const int G = gridDim.x, slot = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+  const int lap = i >> 2, e = i & 3;  // e / 2: outward or return slot of the lap; e % 2: tile of a pair
+  const int k0 = lap * 2 * G;
+  if (k0 >= ps.units) return -1;
+  const int k = k0 + ((e >> 1) == 0 ? slot : 2 * G - 1 - slot);
+  if (k >= ps.units) return 0;
+  int lo = 0, hi = ps.nseq;  // the ranked sequence r with first[r] <= k < first[r + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (ps.first[mid] <= k) lo = mid;
+    else hi = mid;
+  }
+  seq = ps.order[lo];
+  const int nt = ps.key[seq], per = ps.pair ? (nt + 1) / 2 : nt;
+  const int local = k - ps.first[lo], u = local % per;
+  h = local / per;
+  const int heavy = (causal && !heavy_low) ? nt - 1 - u : u;
+  if (e & 1) {
+    if (!ps.pair || heavy == nt - 1 - heavy) return 0;  // no second tile in this unit
+    tile = nt - 1 - heavy;
+  } else {
+    tile = heavy;
+  }
+  return 1;
+}
+
 // Work-group barrier for LDS reuse only: waits for this wave's LDS accesses,
 // not for its global stores to retire (__syncthreads would wait for both).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }

@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cfloat>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -42,6 +43,15 @@ fa_status ok() {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// The kernels' exponent factor scale * log2(e) (* fp8 descales).  At scale 0
+// it is the smallest normal float instead: every finite score then still
+// gives 2^(s c - m) = 1 exactly in fp32 (|s c| < 2^-100), as scale 0 does,
+// while masked scores (-inf) stay -inf rather than becoming -inf * 0 = NaN.
+float exp2_factor(float scale, float descale) {
+  const float c = scale * kLog2e * descale;
+  return c > 0.f ? c : FLT_MIN;
+}
+
 bool valid_dtype(int d) { return d == FA_F32 || d == FA_BF16 || d == FA_FP8_E4M3; }
 
 int dtype_bytes(fa_dtype d) { return d == FA_F32 ? 4 : d == FA_BF16 ? 2 : 1; }
@@ -62,8 +72,10 @@ fa_status check_fwd_common(fa_dtype qkv, fa_dtype o, int32_t heads, int32_t head
   if (heads < 0) return fail(FA_ERR_INVALID_ARGUMENT, "heads must be >= 0 (got %d)", heads);
   if (head_dim != 64 && head_dim != 128)
     return fail(FA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
-  if (!(std::isfinite(scale) && scale > 0.f))
-    return fail(FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0 (got %g)", (double)scale);
+  // applied as given; 0 gives every visible key the same weight.  The kernels
+  // take the row max of the unscaled scores, so a negative scale is refused.
+  if (!(std::isfinite(scale) && scale >= 0.f))
+    return fail(FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0 (got %g)", (double)scale);
   if (causal != 0 && causal != 1)
     return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", causal);
   if (window < 0) return fail(FA_ERR_INVALID_ARGUMENT, "window must be >= 0 (got %d)", window);
@@ -174,8 +186,10 @@ fa_status check_bwd_common(fa_dtype qkv, fa_dtype grad, int heads, int head_dim,
   if (heads < 0) return fail(FA_ERR_INVALID_ARGUMENT, "heads must be >= 0 (got %d)", heads);
   if (head_dim != 64 && head_dim != 128)
     return fail(FA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
-  if (!(std::isfinite(scale) && scale > 0.f))
-    return fail(FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0 (got %g)", (double)scale);
+  // applied as given; 0 gives every visible key the same weight.  The kernels
+  // take the row max of the unscaled scores, so a negative scale is refused.
+  if (!(std::isfinite(scale) && scale >= 0.f))
+    return fail(FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0 (got %g)", (double)scale);
   if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", causal);
   if (window < 0) return fail(FA_ERR_INVALID_ARGUMENT, "window must be >= 0 (got %d)", window);
   if (deterministic != 0 && deterministic != 1)
@@ -335,7 +349,7 @@ fa_status fa_fwd(const fa_fwd_params *p, void *stream) {
                             false, fa::persistent_groups());
   a.nqt = (int32_t)ceil_div(p->seqlen_q, a.br);
   a.causal = p->causal; a.window = p->window;
-  a.scale_log2 = p->softmax_scale * kLog2e * p->q_descale * p->k_descale;
+  a.scale_log2 = exp2_factor(p->softmax_scale, p->q_descale * p->k_descale);
   a.v_descale = p->v_descale;
   a.lazy = lazy_threshold(p->causal, p->window);
   set_dropout(a, p->dropout_p, p->dropout_seed, p->dropout_offset);
@@ -364,7 +378,7 @@ fa_status fa_varlen_fwd(const fa_varlen_fwd_params *p, void *stream) {
                             true, fa::persistent_groups());
   a.nqt = (int32_t)ceil_div(p->max_seqlen, a.br);
   a.causal = p->causal; a.window = p->window;
-  a.scale_log2 = p->softmax_scale * kLog2e * p->q_descale * p->k_descale;
+  a.scale_log2 = exp2_factor(p->softmax_scale, p->q_descale * p->k_descale);
   a.v_descale = p->v_descale;
   a.lazy = lazy_threshold(p->causal, p->window);
   set_dropout(a, p->dropout_p, p->dropout_seed, p->dropout_offset);
@@ -411,7 +425,7 @@ fa_status fa_bwd(const fa_bwd_params *p, void *workspace, size_t workspace_bytes
   a.causal = p->causal; a.window = p->window; a.deterministic = p->deterministic;
   a.grad_f32 = p->grad_dtype == FA_F32;
   a.scale = p->softmax_scale;
-  a.scale_log2 = p->softmax_scale * kLog2e;
+  a.scale_log2 = exp2_factor(p->softmax_scale, 1.f);
   set_dropout(a, p->dropout_p, p->dropout_seed, p->dropout_offset);
   return launched(fa::launch_bwd_bf16(a, p->head_dim, reinterpret_cast<hipStream_t>(stream)));
 }
@@ -467,7 +481,7 @@ fa_status fa_varlen_bwd(const fa_varlen_bwd_params *p, void *workspace, size_t w
   a.causal = p->causal; a.window = p->window; a.deterministic = p->deterministic;
   a.grad_f32 = p->grad_dtype == FA_F32;
   a.scale = p->softmax_scale;
-  a.scale_log2 = p->softmax_scale * kLog2e;
+  a.scale_log2 = exp2_factor(p->softmax_scale, 1.f);
   set_dropout(a, p->dropout_p, p->dropout_seed, p->dropout_offset);
   return launched(fa::launch_bwd_bf16(a, p->head_dim, reinterpret_cast<hipStream_t>(stream)));
 }
@@ -528,8 +542,8 @@ fa_status fa_check_kvcache(const fa_kvcache_params *p) {
     return fail(FA_ERR_UNSUPPORTED, "the KV-cache decode takes at most 8 query rows (got %d)", p->seqlen_q);
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(FA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", p->head_dim);
-  if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f))
-    return fail(FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0 (got %g)", (double)p->softmax_scale);
+  if (!(std::isfinite(p->softmax_scale) && p->softmax_scale >= 0.f))
+    return fail(FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0 (got %g)", (double)p->softmax_scale);
   if (p->causal != 0 && p->causal != 1)
     return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", p->causal);
   if (p->window < 0) return fail(FA_ERR_INVALID_ARGUMENT, "window must be >= 0 (got %d)", p->window);
@@ -596,7 +610,7 @@ fa_status fa_fwd_kvcache(const fa_kvcache_params *p, void *workspace, size_t wor
   a.batch = p->batch; a.nq = p->seqlen_q; a.cache_len = p->cache_len; a.heads = p->heads;
   a.causal = p->causal; a.window = p->window; a.num_splits = splits;
   a.split_len = splits == 1 ? p->cache_len : (int)((((int64_t)p->cache_len + splits - 1) / splits + 63) / 64 * 64);
-  a.scale_log2 = p->softmax_scale * kLog2e;
+  a.scale_log2 = exp2_factor(p->softmax_scale, 1.f);
   a.block_table = p->block_table;
   if (p->block_table) {
     a.max_blocks = p->max_blocks_per_seq;

@@ -138,7 +138,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // AGPRs), so the compiler never shuttles them between files.  The compiler
 // does not see these as MFMAs, so the waits the hardware does not enforce
 // are the caller's: an MFMA result is read by any other instruction only
-// after mfma_drain*() (>= 11 wait states after an 8-pass XDL op), and a VALU
+// after mfma_drain*() (the hardware needs >= 11 wait states after an 8-pass
+// XDL op such as v_mfma_f32_32x32x16_bf16; the drains give 16), and a VALU
 // write of an operand precedes its MFMA read by >= 2 wait states.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x4 vec4(const uint4 &x) { return (u32x4){x.x, x.y, x.z, x.w}; }

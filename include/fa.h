@@ -33,8 +33,10 @@
  *     on `stream` (a hipStream_t; NULL = the default stream) and returns.
  *   - Strides are in ELEMENTS; the last (head_dim) dimension must be
  *     contiguous (stride 1) and every row must start 16-byte aligned.
- *   - head_dim must be 64 or 128.  softmax_scale must be finite and > 0
- *     (callers pass 1/sqrt(head_dim) for the usual default).
+ *   - head_dim must be 64 or 128.  softmax_scale is applied as given and
+ *     must be finite and >= 0 (callers pass 1/sqrt(head_dim) for the usual
+ *     default; 0 gives every visible key the same weight, so O is the mean of
+ *     V over the visible keys and LSE = ln(number of visible keys)).
  *   - causal: key j is visible to query i iff j <= i + (Nk - Nq)
  *     (bottom-right alignment; for Nq == Nk this is j <= i).
  *   - window W > 0: additionally j > i + (Nk - Nq) - W, i.e. each query sees
@@ -145,9 +147,10 @@ typedef struct {
  *   lse [batch, heads, seqlen_q] fp32 from the forward of the same inputs.
  *   dq [batch, seqlen_q, heads, head_dim], dk, dv [batch, seqlen_k, heads,
  *   head_dim] in grad_dtype (FA_F32, the default of the Python layer, or
- *   FA_BF16).  deterministic = 1 computes dQ without atomics, so repeated
- *   calls give bitwise identical gradients; 0 allows a faster atomic dQ
- *   reduction whose rounding may vary from call to call.
+ *   FA_BF16).  deterministic (0 or 1, the pages' deterministic= argument):
+ *   both settings run the same atomic-free kernels -- dQ has a kernel of its
+ *   own rather than a cross-work-group reduction -- so repeated calls always
+ *   give bitwise identical gradients.
  *   workspace: device memory of fa_bwd_workspace_bytes(p) bytes, 256-byte
  *   aligned, owned by the caller; its contents on entry are ignored. */
 typedef struct {
@@ -174,8 +177,8 @@ typedef struct {
  *   cu_seqlens, max_seqlen: as in fa_varlen_fwd, with the same unchecked
  *   device-side contracts.  Every token of every sequence gets its dq, dk,
  *   dv written (zero for a token that neither sees nor is seen by any other).
- *   deterministic: accepted for symmetry with fa_bwd; this path never uses
- *   atomics, so repeated calls are always bitwise identical.
+ *   deterministic: as in fa_bwd (no atomics either way; repeated calls are
+ *   bitwise identical).
  *   workspace: fa_varlen_bwd_workspace_bytes(p) bytes of device memory,
  *   256-byte aligned, owned by the caller; contents on entry are ignored. */
 typedef struct {

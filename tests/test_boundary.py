@@ -98,8 +98,8 @@ def test_valid_params_pass(lib):
     ("window", -3, B.FA_ERR_INVALID_ARGUMENT, "window must be >= 0 (got -3)"),
     ("causal", 2, B.FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got 2)"),
     ("head_dim", 96, B.FA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got 96)"),
-    ("softmax_scale", 0.0, B.FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0"),
-    ("softmax_scale", float("nan"), B.FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0"),
+    ("softmax_scale", -0.5, B.FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0"),
+    ("softmax_scale", float("nan"), B.FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0"),
     ("seqlen_q", -1, B.FA_ERR_INVALID_ARGUMENT, "sizes must be >= 0"),
     ("q_descale", 2.0, B.FA_ERR_INVALID_ARGUMENT, "descales must be 1 for non-fp8 inputs"),
     ("o_dtype", B.FA_F32, B.FA_ERR_DTYPE_MISMATCH, "Input and output tensors must have the same dtype"),

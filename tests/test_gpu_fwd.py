@@ -5,7 +5,7 @@ import pytest
 import torch
 
 import oracle
-from exact_attention_24_amd import fa_fwd
+from exact_attention_24_amd import fa_bwd, fa_fwd
 from exact_attention_24_amd.inputs import WORKLOADS, dense_inputs, workload_inputs
 from tests.parity import assert_close, assert_lse_close, f64, sample_rows
 
@@ -188,3 +188,27 @@ def test_empty_inputs():
     o, lse = fa_fwd(q, kv, kv)
     torch.cuda.synchronize()
     assert (o.float() == 0).all() and torch.isneginf(lse).all()
+
+
+@pytest.mark.parametrize("causal,window,nq,nk", [(True, 0, 700, 700), (True, 40, 700, 700), (False, 100, 300, 500),
+                                                 (True, 0, 200, 600)])
+def test_scale_zero_is_the_mean_over_visible_keys(causal, window, nq, nk):
+    """softmax_scale = 0 weighs every visible key equally: O is the mean of V
+    over them and LSE = ln(their count) (a closed form the oracle is pinned
+    to); this checks the masks and the running sums on every tile size."""
+    q, _, _ = dense_inputs(1, nq, 3, 128, "bf16", seed=nq + 5)
+    _, k, v = dense_inputs(1, nk, 3, 128, "bf16", seed=nk + 6)
+    o, lse = _run(q, k, v, causal, window, scale=0.0)
+    ro, rl = _oracle(q, k, v, 0.0, causal, window)
+    assert_close(f64(o), ro)
+    assert_lse_close(f64(lse), rl)
+    cnt = oracle.visible(np.arange(nq), nk, causal, window, offset=nk - nq).sum(axis=1)
+    assert_lse_close(f64(lse)[0], np.broadcast_to(np.where(cnt > 0, np.log(np.maximum(cnt, 1)), -np.inf), (3, nq)))
+    # backward: scale 0 makes dQ = dK = 0 exactly; dV = P^T dO with uniform P
+    do = dense_inputs(1, nq, 3, 128, "bf16", seed=nq + 7)[0]
+    dq, dk, dv = fa_bwd(do.to(DEV), q.to(DEV), k.to(DEV), v.to(DEV), o.to(DEV), lse.to(DEV), causal=causal,
+                        window=window, softmax_scale=0.0)
+    torch.cuda.synchronize()
+    assert (dq.cpu() == 0).all() and (dk.cpu() == 0).all()
+    _, _, rv = oracle.mha_bwd(f64(q), f64(k), f64(v), f64(do), 0.0, causal, window)
+    assert_close(f64(dv), rv, what="dV")

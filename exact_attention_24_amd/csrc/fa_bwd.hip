@@ -191,6 +191,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int off = nk - nq;
   const int wk0 = k0 + 32 * wave;
   const int my_k = wk0 + ql;
+  // query rows (indices, not positions) that see this lane's key
+  const VisRange vq = vis_range(causal ? (int64_t)my_k - off : 0,
+                                min((int64_t)nq - 1, window > 0 ? (int64_t)my_k + window - 1 - off : (int64_t)INT32_MAX));
 
   const uint16_t *qbase = (const uint16_t *)a.q + b * a.q_sb + (int64_t)seq0 * a.q_st + h * a.q_sh;
   const uint16_t *dobase = (const uint16_t *)a.dout + b * a.do_sb + (int64_t)seq0 * a.do_st + h * a.do_sh;
@@ -368,15 +371,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     mfma_drain2_v(s[0], s[1]);
     mfma_drain2_v(dp[0], dp[1]);
     if (MASK) {
+      const uint32_t vo = vis_offset(vq, q0 + 4 * hf);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qpos = q0 + qb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3) + off;
-          const bool ok = (!causal || my_k <= qpos) && (window <= 0 || my_k > qpos - window) &&
-                          qpos - off < nq;
-          if (!ok) s[qb][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (!vis(vo, vq, qb * 32 + 8 * (r >> 2) + (r & 3))) s[qb][r] = -INFINITY;
     }
     // ---- phase B: the previous tile's products, this tile's P and dS
     constexpr int EPS = 32 / NB;  // elements started per stage
@@ -575,6 +575,14 @@ __device__ __forceinline__ void dq_item(const BwdArgs &a, int b, int h, int qt) 
   const int wq0 = q0 + QW * wave;
   const bool wave_rows = wq0 < nq;
   const int wp_lo = wq0 + off, wp_hi = min(wq0 + QW - 1, nq - 1) + off;
+  // keys that this lane's two query rows see (no length limit: past the end
+  // K loads as zero rows, so those keys add nothing to dQ)
+  VisRange vk[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int my_p = wq0 + 32 * qb + ql + off;
+    vk[qb] = vis_range(window > 0 ? (int64_t)my_p - window + 1 : 0, causal ? (int64_t)my_p : (int64_t)INT32_MAX);
+  }
   auto active = [&](int k0) __attribute__((always_inline)) {  // 32 keys from k0
     return wave_rows && (!causal || k0 <= wp_hi) && (window <= 0 || k0 + 31 > wp_lo - window);
   };
@@ -736,13 +744,10 @@ __device__ __forceinline__ void dq_item(const BwdArgs &a, int b, int h, int qt) 
     if (MASK) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const int my_p = wq0 + 32 * qb + ql + off;
+        const uint32_t vo = vis_offset(vk[qb], k0 + 4 * hf);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = k0 + 8 * (e >> 2) + 4 * hf + (e & 3);
-          const bool ok = (!causal || key <= my_p) && (window <= 0 || key > my_p - window);
-          if (!ok) s[qb][e] = -INFINITY;
-        }
+        for (int e = 0; e < 16; ++e)
+          if (!vis(vo, vk[qb], 8 * (e >> 2) + (e & 3))) s[qb][e] = -INFINITY;
       }
     }
     // ---- dP MFMAs; meanwhile P = 2^(s c - lse2) in place

@@ -319,6 +319,30 @@ __device__ __forceinline__ int packed_schedule_item(const PackedSchedule &ps, in
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // ---------------------------------------------------------------------------
+// Masks as index ranges.  The causal, window and length limits leave each row
+// (or column) an inclusive range [lo, hi] of visible partner positions.  With
+// lo >= 0 and hi < 2^31, position base + c lies in it iff the unsigned 32-bit
+// value c - (lo - base) is at most hi - lo: per element one subtract from a
+// constant and one compare, where testing the limits one by one costs three
+// compares and their combination.  An empty range is lo = 2^31, span 0, which
+// no position below 2^31 passes.
+// ---------------------------------------------------------------------------
+struct VisRange {
+  uint32_t lo, span;
+};
+__device__ __forceinline__ VisRange vis_range(int64_t lo, int64_t hi) {
+  lo = lo < 0 ? 0 : lo;
+  hi = hi > 0x7FFFFFFF ? 0x7FFFFFFF : hi;
+  if (hi < lo) return {0x80000000u, 0u};
+  return {(uint32_t)lo, (uint32_t)(hi - lo)};
+}
+// lo - base, computed once per tile
+__device__ __forceinline__ uint32_t vis_offset(const VisRange &v, int base) { return v.lo - (uint32_t)base; }
+__device__ __forceinline__ bool vis(uint32_t offset, const VisRange &v, int c) {
+  return (uint32_t)c - offset <= v.span;
+}
+
+// ---------------------------------------------------------------------------
 // Dropout randomness: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel
 // random numbers: as easy as 1, 2, 3", SC 2011).  Each round multiplies words
 // 0 and 2 by 0xD2511F53 / 0xCD9E8D57 into 64-bit products and forms

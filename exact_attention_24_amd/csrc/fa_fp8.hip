@@ -128,6 +128,8 @@ __device__ __forceinline__ void fp8_item(const FwdArgs &a, int b, int h, int qt)
   const int wp_lo = wq0 + off, wp_hi = min(wq0 + 31, nq - 1) + off;
   const int my_q = wq0 + ql;
   const int my_p = my_q + off;
+  // keys this lane's query row may see
+  const VisRange vr = vis_range(window > 0 ? (int64_t)my_p - window + 1 : 0, causal ? min(nk - 1, my_p) : nk - 1);
   auto active = [&](int jt) __attribute__((always_inline)) {
     const int k0 = jt * BC;
     return wave_rows && (!causal || k0 <= wp_hi) && (window <= 0 || k0 + BC - 1 > wp_lo - window);
@@ -246,14 +248,12 @@ __device__ __forceinline__ void fp8_item(const FwdArgs &a, int b, int h, int qt)
     if (act) {
       qk(kbuf(jt));
       if (MASK) {
+        const uint32_t vo = vis_offset(vr, k0 + 4 * hf);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            const bool ok = key < nk && (!causal || key <= my_p) && (window <= 0 || key > my_p - window);
-            if (!ok) s[kb][r] = -INFINITY;
-          }
+          for (int r = 0; r < 16; ++r)
+            if (!vis(vo, vr, kb * 32 + 8 * (r >> 2) + (r & 3))) s[kb][r] = -INFINITY;
       }
     }
     rescale_prev();

@@ -161,6 +161,8 @@ __device__ __forceinline__ void drop_item(const FwdArgs &a, int b, int h, int qt
   const int wp_lo = wq0 + off, wp_hi = min(wq0 + 31, nq - 1) + off;
   const int my_q = wq0 + ql;
   const int my_p = my_q + off;
+  // keys this lane's query row may see
+  const VisRange vr = vis_range(window > 0 ? (int64_t)my_p - window + 1 : 0, causal ? min(nk - 1, my_p) : nk - 1);
   const uint32_t slot = (uint32_t)(b * a.heads + h);  // dropout counter word 2
   // dropout randomness of key block (2 jt + kb) for this lane's query
   auto drop_init = [&](Philox &x, int jt, int kb) __attribute__((always_inline)) {
@@ -231,14 +233,12 @@ __device__ __forceinline__ void drop_item(const FwdArgs &a, int b, int h, int qt
   auto softmax = [&](auto mask_tag, int k0, uint4 (&pb)[4]) __attribute__((always_inline)) -> float {
     constexpr bool MASK = decltype(mask_tag)::value;
     if (MASK) {
+      const uint32_t vo = vis_offset(vr, k0 + 4 * hf);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
-          const bool ok = key < nk && (!causal || key <= my_p) && (window <= 0 || key > my_p - window);
-          if (!ok) s[kb][e] = -INFINITY;
-        }
+        for (int e = 0; e < 16; ++e)
+          if (!vis(vo, vr, kb * 32 + 8 * (e >> 2) + (e & 3))) s[kb][e] = -INFINITY;
     }
     float mx = s[0][0];
 #pragma unroll
@@ -484,8 +484,12 @@ constexpr int kOP = D + 8;
 // LDS of the ping-pong kernel: the K and V rings, or the staged O tile
 template <int D>
 constexpr int kPPLds = (4 * 64 * D > 256 * kOP<D>) ? 4 * 64 * D : 256 * kOP<D>;
-// one (batch or sequence b, head h, query tile qt) work item
-template <int D>
+// one (batch or sequence b, head h, query tile qt) work item.  RANGE: edge
+// tiles test each key against the row's visible range with one compare
+// (packed calls, where short sequences make most tiles edge tiles); else
+// against each limit in turn, which holds fewer registers through the loop
+// (measured 1-2% faster on dense calls, whose edge tiles are few).
+template <int D, bool RANGE>
 __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, uint16_t *smem) {
   constexpr int BR = 256, BC = 64;
   constexpr int TS = BC * D;                  // tile elements
@@ -659,7 +663,17 @@ __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, 
   auto softmax = [&](auto mask_tag, int v) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int k0 = v * BC;
-    if (MASK) {
+    if constexpr (MASK && RANGE) {
+      // keys this lane's query row may see (formed here, on edge tiles only,
+      // so that it holds no registers through the loop)
+      const VisRange vr = vis_range(window > 0 ? (int64_t)my_p - window + 1 : 0, causal ? min(nk - 1, my_p) : nk - 1);
+      const uint32_t vo = vis_offset(vr, k0 + 4 * hf);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (!vis(vo, vr, kb * 32 + 8 * (e >> 2) + (e & 3))) s[kb][e] = -INFINITY;
+    } else if constexpr (MASK) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -839,7 +853,7 @@ __device__ __forceinline__ void pp_varlen_persistent(const FwdArgs &a, uint16_t 
       const int local = k - s_first[lo], h = local / per, i = local % per;
       const int heavy = a.causal ? nt - 1 - i : i;  // high query tiles first under a causal mask
       if ((e & 1) && (!pair || heavy == i)) continue;  // no second tile in this unit
-      pp_item<D>(a, sq, h, (e & 1) ? i : heavy, smem);
+      pp_item<D, true>(a, sq, h, (e & 1) ? i : heavy, smem);
       lds_barrier();  // the next item's DMA reuses the LDS that the epilogue read
     }
 }
@@ -858,7 +872,7 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_pp_kernel(FwdArgs a) {
       if (!launch_tile(a.persist, r, u, j, a.batch, a.heads, a.nqt, a.cu_seqlens != nullptr, a.causal, false, b, h,
                        qt))
         break;
-      pp_item<D>(a, b, h, qt, smem);
+      pp_item<D, false>(a, b, h, qt, smem);
       lds_barrier();  // the next item's DMA reuses the LDS that the epilogue read
     }
 }

@@ -318,6 +318,16 @@ __device__ __forceinline__ int packed_schedule_item(const PackedSchedule &ps, in
 // not for its global stores to retire (__syncthreads would wait for both).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// max of three floats in one v_max3_f32.  fmaxf compiles to v_max3_f32 too,
+// but first quiets a possible signalling NaN in every operand it cannot prove
+// canonical (MFMA results among them) with an extra v_max_f32 x, x; no input
+// here is a signalling NaN, so those are skipped.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // Masks as index ranges.  The causal, window and length limits leave each row
 // (or column) an inclusive range [lo, hi] of visible partner positions.  With

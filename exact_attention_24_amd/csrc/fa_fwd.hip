@@ -683,15 +683,22 @@ __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, 
           if (!ok) s[kb][e] = -INFINITY;
         }
     }
-    float mp[4];  // four partial maxima: short dependency chains
+    // row max over the lane's 32 scores: four chains of v_max3 (16 in all)
+    auto sv = [&](int i) __attribute__((always_inline)) { return s[i >> 4][i & 15]; };
+    float mp[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) mp[j] = fmaxf(s[j >> 1][(j & 1) * 8], s[j >> 1][(j & 1) * 8 + 1]);
+    for (int j = 0; j < 4; ++j) mp[j] = max3f(sv(3 * j), sv(3 * j + 1), sv(3 * j + 2));
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int i = 12; i < 28; i += 8)
 #pragma unroll
-      for (int e = 2; e < 8; ++e) mp[j] = fmaxf(mp[j], s[j >> 1][(j & 1) * 8 + e]);
-    float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
-    mx = half_swap_max(mx) * c;
+      for (int j = 0; j < 4; ++j) mp[j] = max3f(mp[j], sv(i + 2 * j), sv(i + 2 * j + 1));
+    mp[0] = max3f(mp[0], sv(28), sv(29));
+    mp[1] = max3f(mp[1], sv(30), sv(31));
+    float mx = max3f(max3f(mp[0], mp[1], mp[2]), mp[3], mp[3]);
+    {  // with lane l ^ 32, which holds the rest of the row
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = max3f(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1])) * c;
+    }
     const bool up = mx > m + a.lazy;
     alpha = up ? fast_exp2(m - mx) : 1.f;
     m = up ? mx : m;

@@ -703,14 +703,15 @@ __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, 
     alpha = up ? fast_exp2(m - mx) : 1.f;
     m = up ? mx : m;
     const float m_use = m == -INFINITY ? 0.f : m;
-    float rp[4] = {0.f, 0.f, 0.f, 0.f};
+    float rp[4];  // four partial row sums, each started from its first term
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float p = fast_exp2(__builtin_fmaf(s[kb][e], c, -m_use));
         s[kb][e] = p;
-        rp[(kb * 16 + e) & 3] += p;
+        const int i = kb * 16 + e;
+        rp[i & 3] = i < 4 ? p : rp[i & 3] + p;
       }
     l = l * alpha + ((rp[0] + rp[1]) + (rp[2] + rp[3]));
 #pragma unroll

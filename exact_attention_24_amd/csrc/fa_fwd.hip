@@ -38,6 +38,8 @@
 // with K/V staged through registers into padded tiles.
 
 #include <hip/hip_runtime.h>
+
+#include <cfloat>
 #include <stdint.h>
 
 #include <type_traits>
@@ -602,7 +604,11 @@ __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, 
   uint4 pb[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) pb[i] = (uint4){0u, 0u, 0u, 0u};
-  float m = -INFINITY, l = 0.f, alpha = 1.f;
+  // The running max starts at -FLT_MAX, not -inf: the first finite score
+  // of a row replaces it (alpha = 2^(-FLT_MAX - mx) = 0 then, on an O and l
+  // that are still 0), and a row whose scores are all masked keeps it and
+  // gets p = 2^(-inf) = 0, so the exponent's offset needs no -inf guard.
+  float m = -FLT_MAX, l = 0.f, alpha = 1.f;
   const float c = a.scale_log2;
 
   // MFMA cluster: S(u+1) = K(u+1) Q^T (kb chains interleaved), then
@@ -702,13 +708,12 @@ __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, 
     const bool up = mx > m + a.lazy;
     alpha = up ? fast_exp2(m - mx) : 1.f;
     m = up ? mx : m;
-    const float m_use = m == -INFINITY ? 0.f : m;
     float rp[4];  // four partial row sums, each started from its first term
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = fast_exp2(__builtin_fmaf(s[kb][e], c, -m_use));
+        const float p = fast_exp2(__builtin_fmaf(s[kb][e], c, -m));
         s[kb][e] = p;
         const int i = kb * 16 + e;
         rp[i & 3] = i < 4 ? p : rp[i & 3] + p;

@@ -21,6 +21,8 @@
 // 2^-6 up to 448 (subnormals to 2^-9).
 
 #include <hip/hip_runtime.h>
+
+#include <cfloat>
 #include <stdint.h>
 
 #include "fa_device.h"
@@ -194,7 +196,10 @@ __device__ __forceinline__ void fp8_item(const FwdArgs &a, int b, int h, int qt)
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
-  float m = -INFINITY, l = 0.f;
+  // the running max starts at -FLT_MAX, not -inf: the first finite score of
+  // a row replaces it, and a row whose scores are all masked keeps it and
+  // gets p = 2^(-inf) = 0, so the exponent's offset needs no -inf guard
+  float m = -FLT_MAX, l = 0.f;
   const float c = a.scale_log2;  // includes the q and k descales
   f32x16 s[2];
   uint4 pb0_prev = {0u, 0u, 0u, 0u}, pb1_prev = {0u, 0u, 0u, 0u};
@@ -260,7 +265,7 @@ __device__ __forceinline__ void fp8_item(const FwdArgs &a, int b, int h, int qt)
     const uint8_t *vs = vbuf(jt - 1);
     uint4 vlo, vhi;
     vfrag(vs, 0, vlo, vhi);
-    float mx = 0.f, m_use = 0.f, rs = 0.f;
+    float mx = 0.f, mx1 = 0.f, rs[2] = {0.f, 0.f};
     __builtin_amdgcn_sched_barrier(0);
     // stages: 0 max, 1 max + new m, 2..5 exponentials (8 each), 6 pack;
     // the product MFMA of block db is issued at stage 2 db (its operand
@@ -278,28 +283,41 @@ __device__ __forceinline__ void fp8_item(const FwdArgs &a, int b, int h, int qt)
       }
       if (act) {
         if (i == 0) {
-          mx = s[0][0];
+          // row max as two chains of v_max3 over the 32 scores
+          mx = max3f(s[0][0], s[0][1], s[0][2]);
+          mx1 = max3f(s[0][3], s[0][4], s[0][5]);
 #pragma unroll
-          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+          for (int r = 6; r < 14; r += 4) {
+            mx = max3f(mx, s[0][r], s[0][r + 1]);
+            mx1 = max3f(mx1, s[0][r + 2], s[0][r + 3]);
+          }
+          mx = max3f(mx, s[0][14], s[0][15]);
         } else if (i == 1) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-          mx = half_swap_max(mx) * c;
+          for (int r = 0; r < 16; r += 4) {
+            mx = max3f(mx, s[1][r], s[1][r + 1]);
+            mx1 = max3f(mx1, s[1][r + 2], s[1][r + 3]);
+          }
+          mx = max3f(mx, mx1, mx1);
+          {  // with lane l ^ 32, which holds the rest of the row
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = max3f(__uint_as_float(sw[0]), __uint_as_float(sw[1]), __uint_as_float(sw[1])) * c;
+          }
           // the running max moves only when a row max jumps by more than
           // a.lazy <= 8 (P~ <= 256 stays inside e4m3's range of 448)
           const bool up = mx > m + a.lazy;
           alpha = up ? fast_exp2(m - mx) : 1.f;
           m = up ? mx : m;
-          m_use = m == -INFINITY ? 0.f : m;
         } else if (i < 6) {
           const int kb = (i - 2) >> 1, r0 = ((i - 2) & 1) * 8;
 #pragma unroll
           for (int r = r0; r < r0 + 8; ++r) {
-            const float p = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
+            const float p = fast_exp2(__builtin_fmaf(s[kb][r], c, -m));
             s[kb][r] = p;
-            rs += p;
+            // two partial sums, each started from its first term
+            rs[r & 1] = (i == 2 && r < 2) ? p : rs[r & 1] + p;
           }
-          if (i == 5) l = l * alpha + rs;
+          if (i == 5) l = l * alpha + (rs[0] + rs[1]);
         } else if (i == 6) {
           // B operand bytes b = 0..31 <- (kb, r) = (b / 16, b % 16)
           pb0.x = pack_fp8x4(s[0][0], s[0][1], s[0][2], s[0][3]);

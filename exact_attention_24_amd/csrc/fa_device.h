@@ -327,6 +327,12 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
 }
+// half_swap_max through max3f: the row max with lane l ^ 32, without the
+// NaN-quieting instructions that fmaxf adds
+__device__ __forceinline__ float swap_max3(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max3f(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
+}
 
 // ---------------------------------------------------------------------------
 // Masks as index ranges.  The causal, window and length limits leave each row

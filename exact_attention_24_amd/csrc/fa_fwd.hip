@@ -196,7 +196,10 @@ __device__ __forceinline__ void drop_item(const FwdArgs &a, int b, int h, int qt
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = (f32x16){};
-  float m = -INFINITY, l = 0.f;
+  // the running max starts at -FLT_MAX, not -inf: the first finite score of
+  // a row replaces it, and a row whose scores are all masked keeps it and
+  // gets p = 2^(-inf) = 0, so the exponent's offset needs no -inf guard
+  float m = -FLT_MAX, l = 0.f;
   const float c = a.scale_log2;
   f32x16 s[2];
   uint4 pb_prev[4] = {};   // P~ of the previous tile (B operands)
@@ -242,26 +245,28 @@ __device__ __forceinline__ void drop_item(const FwdArgs &a, int b, int h, int qt
         for (int e = 0; e < 16; ++e)
           if (!vis(vo, vr, kb * 32 + 8 * (e >> 2) + (e & 3))) s[kb][e] = -INFINITY;
     }
-    float mx = s[0][0];
+    // row max: two chains of v_max3 over the lane's 32 scores
+    float mx = max3f(s[0][0], s[0][1], s[0][2]), mx1 = max3f(s[0][3], s[0][4], s[0][5]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
-    mx = half_swap_max(mx) * c;
+    for (int i = 6; i < 30; i += 4) {
+      mx = max3f(mx, s[i >> 4][i & 15], s[(i + 1) >> 4][(i + 1) & 15]);
+      mx1 = max3f(mx1, s[(i + 2) >> 4][(i + 2) & 15], s[(i + 3) >> 4][(i + 3) & 15]);
+    }
+    mx = max3f(mx, s[1][14], s[1][15]);
+    mx = swap_max3(max3f(mx, mx1, mx1)) * c;
     const bool up = mx > m + a.lazy;
     const float alpha = up ? fast_exp2(m - mx) : 1.f;
     m = up ? mx : m;
-    const float m_use = m == -INFINITY ? 0.f : m;
-    float rs = 0.f;
+    float rs[2];  // two partial row sums, each started from its first term
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = fast_exp2(__builtin_fmaf(s[kb][e], c, -m_use));
+        const float p = fast_exp2(__builtin_fmaf(s[kb][e], c, -m));
         s[kb][e] = p;
-        rs += p;
+        rs[e & 1] = (kb == 0 && e < 2) ? p : rs[e & 1] + p;
       }
-    l = l * alpha + rs;
+    l = l * alpha + (rs[0] + rs[1]);
     if constexpr (DROP) {  // the row sum above is of the undropped P~
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -312,7 +317,7 @@ __device__ __forceinline__ void drop_item(const FwdArgs &a, int b, int h, int qt
       uint4 va[NOP];
       va[0] = vread(0);
       va[1] = vread(1);
-      float mx = 0.f, m_use = 0.f, rs = 0.f;
+      float mx = 0.f, mx1 = 0.f, rs[2] = {0.f, 0.f};
       Philox rx[2];
       if constexpr (DROP) {
         drop_init(rx[0], jt, 0);
@@ -330,27 +335,35 @@ __device__ __forceinline__ void drop_item(const FwdArgs &a, int b, int h, int qt
           }
         }
         // softmax stage i
-        if (i == 0) {
-          mx = s[0][0];
+        if (i == 0) {  // row max: two chains of v_max3
+          mx = max3f(s[0][0], s[0][1], s[0][2]);
+          mx1 = max3f(s[0][3], s[0][4], s[0][5]);
 #pragma unroll
-          for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[0][e]);
+          for (int e = 6; e < 14; e += 4) {
+            mx = max3f(mx, s[0][e], s[0][e + 1]);
+            mx1 = max3f(mx1, s[0][e + 2], s[0][e + 3]);
+          }
+          mx = max3f(mx, s[0][14], s[0][15]);
         } else if (i == 1) {
 #pragma unroll
-          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[1][e]);
-          mx = half_swap_max(mx) * c;
+          for (int e = 0; e < 16; e += 4) {
+            mx = max3f(mx, s[1][e], s[1][e + 1]);
+            mx1 = max3f(mx1, s[1][e + 2], s[1][e + 3]);
+          }
+          mx = swap_max3(max3f(mx, mx1, mx1)) * c;
           const bool up = mx > m + a.lazy;
           alpha = up ? fast_exp2(m - mx) : 1.f;
           m = up ? mx : m;
-          m_use = m == -INFINITY ? 0.f : m;
         } else if (i < 10) {
           const int kb = (i - 2) >> 2, e0 = ((i - 2) & 3) * 4;
 #pragma unroll
           for (int e = e0; e < e0 + 4; ++e) {
-            const float p = fast_exp2(__builtin_fmaf(s[kb][e], c, -m_use));
+            const float p = fast_exp2(__builtin_fmaf(s[kb][e], c, -m));
             s[kb][e] = p;
-            rs += p;
+            // two partial row sums, each started from its first term
+            rs[e & 1] = (i == 2 && e < 2) ? p : rs[e & 1] + p;
           }
-          if (i == 9) l = l * alpha + rs;
+          if (i == 9) l = l * alpha + (rs[0] + rs[1]);
         } else if (i < 14) {
           const int cc = i - 10, kb = cc >> 1, r0 = (cc & 1) * 8;
           if constexpr (DROP) drop_apply(rx[kb], s[kb], r0, r0 + 8);  // after the row sum

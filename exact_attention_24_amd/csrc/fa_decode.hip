@@ -98,7 +98,7 @@ template <int D, int NQ, bool PAGED>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr int LPK = D / 8;   // lanes per key row
   constexpr int G = 64 / LPK;  // keys per wave-wide load
-  constexpr int U = 2;         // loads per wave per step
+  constexpr int U = 4;         // loads per wave per step
   constexpr int KW = G * U;    // keys per wave per step
   constexpr int KS = 4 * KW;   // keys per work-group per step
   __shared__ float s_m[4][NQ], s_l[4][NQ];

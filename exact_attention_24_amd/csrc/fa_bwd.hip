@@ -882,13 +882,12 @@ __device__ __forceinline__ void dq_item(const BwdArgs &a, int b, int h, int qt) 
 // push it to scratch).
 template <int D, bool DROP>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
-  __shared__ int s_key[kPackedSeqs], s_order[kPackedSeqs], s_first[kPackedSeqs + 1], s_lev[kPackedLevels + 3];
+  __shared__ int s_key[kPackedSeqs], s_order[kPackedSeqs], s_first[kPackedSeqs + 2];
   const int nqt = (a.nq + 255) / 256;
   const bool varlen = a.cu_seqlens != nullptr;
   const bool packed = a.persist == 2;
-  // a causal pair carries equal work only without a window
-  PackedSchedule ps{s_key, s_order, s_first, s_lev, a.batch, a.heads, a.causal && a.window <= 0};
-  if (packed) packed_schedule_build(ps, a.cu_seqlens, 256, a.causal ? a.window : 0);
+  PackedSchedule ps{s_key, s_order, s_first, a.batch, a.heads};
+  if (packed) packed_schedule_build(ps, a.cu_seqlens, 256, a.causal, a.window);
   const UnitRange r = launch_units(a.persist == 1, a.batch, a.heads, nqt, a.causal);
   for (int i = 0;; ++i) {
     int b, h, qt;

@@ -238,36 +238,39 @@ __device__ __forceinline__ bool launch_tile(bool persist, const UnitRange &r, in
 // Persistent schedule of a packed (cu_seqlens) call over query tiles, derived
 // on the device.  The host does not know the sequence lengths, so every
 // work-group builds the same tables in LDS: tiles of `rows` rows per
-// sequence, sequences ranked longest first, and the units in order of
-// decreasing work.  A unit is one (sequence, head, query tile), or under
-// `pair` (causal, no window) the two tiles n - 1 - i and i of a sequence,
-// which together carry as much work as any other pair of it.
-//   Without levels the units run sequence by sequence in rank order (heads,
-// then tiles, heaviest first), which decreases in work.  Under a causal
-// window that order is a sawtooth instead: query tiles qt >= F see the whole
-// window (all equal), tiles below F see only the keys since the sequence
-// start.  So the full tiles come first, sequence by sequence, and then the
-// partial tiles level by level, qt = F - 1 down to 0, each level over all
-// ranked sequences long enough to have it.
-//   Unit k goes to slot k mod 2G, or 2G - 1 - (k mod 2G) on the way back (a
-// snake over decreasing unit sizes, close to longest-processing-time
-// first); slots are numbered XCD-major (slot = (block % 8) G / 8 +
-// block / 8), so consecutive units of one (sequence, head) share an XCD's L2.
+// sequence, sequences ranked longest first, and the first unit of each ranked
+// sequence.  A unit is one query tile, or two tiles whose work adds up to that
+// of one full tile:
+//   - under a causal mask, tile qt sees qt + 1 tiles' worth of keys until the
+//     window (if any) caps it; with F the first tile the window caps (F = all
+//     tiles without a window), tiles qt >= F are single units of the full
+//     window, and the tiles below F pair up as (f - 1 - i, i), f = min(F, n),
+//     which together see f + 1 tiles' worth, as much as one full tile (the
+//     plain causal case pairs n - 1 - i with i);
+//   - without a causal mask every tile is a unit.
+// So the units of one sequence carry equal work, and ranked longest first the
+// list decreases.  Unit k goes to slot k mod 2G, or 2G - 1 - (k mod 2G) on the
+// way back (a snake over decreasing unit sizes, close to longest-processing-
+// time first); slots are numbered XCD-major (slot = (block % 8) G / 8 +
+// block / 8), so consecutive units, those of one (sequence, head), share an
+// XCD's L2.
 // ---------------------------------------------------------------------------
-constexpr int kPackedSeqs = 512;    // packed calls with more sequences take one work-group per item
-constexpr int kPackedLevels = 512;  // more partial-window levels than this: no level order
+constexpr int kPackedSeqs = 512;  // packed calls with more sequences take one work-group per item
 struct PackedSchedule {
-  int *key;     // [kPackedSeqs] tiles of sequence i
-  int *order;   // [kPackedSeqs] sequences, longest first
-  int *first;   // [kPackedSeqs + 1] first full unit of each ranked sequence
-  int *lfirst;  // [kPackedLevels + 3] first unit of each partial level; then the level count and F
+  int *key;    // [kPackedSeqs] tiles of sequence i
+  int *order;  // [kPackedSeqs] sequences, longest first
+  int *first;  // [kPackedSeqs + 2] first unit of each ranked sequence; then F
   int nseq, heads;
-  bool pair;
-  int units = 0, full = 0, lev_f = 0, nlev = 0;  // lev_f: first full tile (0: no levels)
+  int units = 0, fcap = 0;  // fcap: tiles below it pair up (0: none)
 };
-// All threads of the work-group; ends with a barrier.  window: the call's
-// causal window in positions (0: none), which sets the levels.
-__device__ __forceinline__ void packed_schedule_build(PackedSchedule &ps, const int32_t *cu, int rows, int window) {
+// Units of a sequence of nt tiles: full single tiles, then pairs.
+__device__ __forceinline__ int packed_units(int nt, int fcap) {
+  const int f = min(fcap, nt);
+  return nt - f + (f + 1) / 2;
+}
+// All threads of the work-group; ends with a barrier.
+__device__ __forceinline__ void packed_schedule_build(PackedSchedule &ps, const int32_t *cu, int rows, bool causal,
+                                                      int window) {
   const int tid = threadIdx.x, nseq = ps.nseq;
   for (int i = tid; i < nseq; i += blockDim.x) ps.key[i] = max(0, cu[i + 1] - cu[i] + rows - 1) / rows;
   __syncthreads();
@@ -283,42 +286,24 @@ __device__ __forceinline__ void packed_schedule_build(PackedSchedule &ps, const 
   __syncthreads();
   if (tid == 0) {
     // tile qt sees the whole window iff qt rows >= window - 1
-    int f = 0;
-    if (window > 0 && !ps.pair) f = (int)(((int64_t)window - 1 + rows - 1) / rows);
-    const int maxnt = nseq > 0 ? ps.key[ps.order[0]] : 0;
-    int nlev = min(f, maxnt);
-    if (nlev > kPackedLevels) f = nlev = 0;
+    int fcap = 0;
+    if (causal) fcap = window > 0 ? (int)min((int64_t)0x7FFFFFFF, ((int64_t)window - 1 + rows - 1) / rows) : 0x7FFFFFFF;
     int acc = 0;
     for (int r = 0; r < nseq; ++r) {
       ps.first[r] = acc;
-      const int nt = ps.key[ps.order[r]];
-      acc += ps.heads * (ps.pair ? (nt + 1) / 2 : max(0, nt - f));
+      acc += ps.heads * packed_units(ps.key[ps.order[r]], fcap);
     }
     ps.first[nseq] = acc;
-    ps.full = acc;
-    // level l holds tile qt = nlev - 1 - l of every ranked sequence with more
-    // than qt tiles (a prefix of the ranking, growing as qt falls)
-    int c = 0;
-    for (int l = 0; l < nlev; ++l) {
-      const int qt = nlev - 1 - l;
-      while (c < nseq && ps.key[ps.order[c]] > qt) ++c;
-      ps.lfirst[l] = acc;
-      acc += ps.heads * c;
-    }
-    ps.lfirst[nlev] = acc;
-    ps.lfirst[kPackedLevels + 1] = nlev;
-    ps.lfirst[kPackedLevels + 2] = f;
+    ps.first[nseq + 1] = fcap;
   }
   __syncthreads();
-  ps.full = ps.first[nseq];
-  ps.nlev = ps.lfirst[kPackedLevels + 1];
-  ps.lev_f = ps.lfirst[kPackedLevels + 2];
-  ps.units = ps.lfirst[ps.nlev];
+  ps.units = ps.first[nseq];
+  ps.fcap = ps.first[nseq + 1];
 }
 // Item i (0, 1, ...) of this work-group: 1 and (seq, head, tile) for an
 // item, 0 for a slot with nothing to do, -1 when the work-group is done.
-// Under a causal mask the heavier tile of a pair, or the sequence's highest
-// tiles, come first.
+// The full tiles of a sequence come highest first, then the pairs, the
+// higher tile of each first.
 __device__ __forceinline__ int packed_schedule_item(const PackedSchedule &ps, int i, bool causal, int &seq, int &h,
                                                     int &tile) {
   const int G = gridDim.x, slot = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
@@ -327,20 +312,6 @@ __device__ __forceinline__ int packed_schedule_item(const PackedSchedule &ps, in
   if (k0 >= ps.units) return -1;
   const int k = k0 + ((e >> 1) == 0 ? slot : 2 * G - 1 - slot);
   if (k >= ps.units) return 0;
-  if (k >= ps.full) {  // a partial-window level: one tile per unit
-    if (e & 1) return 0;
-    int lo = 0, hi = ps.nlev;  // the level l with lfirst[l] <= k < lfirst[l + 1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (ps.lfirst[mid] <= k) lo = mid;
-      else hi = mid;
-    }
-    const int j = k - ps.lfirst[lo];
-    seq = ps.order[j / ps.heads];
-    h = j % ps.heads;
-    tile = ps.nlev - 1 - lo;
-    return 1;
-  }
   int lo = 0, hi = ps.nseq;  // the ranked sequence r with first[r] <= k < first[r + 1]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -348,15 +319,20 @@ __device__ __forceinline__ int packed_schedule_item(const PackedSchedule &ps, in
     else hi = mid;
   }
   seq = ps.order[lo];
-  const int nt = ps.key[seq], per = ps.pair ? (nt + 1) / 2 : nt - ps.lev_f;
+  const int nt = ps.key[seq], f = min(ps.fcap, nt), per = nt - f + (f + 1) / 2;
   const int local = k - ps.first[lo], u = local % per;
   h = local / per;
-  const int heavy = causal ? nt - 1 - u : ps.lev_f + u;
+  if (u < nt - f) {  // a full tile
+    if (e & 1) return 0;
+    tile = causal ? nt - 1 - u : u;
+    return 1;
+  }
+  const int j = u - (nt - f), hi_t = f - 1 - j;
   if (e & 1) {
-    if (!ps.pair || heavy == nt - 1 - heavy) return 0;  // no second tile in this unit
-    tile = nt - 1 - heavy;
+    if (hi_t == j) return 0;  // the middle tile stands alone
+    tile = j;
   } else {
-    tile = heavy;
+    tile = hi_t;
   }
   return 1;
 }

@@ -822,15 +822,13 @@ __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, 
 // the item body is called from one place, on the kernel's by-value arguments.
 // Packed varlen calls with up to kPackedSeqs sequences run persistently too,
 // on the schedule that every work-group derives from cu_seqlens
-// (packed_schedule_build: units in decreasing work, dealt in a snake over
-// XCD-major slots).
+// (packed_schedule_build: units of equal work per sequence, sequences longest
+// first, dealt in a snake over XCD-major slots).
 template <int D>
 __device__ __forceinline__ void pp_varlen_persistent(const FwdArgs &a, uint16_t *smem) {
-  __shared__ int s_key[kPackedSeqs], s_order[kPackedSeqs], s_first[kPackedSeqs + 1], s_lev[kPackedLevels + 3];
-  // a causal pair (nqt - 1 - i, i) carries as much work as any other pair of
-  // its sequence only without a window; with one, units are single tiles
-  PackedSchedule ps{s_key, s_order, s_first, s_lev, a.batch, a.heads, a.causal && a.window <= 0};
-  packed_schedule_build(ps, a.cu_seqlens, 256, a.causal ? a.window : 0);
+  __shared__ int s_key[kPackedSeqs], s_order[kPackedSeqs], s_first[kPackedSeqs + 2];
+  PackedSchedule ps{s_key, s_order, s_first, a.batch, a.heads};
+  packed_schedule_build(ps, a.cu_seqlens, 256, a.causal, a.window);
   for (int i = 0;; ++i) {
     int sq, h, qt;
     const int st = packed_schedule_item(ps, i, a.causal, sq, h, qt);

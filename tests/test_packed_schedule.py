@@ -1,44 +1,33 @@
-"""CPU model of the packed persistent schedule (fa_device.h: packed_schedule_build,
-packed_schedule_item): over all work-groups, every (sequence, head, query tile)
-comes out exactly once, for causal / non-causal calls, with and without a window,
-and the unit order under a causal window decreases in work level by level."""
+"""CPU model of the packed persistent schedule (fa_device.h: packed_units,
+packed_schedule_build, packed_schedule_item): over all work-groups, every
+(sequence, head, query tile) comes out exactly once, for causal / non-causal
+calls, with and without a window; and under a causal window the units of a
+sequence carry equal work, so the ranked list decreases."""
 import random
 
 import pytest
 
 ROWS = 256
-LEVELS_MAX = 512
+INT_MAX = 0x7FFFFFFF
+
+
+def units_of(nt, fcap):
+    f = min(fcap, nt)
+    return nt - f + (f + 1) // 2
 
 
 def build(lengths, heads, causal, window):
-    pair = causal and window <= 0
     key = [max(0, n + ROWS - 1) // ROWS for n in lengths]
     order = sorted(range(len(key)), key=lambda i: (-key[i], i))
-    f = 0
-    w = window if causal else 0
-    if w > 0 and not pair:
-        f = (w - 1 + ROWS - 1) // ROWS
-    maxnt = key[order[0]] if key else 0
-    nlev = min(f, maxnt)
-    if nlev > LEVELS_MAX:
-        f = nlev = 0
+    fcap = 0
+    if causal:
+        fcap = min(INT_MAX, (window - 1 + ROWS - 1) // ROWS) if window > 0 else INT_MAX
     first, acc = [], 0
     for r in range(len(key)):
         first.append(acc)
-        nt = key[order[r]]
-        acc += heads * ((nt + 1) // 2 if pair else max(0, nt - f))
+        acc += heads * units_of(key[order[r]], fcap)
     first.append(acc)
-    full = acc
-    lfirst, c = [], 0
-    for lv in range(nlev):
-        qt = nlev - 1 - lv
-        while c < len(key) and key[order[c]] > qt:
-            c += 1
-        lfirst.append(acc)
-        acc += heads * c
-    lfirst.append(acc)
-    return dict(key=key, order=order, first=first, lfirst=lfirst, full=full, units=acc, f=f, nlev=nlev,
-                heads=heads, pair=pair, nseq=len(key))
+    return dict(key=key, order=order, first=first, units=acc, fcap=fcap, heads=heads, nseq=len(key))
 
 
 def item(ps, i, causal, block, grid):
@@ -50,18 +39,6 @@ def item(ps, i, causal, block, grid):
     k = k0 + (slot if (e >> 1) == 0 else 2 * grid - 1 - slot)
     if k >= ps["units"]:
         return 0, None
-    if k >= ps["full"]:
-        if e & 1:
-            return 0, None
-        lo, hi = 0, ps["nlev"]
-        while hi - lo > 1:
-            mid = (lo + hi) >> 1
-            if ps["lfirst"][mid] <= k:
-                lo = mid
-            else:
-                hi = mid
-        j = k - ps["lfirst"][lo]
-        return 1, (ps["order"][j // ps["heads"]], j % ps["heads"], ps["nlev"] - 1 - lo)
     lo, hi = 0, ps["nseq"]
     while hi - lo > 1:
         mid = (lo + hi) >> 1
@@ -71,15 +48,21 @@ def item(ps, i, causal, block, grid):
             hi = mid
     seq = ps["order"][lo]
     nt = ps["key"][seq]
-    per = (nt + 1) // 2 if ps["pair"] else nt - ps["f"]
+    f = min(ps["fcap"], nt)
+    per = nt - f + (f + 1) // 2
     local = k - ps["first"][lo]
     u, h = local % per, local // per
-    heavy = nt - 1 - u if causal else ps["f"] + u
-    if e & 1:
-        if not ps["pair"] or heavy == nt - 1 - heavy:
+    if u < nt - f:
+        if e & 1:
             return 0, None
-        return 1, (seq, h, nt - 1 - heavy)
-    return 1, (seq, h, heavy)
+        return 1, (seq, h, nt - 1 - u if causal else u)
+    j = u - (nt - f)
+    hi_t = f - 1 - j
+    if e & 1:
+        if hi_t == j:
+            return 0, None
+        return 1, (seq, h, j)
+    return 1, (seq, h, hi_t)
 
 
 def run(lengths, heads, causal, window, grid):
@@ -129,25 +112,21 @@ def test_random_lengths():
         assert sorted(got) == sorted(want)
 
 
-def _work(n, qt, window):
+def key_tiles(n, qt, window):
+    """64-key tiles a causal query tile qt of a sequence of n visits (window 0: none)."""
     q0, q1 = qt * ROWS, min(qt * ROWS + ROWS, n) - 1
-    lo = max(0, q0 - window + 1)
+    lo = max(0, q0 - window + 1) if window > 0 else 0
     return (q1 + 1 + 63) // 64 - lo // 64
 
 
-def test_level_order_decreases_in_work():
-    lengths, heads, window = CASES[0][0], 28, 4096
-    ps = build(lengths, heads, True, window)
-    assert ps["f"] == 16 and ps["nlev"] == 16
-    # the partial levels, in order, carry non-increasing work
-    level_work = []
-    for lv in range(ps["nlev"]):
-        qt = ps["nlev"] - 1 - lv
-        seqs = [ps["order"][r] for r in range((ps["lfirst"][lv + 1] - ps["lfirst"][lv]) // heads)]
-        level_work.append(max(_work(lengths[s_], qt, window) for s_ in seqs))
-    assert all(level_work[i] >= level_work[i + 1] for i in range(len(level_work) - 1))
-    # every full tile but a sequence's last (shorter) one carries at least as
-    # much work as the heaviest partial tile
-    for s_, n in enumerate(lengths):
-        for qt in range(ps["f"], (n + ROWS - 1) // ROWS - 1):
-            assert _work(n, qt, window) >= level_work[0]
+@pytest.mark.parametrize("window", [0, 4096, 1000])
+def test_units_of_a_sequence_carry_equal_work(window):
+    """Full tiles and pairs of partial tiles see the same number of key tiles (up to
+    the sequence's last, shorter tile and the middle tile of an odd count)."""
+    ps = build([8192, 5000], 1, True, window)
+    for s_, n in enumerate([8192, 5000]):
+        nt = ps["key"][s_]
+        f = min(ps["fcap"], nt)
+        work = [key_tiles(n, qt, window) for qt in range(f, nt - 1)]
+        work += [key_tiles(n, f - 1 - j, window) + key_tiles(n, j, window) for j in range(f // 2)]
+        assert max(work) - min(work) <= 5, (window, n, work)

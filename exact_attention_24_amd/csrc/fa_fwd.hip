@@ -478,15 +478,16 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------
 // bf16 forward, ping-pong between the two waves of each SIMD (no dropout).
 // A wave alternates two clusters:
-//   M(u): S(u+1) = K(u+1) Q^T, then O = alpha O + V(u)^T P~(u)^T: 32 MFMAs
-//         (d = 128) fed only by their LDS operand reads;
+//   M(u): O = alpha O + V(u)^T P~(u)^T, then S(u+1) = K(u+1) Q^T: 32 MFMAs
+//         per 64 keys (d = 128) fed only by their LDS operand reads (P~(u)
+//         dies before S(u+1) is born, which leaves room for 128-key tiles);
 //   V(u): the online softmax of S(u) into P~(u) (row max, rescale factor,
 //         exponentials, row sum, bf16 packing), and the issue of this wave
 //         group's half of the next K/V tiles as LDS DMA.
 // Waves 0-3 (one per SIMD) run half a step ahead of waves 4-7, and one
 // barrier per half step keeps them there: on every SIMD one wave issues
 // MFMAs back to back while the other works through its VALU cluster.
-// K/V tiles (64 keys) travel HBM -> LDS by buffer_load ... lds, so staging
+// K/V tiles (64 or 128 keys) travel HBM -> LDS by buffer_load ... lds, so staging
 // takes neither registers nor LDS store instructions from the softmax wave;
 // the tiles are stored unpadded with 16-byte chunks XOR-swizzled per row,
 // which keeps the row-wise K reads and the transposed V reads conflict free.
@@ -497,16 +498,17 @@ constexpr int kRA = 3;  // MFMA operands read this many MFMAs ahead
 template <int D>
 constexpr int kOP = D + 8;
 // LDS of the ping-pong kernel: the K and V rings, or the staged O tile
-template <int D>
-constexpr int kPPLds = (4 * 64 * D > 256 * kOP<D>) ? 4 * 64 * D : 256 * kOP<D>;
+template <int D, int BC>
+constexpr int kPPLds = (4 * BC * D > 256 * kOP<D>) ? 4 * BC * D : 256 * kOP<D>;
 // one (batch or sequence b, head h, query tile qt) work item.  RANGE: edge
 // tiles test each key against the row's visible range with one compare
 // (packed calls, where short sequences make most tiles edge tiles); else
 // against each limit in turn, which holds fewer registers through the loop
 // (measured 1-2% faster on dense calls, whose edge tiles are few).
-template <int D, bool RANGE>
+template <int D, bool RANGE, int BC>
 __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, uint16_t *smem) {
-  constexpr int BR = 256, BC = 64;
+  constexpr int BR = 256;
+  constexpr int NKB = BC / 32, NKS = BC / 16;  // 32-key blocks of S, 16-key steps of P.V
   constexpr int TS = BC * D;                  // tile elements
   constexpr int NKK = D / 16, NDB = D / 32;
   constexpr int NBLK = TS * 2 / 1024;         // 1 KB DMA blocks per tile
@@ -612,11 +614,12 @@ __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, 
   f32x16 acc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) acc[i] = (f32x16){};
-  f32x16 s[2];
-  s[0] = s[1] = (f32x16){};
-  uint4 pb[4];
+  f32x16 s[NKB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) pb[i] = (uint4){0u, 0u, 0u, 0u};
+  for (int i = 0; i < NKB; ++i) s[i] = (f32x16){};
+  uint4 pb[NKS];
+#pragma unroll
+  for (int i = 0; i < NKS; ++i) pb[i] = (uint4){0u, 0u, 0u, 0u};
   // The running max starts at -FLT_MAX, not -inf: the first finite score
   // of a row replaces it (alpha = 2^(-FLT_MAX - mx) = 0 then, on an O and l
   // that are still 0), and a row whose scores are all masked keeps it and
@@ -624,30 +627,12 @@ __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, 
   float m = -FLT_MAX, l = 0.f, alpha = 1.f;
   const float c = a.scale_log2;
 
-  // MFMA cluster: S(u+1) = K(u+1) Q^T (kb chains interleaved), then
-  // O = alpha O + V(u)^T P~(u)^T (four independent accumulators in turn)
-  auto m_cluster = [&](int u) __attribute__((always_inline)) {
-    // the MFMA wave issues ahead of its softmax partner on the SIMD (the
-    // arbiter otherwise favours the older wave, i.e. always group 0)
-    __builtin_amdgcn_s_setprio(3);
-    if (u + 1 < jt1 && active(u + 1)) {
-      const uint16_t *ks = smem + kslot(u + 1);
-      auto kread = [&](int i) __attribute__((always_inline)) {
-        const int kb = i & 1, kk = i >> 1;
-        return *(const uint4 *)(ks + ((kbase_off ^ (16 * kk)) + kb * 32 * D));
-      };
-      uint4 kf[2 * NKK];
-#pragma unroll
-      for (int i = 0; i < kRA; ++i) kf[i] = kread(i);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < 2 * NKK; ++i) {
-        const int kb = i & 1, kk = i >> 1;
-        if (i + kRA < 2 * NKK) kf[i + kRA] = kread(i + kRA);
-        s[kb] = mfma_bf16(kf[i], qreg[kk], kk == 0 ? (f32x16){} : s[kb]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+  // MFMA cluster: O = alpha O + V(u)^T P~(u)^T (four independent
+  // accumulators in turn) and S(u+1) = K(u+1) Q^T (kb chains interleaved).
+  // With 128-key tiles P.V runs first, so that P~(u) dies before S(u+1) is
+  // born (the registers of both would not fit); with 64-key tiles Q.K^T
+  // first measured 1% faster.
+  auto pv_part = [&](int u) __attribute__((always_inline)) {
     if (u >= jt0 && active(u)) {
       if (__ballot(alpha != 1.f)) {  // rarely taken once the row maxima settle
         float a_r = alpha;
@@ -662,7 +647,7 @@ __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, 
         const uint2 hi = lds_read_tr16(vs + ((vt_off1 ^ (32 * db)) + cc * 16 * D));
         return (uint4){lo.x, lo.y, hi.x, hi.y};
       };
-      constexpr int NPV = 4 * NDB;
+      constexpr int NPV = NKS * NDB;
       uint4 vf[NPV];
 #pragma unroll
       for (int i = 0; i < kRA; ++i) vf[i] = vread(i);
@@ -674,6 +659,38 @@ __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, 
         acc[db] = mfma_bf16(vf[i], pb[cc], acc[db]);
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
+  };
+  auto qk_part = [&](int u) __attribute__((always_inline)) {
+    if (u + 1 < jt1 && active(u + 1)) {
+      const uint16_t *ks = smem + kslot(u + 1);
+      auto kread = [&](int i) __attribute__((always_inline)) {
+        const int kb = i % NKB, kk = i / NKB;
+        return *(const uint4 *)(ks + ((kbase_off ^ (16 * kk)) + kb * 32 * D));
+      };
+      uint4 kf[NKB * NKK];
+#pragma unroll
+      for (int i = 0; i < kRA; ++i) kf[i] = kread(i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NKB * NKK; ++i) {
+        const int kb = i % NKB, kk = i / NKB;
+        if (i + kRA < NKB * NKK) kf[i + kRA] = kread(i + kRA);
+        s[kb] = mfma_bf16(kf[i], qreg[kk], kk == 0 ? (f32x16){} : s[kb]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  auto m_cluster = [&](int u) __attribute__((always_inline)) {
+    // the MFMA wave issues ahead of its softmax partner on the SIMD (the
+    // arbiter otherwise favours the older wave, i.e. always group 0)
+    __builtin_amdgcn_s_setprio(3);
+    if constexpr (BC == 128) {
+      pv_part(u);
+      qk_part(u);
+    } else {
+      qk_part(u);
+      pv_part(u);
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -688,13 +705,13 @@ __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, 
       const VisRange vr = vis_range(window > 0 ? (int64_t)my_p - window + 1 : 0, causal ? min(nk - 1, my_p) : nk - 1);
       const uint32_t vo = vis_offset(vr, k0 + 4 * hf);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
           if (!vis(vo, vr, kb * 32 + 8 * (e >> 2) + (e & 3))) s[kb][e] = -INFINITY;
     } else if constexpr (MASK) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
@@ -702,17 +719,14 @@ __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, 
           if (!ok) s[kb][e] = -INFINITY;
         }
     }
-    // row max over the lane's 32 scores: four chains of v_max3 (16 in all)
+    // row max over the lane's 16 NKB scores: four chains of v_max3
+    constexpr int NV = 16 * NKB;
     auto sv = [&](int i) __attribute__((always_inline)) { return s[i >> 4][i & 15]; };
     float mp[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) mp[j] = max3f(sv(3 * j), sv(3 * j + 1), sv(3 * j + 2));
 #pragma unroll
-    for (int i = 12; i < 28; i += 8)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) mp[j] = max3f(mp[j], sv(i + 2 * j), sv(i + 2 * j + 1));
-    mp[0] = max3f(mp[0], sv(28), sv(29));
-    mp[1] = max3f(mp[1], sv(30), sv(31));
+    for (int i = 12; i < NV; i += 2) mp[(i / 2) & 3] = max3f(mp[(i / 2) & 3], sv(i), sv(i + 1));
     float mx = max3f(max3f(mp[0], mp[1], mp[2]), mp[3], mp[3]);
     {  // with lane l ^ 32, which holds the rest of the row
       const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
@@ -723,7 +737,7 @@ __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, 
     m = up ? mx : m;
     float rp[4];  // four partial row sums, each started from its first term
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float p = fast_exp2(__builtin_fmaf(s[kb][e], c, -m));
@@ -733,7 +747,7 @@ __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, 
       }
     l = l * alpha + ((rp[0] + rp[1]) + (rp[2] + rp[3]));
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
+    for (int cc = 0; cc < NKS; ++cc) {
       const int kb = cc >> 1, r0 = (cc & 1) * 8;
       pb[cc].x = pack_bf16x2(s[kb][r0 + 0], s[kb][r0 + 1]);
       pb[cc].y = pack_bf16x2(s[kb][r0 + 2], s[kb][r0 + 3]);
@@ -834,16 +848,20 @@ __device__ __forceinline__ void pp_varlen_persistent(const FwdArgs &a, uint16_t 
     const int st = packed_schedule_item(ps, i, a.causal, sq, h, qt);
     if (st < 0) break;
     if (st == 0) continue;
-    pp_item<D, true>(a, sq, h, qt, smem);
+    pp_item<D, true, 64>(a, sq, h, qt, smem);
     lds_barrier();  // the next item's DMA reuses the LDS that the epilogue read
   }
 }
 
-template <int D>
+// BC keys per tile: 128 for dense calls without a window (twice the work per
+// step over the same fixed costs of each cluster: barrier, first-operand
+// latency, DMA issue), 64 for packed and windowed calls, whose edge tiles a
+// wider tile would make costlier.
+template <int D, int BC>
 __global__ __launch_bounds__(512, 2) void fwd_bf16_pp_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[kPPLds<D>];  // K ring, V ring / staged O
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[kPPLds<D, BC>];  // K ring, V ring / staged O
   if (a.persist == 2) {
-    pp_varlen_persistent<D>(a, smem);
+    if constexpr (BC == 64) pp_varlen_persistent<D>(a, smem);
     return;
   }
   const UnitRange r = launch_units(a.persist, a.batch, a.heads, a.nqt, a.causal);
@@ -853,7 +871,7 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_pp_kernel(FwdArgs a) {
       if (!launch_tile(a.persist, r, u, j, a.batch, a.heads, a.nqt, a.cu_seqlens != nullptr, a.causal, false, b, h,
                        qt))
         break;
-      pp_item<D, false>(a, b, h, qt, smem);
+      pp_item<D, false, BC>(a, b, h, qt, smem);
       lds_barrier();  // the next item's DMA reuses the LDS that the epilogue read
     }
 }
@@ -1016,8 +1034,14 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, int head_dim, hipStream_t s) {
       p.persist = 2;
       g = dim3((unsigned)cus);
     }
-    if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_pp_kernel<128>), g, dim3(512), 0, s, p);
-    else hipLaunchKernelGGL((fwd_bf16_pp_kernel<64>), g, dim3(512), 0, s, p);
+    const bool wide = !a.cu_seqlens && a.window <= 0;
+    if (head_dim == 128) {
+      if (wide) hipLaunchKernelGGL((fwd_bf16_pp_kernel<128, 128>), g, dim3(512), 0, s, p);
+      else hipLaunchKernelGGL((fwd_bf16_pp_kernel<128, 64>), g, dim3(512), 0, s, p);
+    } else {
+      if (wide) hipLaunchKernelGGL((fwd_bf16_pp_kernel<64, 128>), g, dim3(512), 0, s, p);
+      else hipLaunchKernelGGL((fwd_bf16_pp_kernel<64, 64>), g, dim3(512), 0, s, p);
+    }
   }
   return hipGetLastError();
 }

@@ -240,7 +240,7 @@ fa_status fa_check_fwd(const fa_fwd_params *p) {
   if ((st = check_tensor("k", p->k, p->k_stride, 3, eb, k_empty, p->seqlen_k, hd)) != FA_OK) return st;
   if ((st = check_tensor("v", p->v, p->v_stride, 3, eb, k_empty, p->seqlen_k, hd)) != FA_OK) return st;
   if ((st = check_tensor("o", p->o, p->o_stride, 3, ob, q_empty, p->seqlen_q, hd)) != FA_OK) return st;
-  const int64_t items = ceil_div(p->seqlen_q, fa::kFwdMinBlockRows) * (int64_t)p->heads * p->batch;
+  const int64_t items = ceil_div(p->seqlen_q, fa::fwd_min_block_rows(p->qkv_dtype)) * (int64_t)p->heads * p->batch;
   if (items > INT32_MAX) return fail(FA_ERR_INVALID_ARGUMENT, "problem too large for one launch");
   return ok();
 }
@@ -265,7 +265,8 @@ fa_status fa_check_varlen_fwd(const fa_varlen_fwd_params *p) {
   if ((st = check_tensor("k", p->k, p->k_stride, 2, eb, empty, tt, hd)) != FA_OK) return st;
   if ((st = check_tensor("v", p->v, p->v_stride, 2, eb, empty, tt, hd)) != FA_OK) return st;
   if ((st = check_tensor("o", p->o, p->o_stride, 2, ob, empty, tt, hd)) != FA_OK) return st;
-  const int64_t items = ceil_div(p->max_seqlen, fa::kFwdMinBlockRows) * (int64_t)p->heads * p->num_seqs;
+  const int64_t items =
+      ceil_div(p->max_seqlen, fa::fwd_min_block_rows(p->qkv_dtype)) * (int64_t)p->heads * p->num_seqs;
   if (items > INT32_MAX) return fail(FA_ERR_INVALID_ARGUMENT, "problem too large for one launch");
   return ok();
 }

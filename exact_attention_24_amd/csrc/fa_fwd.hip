@@ -876,18 +876,34 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_pp_kernel(FwdArgs a) {
     }
 }
 
-// fp32 forward (small workloads): 4 waves x 16 query rows; a query's dot
+// fp32 forward (small workloads): 16 query rows per work-group, and its 4
+// waves split the keys: wave w takes key tiles w, w + 4, ..., each with its
+// own online softmax state (m, l, O rows), staged through its own LDS slice
+// with no work-group barrier, and the four states are merged at the end the
+// way partial results over disjoint key sets combine (the merge recurrence of
+// "FlashAttention优化Transformer显存与计算效率" section 2.2.2).  A query's dot
 // product is split over 4 lanes (one quarter of the head dim each) and
-// combined with two lane exchanges.  Key tiles of 32 in LDS, the same online
-// softmax as the bf16 kernel, all arithmetic in fp32 FMA.
+// combined with two lane exchanges.  Key tiles of 32, all arithmetic in fp32
+// FMA.  Splitting the keys cuts the serial chain of tiles each wave walks
+// (latency-bound at these sizes) by 4.
+// x summed over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four quarters of a
+// query's dot product) by two lane-half swaps on the VALU; each pair sum is
+// formed in the same order on both lanes of the pair.
+__device__ __forceinline__ float quarter_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
 template <int D>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
-  constexpr int BC = 32, BR = 64, DQ = D / 4, KP = D + 4;
-  __shared__ float ks[BC * KP];
-  __shared__ float vs[BC * KP];
+  constexpr int BC = 32, BR = 16, DQ = D / 4, KP = D + 4, NWV = 4;
+  __shared__ __attribute__((aligned(16))) float tiles[NWV][2][BC * KP];  // per wave: K, V tile
+  __shared__ float s_m[NWV][BR], s_l[NWV][BR];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int qr = lane & 15, quarter = lane >> 4;
+  float *ks = tiles[wave][0], *vs = tiles[wave][1];
 
   int b, h, qt;
   decode_item(a, b, h, qt);
@@ -897,7 +913,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
     nq = nk = a.cu_seqlens[b + 1] - seq0;
   }
   const int q0 = qt * BR;
-  if (q0 >= nq) return;
+  if (q0 >= nq) return;  // uniform for the whole work-group
   const int off = nk - nq;
   const int causal = a.causal, window = a.window;
   const float *qbase = (const float *)a.q + b * a.q_sb + (int64_t)seq0 * a.q_st + h * a.q_sh;
@@ -909,7 +925,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
   if (causal) kv_hi = min(nk, p_hi + 1);
   if (window > 0) kv_lo = max(0, p_lo - window + 1);
 
-  const int my_q = q0 + wave * 16 + qr;
+  const int my_q = q0 + qr;
   const int my_p = my_q + off;
   float qv[DQ], acc[DQ];
 #pragma unroll
@@ -920,27 +936,29 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
   float m = -INFINITY, l = 0.f;
   const float c = a.scale_log2;
 
-  for (int k0 = (kv_lo / BC) * BC; k0 < kv_hi; k0 += BC) {
-    __syncthreads();
-    for (int i = tid; i < BC * D; i += 256) {
-      const int row = i / D, col = i % D, key = k0 + row;
-      ks[row * KP + col] = key < nk ? kbase[(int64_t)key * a.k_st + col] : 0.f;
-      vs[row * KP + col] = key < nk ? vbase[(int64_t)key * a.v_st + col] : 0.f;
+  for (int k0 = (kv_lo / BC + wave) * BC; k0 < kv_hi; k0 += NWV * BC) {
+    // this wave's tile: the wave's LDS operations run in order, so its reads
+    // of the previous tile come before these stores
+    for (int i = lane; i < BC * D / 4; i += 64) {
+      const int row = i / (D / 4), col = 4 * (i % (D / 4)), key = k0 + row;
+      const float4 z = {0.f, 0.f, 0.f, 0.f};
+      *(float4 *)(ks + row * KP + col) = key < nk ? *(const float4 *)(kbase + (int64_t)key * a.k_st + col) : z;
+      *(float4 *)(vs + row * KP + col) = key < nk ? *(const float4 *)(vbase + (int64_t)key * a.v_st + col) : z;
     }
-    __syncthreads();
-    float s[BC];
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the stores are done before the reads below
+    __builtin_amdgcn_wave_barrier();
+    float sc[BC];
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < BC; ++j) {
       float part = 0.f;
 #pragma unroll
       for (int e = 0; e < DQ; ++e) part = __builtin_fmaf(qv[e], ks[j * KP + quarter * DQ + e], part);
-      part += __shfl_xor(part, 16);
-      part += __shfl_xor(part, 32);
+      part = quarter_sum(part);
       const int key = k0 + j;
       const bool ok = key < nk && (!causal || key <= my_p) && (window <= 0 || key > my_p - window);
-      s[j] = ok ? part : -INFINITY;
-      mx = fmaxf(mx, s[j]);
+      sc[j] = ok ? part : -INFINITY;
+      mx = fmaxf(mx, sc[j]);
     }
     const float m_new = fmaxf(m, mx * c);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
@@ -949,25 +967,56 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
     float rs = 0.f;
 #pragma unroll
     for (int j = 0; j < BC; ++j) {
-      s[j] = exp2f(__builtin_fmaf(s[j], c, -m_use));
-      rs += s[j];
+      sc[j] = exp2f(__builtin_fmaf(sc[j], c, -m_use));
+      rs += sc[j];
     }
     l = l * alpha + rs;
 #pragma unroll
     for (int e = 0; e < DQ; ++e) {
       float t = acc[e] * alpha;
 #pragma unroll
-      for (int j = 0; j < BC; ++j) t = __builtin_fmaf(s[j], vs[j * KP + quarter * DQ + e], t);
+      for (int j = 0; j < BC; ++j) t = __builtin_fmaf(sc[j], vs[j * KP + quarter * DQ + e], t);
       acc[e] = t;
     }
+    __builtin_amdgcn_wave_barrier();
   }
-  if (my_q < nq) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    float *orow = (float *)a.o + b * a.o_sb + (int64_t)(seq0 + my_q) * a.o_st + h * a.o_sh;
+
+  // merge the waves' states: M = max m_w, L = sum l_w 2^(m_w - M),
+  // O = sum O_w 2^(m_w - M) / L (m in log2 units)
+  __syncthreads();  // every wave is done with its tile slice
+  float *ost = &tiles[0][0][0];  // [wave][row][D] partial O rows
 #pragma unroll
-    for (int e = 0; e < DQ; ++e) orow[quarter * DQ + e] = acc[e] * inv;
-    if (quarter == 0 && a.lse)
-      a.lse[b * a.lse_sb + h * a.lse_sh + seq0 + my_q] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+  for (int e = 0; e < DQ; ++e) ost[(wave * BR + qr) * D + quarter * DQ + e] = acc[e];
+  if (quarter == 0) {
+    s_m[wave][qr] = m;
+    s_l[wave][qr] = l;
+  }
+  __syncthreads();
+  // thread t: row t / 16, head dims (t % 16) * D / 16 ...
+  constexpr int DT = D / 16;
+  const int row = tid / 16, d0 = (tid % 16) * DT;
+  const int q = q0 + row;
+  if (q < nq) {
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) mm = fmaxf(mm, s_m[w][row]);
+    float wgt[NWV], lt = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      wgt[w] = s_m[w][row] == -INFINITY ? 0.f : exp2f(s_m[w][row] - mm);
+      lt += s_l[w][row] * wgt[w];
+    }
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    float *orow = (float *)a.o + b * a.o_sb + (int64_t)(seq0 + q) * a.o_st + h * a.o_sh;
+#pragma unroll
+    for (int e = 0; e < DT; ++e) {
+      float o = 0.f;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) o = __builtin_fmaf(wgt[w], ost[(w * BR + row) * D + d0 + e], o);
+      orow[d0 + e] = o * inv;
+    }
+    if (tid % 16 == 0 && a.lse)
+      a.lse[b * a.lse_sb + h * a.lse_sh + seq0 + q] = lt > 0.f ? (mm + log2f(lt)) * kLn2 : -INFINITY;
   }
 }
 
@@ -991,7 +1040,7 @@ int persistent_groups() {
 int fwd_block_rows(int qkv_dtype, int head_dim, int64_t batch_heads, int64_t nq, bool causal, bool varlen,
                    int cus) {
   (void)head_dim;
-  if (qkv_dtype == 0) return 64;  // fp32 kernel: 4 waves x 16 rows
+  if (qkv_dtype == 0) return 16;  // fp32 kernel: 16 rows, the keys split over 4 waves
   if (qkv_dtype != 1) return 256;  // fp8 kernel
   const int64_t want = cus > 0 ? cus : 256;
   // 256 rows where that launch runs persistently (dense causal calls pair

@@ -117,10 +117,13 @@ int persistent_groups();
 // else 128 rows (4 waves) if that gives one work-group per CU, else 64 (2
 // waves), so that short sequences still spread over the chip; packed calls
 // count sequences x heads tiles of max_seqlen rows.  fp8 takes 256, fp32
-// 64.  `cus` is the device's CU count (0: unknown).
+// 16.  `cus` is the device's CU count (0: unknown).
 int fwd_block_rows(int qkv_dtype, int head_dim, int64_t batch_heads, int64_t nq, bool causal, bool varlen,
                    int cus);
-// Smallest tile any call may take (bounds of the host checks).
+// Smallest tile a call may take (bounds of the host checks): 64 rows for
+// bf16 and fp8 inputs, 16 for the fp32 kernel.
 constexpr int kFwdMinBlockRows = 64;
+constexpr int kFwdF32BlockRows = 16;
+inline int fwd_min_block_rows(int qkv_dtype) { return qkv_dtype == 0 ? kFwdF32BlockRows : kFwdMinBlockRows; }
 
 }  // namespace fa

@@ -61,6 +61,19 @@ def test_f32_small_elementwise(d):
     assert_lse_close(f64(lse), rl, tol=1e-5)
 
 
+@pytest.mark.parametrize("b,nq,nk,h,d,causal,window", SMALL)
+def test_f32_shapes_elementwise(b, nq, nk, h, d, causal, window):
+    """The fp32 kernel splits each tile's keys over its 4 waves and merges the
+    waves' states: windows, tails, Nq != Nk and rows that see no key."""
+    print(f"[fwd f32] b={b} nq={nq} nk={nk} h={h} d={d} causal={causal} window={window}", flush=True)
+    q, _, _ = dense_inputs(b, nq, h, d, "f32", seed=nq * 17 + nk)
+    _, k, v = dense_inputs(b, nk, h, d, "f32", seed=nq * 17 + nk + 1)
+    o, lse = _run(q, k, v, causal, window)
+    ro, rl = _oracle(q, k, v, 1 / np.sqrt(d), causal, window)
+    assert_close(f64(o), ro, max_abs=1e-5, mean_abs=1e-6)
+    assert_lse_close(f64(lse), rl, tol=1e-5)
+
+
 def test_tiny_fp32_workload():
     """B1 H1 N256 d64 fp32, non-causal, scale 1/8: the whole output."""
     w = WORKLOADS["tiny_fp32"]

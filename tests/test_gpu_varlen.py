@@ -27,6 +27,7 @@ def _run(q, k, v, cu, causal, window, dtype_out=None):
     ([200, 201, 1], 3, 128, False, 0, "bf16"),
     ([129, 40], 2, 128, False, 33, "bf16"),
     ([70, 3, 150], 2, 64, True, 0, "f32"),
+    ([90, 0, 161, 33], 2, 128, True, 40, "f32"),
 ])
 def test_varlen_small_elementwise(lengths, h, d, causal, window, dt):
     print(f"[varlen] lengths={lengths} h={h} d={d} causal={causal} window={window} {dt}", flush=True)

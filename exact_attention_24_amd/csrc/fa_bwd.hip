@@ -84,6 +84,7 @@ __device__ __forceinline__ void store_grad4(void *base, int64_t elem_off, bool f
 // Rows of a causal sequence that see fewer than this many keys (its first
 // kStartRows positions) are computed by bwd_start_kernel in fp32.
 constexpr int kStartRows = 64;
+constexpr int kDsumRows = 4;  // rows per lane group of the D = rowsum(dO * O) kernel
 
 __device__ __forceinline__ float load_grad(const void *base, int64_t off, bool f32) {
   return f32 ? ((const float *)base)[off] : bf16_to_f32(((const uint16_t *)base)[off]);
@@ -99,48 +100,61 @@ __device__ __forceinline__ float load_grad(const void *base, int64_t off, bool f
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dsum_kernel(BwdArgs a, int64_t total) {
-  constexpr int LPR = D / 8;       // lanes per row, 8 bf16 each
-  constexpr int RPB = 256 / LPR;   // rows per block
+  constexpr int LPR = D / 8;      // lanes per row, 8 bf16 each
+  constexpr int GPB = 256 / LPR;  // lane groups per block
+  // rows per lane group: their O and dO loads are all in flight at once
+  // (one row per group left the kernel at 3.4-4.1 TB/s)
+  constexpr int R = kDsumRows;
   const int tid = threadIdx.x, sub = tid % LPR;
-  const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;  // (b, h, q) or (h, token) order
-  float acc = 0.f;
-  bool start_row = false;
-  if (row < total) {
-    int b = 0, h, q, pos, off;  // q: token row of the tensors; pos: position in its sequence
-    if (a.cu_seqlens) {
-      const int ntok = (int)a.lse_sh;
-      h = (int)(row / ntok);
-      q = (int)(row % ntok);
-      int lo = 0, hi = a.batch;  // the sequence s with cu[s] <= q < cu[s + 1]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (a.cu_seqlens[mid] <= q) lo = mid;
-        else hi = mid;
-      }
-      pos = q - a.cu_seqlens[lo];
-      off = 0;
-    } else {
-      q = (int)(row % a.nq);
-      const int64_t bh = row / a.nq;
-      h = (int)(bh % a.heads);
-      b = (int)(bh / a.heads);
-      pos = q;
-      off = a.nk - a.nq;
-    }
-    start_row = a.causal && pos + off >= 0 && pos + off < kStartRows;
-    const uint4 ov = *(const uint4 *)((const uint16_t *)a.o + b * a.o_sb + (int64_t)q * a.o_st +
-                                      h * a.o_sh + sub * 8);
-    const uint4 dv = *(const uint4 *)((const uint16_t *)a.dout + b * a.do_sb + (int64_t)q * a.do_st +
-                                      h * a.do_sh + sub * 8);
+  const int64_t row0 = ((int64_t)blockIdx.x * GPB + tid / LPR) * R;  // (b, h, q) or (h, token) order
+  uint4 ov[R], dv[R];
+  bool start_row[R];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(bf16_to_f32(u16_at(ov, e)), bf16_to_f32(u16_at(dv, e)), acc);
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = row0 + r;
+    ov[r] = dv[r] = uint4{0u, 0u, 0u, 0u};
+    start_row[r] = false;
+    if (row < total) {
+      int b = 0, h, q, pos, off;  // q: token row of the tensors; pos: position in its sequence
+      if (a.cu_seqlens) {
+        const int ntok = (int)a.lse_sh;
+        h = (int)(row / ntok);
+        q = (int)(row % ntok);
+        int lo = 0, hi = a.batch;  // the sequence s with cu[s] <= q < cu[s + 1]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (a.cu_seqlens[mid] <= q) lo = mid;
+          else hi = mid;
+        }
+        pos = q - a.cu_seqlens[lo];
+        off = 0;
+      } else {
+        q = (int)(row % a.nq);
+        const int64_t bh = row / a.nq;
+        h = (int)(bh % a.heads);
+        b = (int)(bh / a.heads);
+        pos = q;
+        off = a.nk - a.nq;
+      }
+      start_row[r] = a.causal && pos + off >= 0 && pos + off < kStartRows;
+      ov[r] = *(const uint4 *)((const uint16_t *)a.o + b * a.o_sb + (int64_t)q * a.o_st + h * a.o_sh + sub * 8);
+      dv[r] = *(const uint4 *)((const uint16_t *)a.dout + b * a.do_sb + (int64_t)q * a.do_st + h * a.do_sh + sub * 8);
+    }
   }
 #pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  if (row < total && sub == 0) {
-    a.dpsum[row] = acc;
-    const float x = a.lse[row];
-    a.lse2[row] = (x == -INFINITY || start_row) ? INFINITY : x * kLog2e;
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = row0 + r;
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      acc = __builtin_fmaf(bf16_to_f32(u16_at(ov[r], e)), bf16_to_f32(u16_at(dv[r], e)), acc);
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+    if (row < total && sub == 0) {
+      a.dpsum[row] = acc;
+      const float x = a.lse[row];
+      a.lse2[row] = (x == -INFINITY || start_row[r]) ? INFINITY : x * kLog2e;
+    }
   }
 }
 
@@ -1431,7 +1445,7 @@ hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t s) {
   // rows for a packed call (its lse layout)
   const int64_t rows = a.cu_seqlens ? (int64_t)a.heads * a.lse_sh : (int64_t)a.batch * a.heads * a.nq;
   if (rows > 0) {
-    constexpr int RPB = 256 / (D / 8);
+    constexpr int RPB = 256 / (D / 8) * kDsumRows;
     hipLaunchKernelGGL((bwd_dsum_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, a, rows);
   }
   const int cus = persistent_groups();

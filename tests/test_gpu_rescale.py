@@ -19,7 +19,7 @@ import torch
 
 import oracle
 from exact_attention_24_amd import fa_fwd, fa_fwd_kvcache, fa_merge, fa_varlen_fwd
-from exact_attention_24_amd.inputs import (cu_seqlens_of, dense_inputs, kvcache_inputs, quantize_e4m3, spike_keys,
+from exact_attention_24_amd.inputs import (dense_inputs, kvcache_inputs, quantize_e4m3, spike_keys,
                                            varlen_inputs)
 from tests.parity import FP8_MAX_ABS, assert_close, assert_lse_close, f64, sample_rows
 

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from exact_attention_24_amd import fa_fwd, fa_varlen_fwd
-from exact_attention_24_amd.inputs import WORKLOADS, cu_seqlens_of, varlen_inputs, workload_inputs
+from exact_attention_24_amd.inputs import WORKLOADS, varlen_inputs, workload_inputs
 from tests.parity import assert_close, assert_lse_close, f64
 
 pytestmark = pytest.mark.gpu

@@ -260,11 +260,13 @@ fa_status fa_check_varlen_fwd(const fa_varlen_fwd_params *p) {
   const bool empty = (int64_t)p->total_tokens * p->heads == 0 || p->num_seqs == 0;
   if (!empty && !p->cu_seqlens) return fail(FA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
   const int eb = dtype_bytes(p->qkv_dtype), ob = dtype_bytes(p->o_dtype);
-  const int hd = p->head_dim, tt = p->total_tokens;
-  if ((st = check_tensor("q", p->q, p->q_stride, 2, eb, empty, tt, hd)) != FA_OK) return st;
-  if ((st = check_tensor("k", p->k, p->k_stride, 2, eb, empty, tt, hd)) != FA_OK) return st;
-  if ((st = check_tensor("v", p->v, p->v_stride, 2, eb, empty, tt, hd)) != FA_OK) return st;
-  if ((st = check_tensor("o", p->o, p->o_stride, 2, ob, empty, tt, hd)) != FA_OK) return st;
+  // the kernels address each sequence's rows from its own start (64-bit
+  // pointer arithmetic), so the 32-bit offset bound applies per sequence
+  const int hd = p->head_dim, ms = p->max_seqlen;
+  if ((st = check_tensor("q", p->q, p->q_stride, 2, eb, empty, ms, hd)) != FA_OK) return st;
+  if ((st = check_tensor("k", p->k, p->k_stride, 2, eb, empty, ms, hd)) != FA_OK) return st;
+  if ((st = check_tensor("v", p->v, p->v_stride, 2, eb, empty, ms, hd)) != FA_OK) return st;
+  if ((st = check_tensor("o", p->o, p->o_stride, 2, ob, empty, ms, hd)) != FA_OK) return st;
   const int64_t items =
       ceil_div(p->max_seqlen, fa::fwd_min_block_rows(p->qkv_dtype)) * (int64_t)p->heads * p->num_seqs;
   if (items > INT32_MAX) return fail(FA_ERR_INVALID_ARGUMENT, "problem too large for one launch");
@@ -316,15 +318,16 @@ fa_status fa_check_varlen_bwd(const fa_varlen_bwd_params *p) {
   const bool empty = (int64_t)p->total_tokens * p->heads == 0 || p->num_seqs == 0;
   if (!empty && !p->cu_seqlens) return fail(FA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
   const int gb = dtype_bytes(p->grad_dtype);
-  const int hd = p->head_dim, tt = p->total_tokens;
-  if ((st = check_tensor("q", p->q, p->q_stride, 2, 2, empty, tt, hd)) != FA_OK) return st;
-  if ((st = check_tensor("k", p->k, p->k_stride, 2, 2, empty, tt, hd)) != FA_OK) return st;
-  if ((st = check_tensor("v", p->v, p->v_stride, 2, 2, empty, tt, hd)) != FA_OK) return st;
-  if ((st = check_tensor("o", p->o, p->o_stride, 2, 2, empty, tt, hd)) != FA_OK) return st;
-  if ((st = check_tensor("dout", p->dout, p->do_stride, 2, 2, empty, tt, hd)) != FA_OK) return st;
-  if ((st = check_tensor("dq", p->dq, p->dq_stride, 2, gb, empty, tt, hd)) != FA_OK) return st;
-  if ((st = check_tensor("dk", p->dk, p->dk_stride, 2, gb, empty, tt, hd)) != FA_OK) return st;
-  if ((st = check_tensor("dv", p->dv, p->dv_stride, 2, gb, empty, tt, hd)) != FA_OK) return st;
+  // per-sequence 32-bit offsets, as in the packed forward
+  const int hd = p->head_dim, ms = p->max_seqlen;
+  if ((st = check_tensor("q", p->q, p->q_stride, 2, 2, empty, ms, hd)) != FA_OK) return st;
+  if ((st = check_tensor("k", p->k, p->k_stride, 2, 2, empty, ms, hd)) != FA_OK) return st;
+  if ((st = check_tensor("v", p->v, p->v_stride, 2, 2, empty, ms, hd)) != FA_OK) return st;
+  if ((st = check_tensor("o", p->o, p->o_stride, 2, 2, empty, ms, hd)) != FA_OK) return st;
+  if ((st = check_tensor("dout", p->dout, p->do_stride, 2, 2, empty, ms, hd)) != FA_OK) return st;
+  if ((st = check_tensor("dq", p->dq, p->dq_stride, 2, gb, empty, ms, hd)) != FA_OK) return st;
+  if ((st = check_tensor("dk", p->dk, p->dk_stride, 2, gb, empty, ms, hd)) != FA_OK) return st;
+  if ((st = check_tensor("dv", p->dv, p->dv_stride, 2, gb, empty, ms, hd)) != FA_OK) return st;
   if (!empty && !p->lse) return fail(FA_ERR_INVALID_ARGUMENT, "lse is NULL");
   if (ceil_div(p->max_seqlen, 128) * (int64_t)p->heads * p->num_seqs > INT32_MAX ||
       (fa::bwd_band(p->causal, p->window) &&

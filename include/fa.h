@@ -100,7 +100,10 @@ typedef enum {
  *   (FP8_E4M3, BF16).  For fp8 the values are code * descale (per tensor);
  *   for the other dtypes the descales must be 1.
  *   Packed QKV (batch, seqlen, 3, heads, head_dim) is expressed by pointing
- *   q, k, v at slices 0, 1, 2 of one buffer with token stride 3*heads*head_dim. */
+ *   q, k, v at slices 0, 1, 2 of one buffer with token stride 3*heads*head_dim.
+ *   The kernels read rows with 32-bit byte offsets from the start of each
+ *   (batch, head) slice: (seqlen + 256) * token stride * element size must
+ *   be below 2^31 for every tensor, else FA_ERR_INVALID_ARGUMENT. */
 typedef struct {
   const void *q, *k, *v;
   void *o;
@@ -124,7 +127,9 @@ typedef struct {
  *   cu_seqlens: DEVICE int32 [num_seqs + 1], cu_seqlens[0] = 0,
  *   non-decreasing, cu_seqlens[num_seqs] = total_tokens.  Every length must be
  *   <= max_seqlen, which sizes the launch grid.  These device-side contracts
- *   are not checked: violating them reads or writes out of bounds.
+ *   are not checked: violating them reads or writes out of bounds.  Rows are
+ *   addressed from each sequence's own start, so the 2^31-byte bound of
+ *   fa_fwd applies with max_seqlen in place of seqlen, whatever total_tokens.
  *   lse [heads, total_tokens] fp32 contiguous, or NULL. */
 typedef struct {
   const void *q, *k, *v;

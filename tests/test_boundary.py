@@ -154,6 +154,25 @@ def test_varlen_checks(lib):
     assert lib.fa_check_varlen_fwd(ctypes.byref(p)) == B.FA_ERR_INVALID_ARGUMENT
 
 
+def test_slice_offset_bound(lib):
+    # 32-bit row offsets: the bound is per (batch, head) slice for dense calls
+    # and per sequence for packed ones (checks only, nothing is launched)
+    q = torch.zeros(1, 8, 32, 128, dtype=torch.bfloat16)
+    p = B.make_fwd_params(q, q, q, q, None)
+    p.seqlen_q = p.seqlen_k = 300_000  # 300K rows x 32 heads x 128 x 2 B > 2 GiB
+    assert lib.fa_check_fwd(ctypes.byref(p)) == B.FA_ERR_INVALID_ARGUMENT
+    assert b"2 GiB" in lib.fa_last_error()
+    qp = torch.zeros(40, 32, 128, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 10, 40], dtype=torch.int32)
+    p = B.make_varlen_params(qp, qp, qp, qp, None, cu, 30)
+    p.total_tokens = 300_000
+    p.max_seqlen = 8192
+    assert lib.fa_check_varlen_fwd(ctypes.byref(p)) == B.FA_OK
+    p.max_seqlen = 300_000
+    assert lib.fa_check_varlen_fwd(ctypes.byref(p)) == B.FA_ERR_INVALID_ARGUMENT
+    assert b"2 GiB" in lib.fa_last_error()
+
+
 def test_bwd_checks(lib):
     q = torch.zeros(1, 16, 2, 128, dtype=torch.bfloat16)
     g = torch.zeros(1, 16, 2, 128, dtype=torch.float32)

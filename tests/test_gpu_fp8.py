@@ -40,7 +40,8 @@ def test_fp8_small_elementwise(b, n, h, d, causal, window):
     ro, rl = oracle.mha_fwd(_deq(q8, sq), _deq(k8, sk), _deq(v8, sv), 1 / np.sqrt(d), causal, window)
     assert_close(o.cpu().double().numpy(), ro, max_abs=FP8_MAX_ABS, mean_abs=None, what="O fp8")
     # LSE uses fp32 probabilities before quantisation: as accurate as bf16
-    assert_lse_close(lse.cpu().double().numpy(), rl, tol=2e-3)
+    mx = assert_lse_close(lse.cpu().double().numpy(), rl)
+    print(f"[fp8 small] LSE max abs error {mx:.2e}", flush=True)
 
 
 @pytest.mark.parametrize("causal", [True, False])
@@ -54,12 +55,15 @@ def test_fp8_n8192_sampled_rows(causal):
     q = _deq(t["q8"], ds[0])
     k = _deq(t["k8"], ds[1])
     v = _deq(t["v8"], ds[2])
-    o64 = o.cpu().double().numpy()
+    o64, lse64 = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    worst = 0.0
     for h in range(0, w.heads, 3):
         rows = sample_rows(w.seqlen, 48, seed=100 + h)
         ro, rl = oracle.attention_fwd(q[0, rows, h], k[0, :, h], v[0, :, h], w.scale, causal, 0,
                                       q_pos=rows, nq=w.seqlen)
         assert_close(o64[0, rows, h], ro, max_abs=FP8_MAX_ABS, mean_abs=None, what=f"O fp8 head {h}")
+        worst = max(worst, assert_lse_close(lse64[0, h, rows], rl))
+    print(f"[fp8 n8192 causal={causal}] LSE max abs error {worst:.2e}", flush=True)
     ro, _ = oracle.attention_fwd(q[0, :, 7], k[0, :, 7], v[0, :, 7], w.scale, causal, 0)
     assert_close(o64[0, :, 7], ro, max_abs=FP8_MAX_ABS, mean_abs=None, what="O fp8 full head 7")
 
@@ -84,7 +88,7 @@ def test_fp8_persistent_schedule_sampled_rows(b, n, h, d, causal, window):
             ro, rl = oracle.attention_fwd(qd[bi, rows, hh], kd[bi, :, hh], vd[bi, :, hh], 1 / np.sqrt(d), causal, window,
                                           q_pos=rows, nq=n)
             assert_close(o64[bi, rows, hh], ro, max_abs=FP8_MAX_ABS, mean_abs=None, what=f"O fp8 batch {bi} head {hh}")
-            assert_lse_close(lse64[bi, hh, rows], rl, tol=2e-3)
+            assert_lse_close(lse64[bi, hh, rows], rl)
 
 
 def test_fp8_causal_row0():

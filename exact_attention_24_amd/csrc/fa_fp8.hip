@@ -43,9 +43,14 @@ __device__ __forceinline__ f32x16 mfma_fp8(const uint4 &a0, const uint4 &a1, con
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// four fp32 values -> four e4m3 codes in one dword (RNE)
-__device__ __forceinline__ uint32_t pack_fp8x4(float x0, float x1, float x2, float x3) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+// four fp32 values -> four e4m3 codes in one dword (RNE).  The first
+// conversion writes the low half and keeps the high half of its `old`
+// operand, which the second one overwrites; `dead` is a dword whose last use
+// has passed (the previous tile's packed P~ word that this one replaces), so
+// the compiler converts in that register instead of first zeroing or copying
+// into one.
+__device__ __forceinline__ uint32_t pack_fp8x4(float x0, float x1, float x2, float x3, uint32_t dead) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, (int)dead, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
   return (uint32_t)w;
 }
@@ -320,14 +325,14 @@ __device__ __forceinline__ void fp8_item(const FwdArgs &a, int b, int h, int qt)
           if (i == 5) l = l * alpha + (rs[0] + rs[1]);
         } else if (i == 6) {
           // B operand bytes b = 0..31 <- (kb, r) = (b / 16, b % 16)
-          pb0.x = pack_fp8x4(s[0][0], s[0][1], s[0][2], s[0][3]);
-          pb0.y = pack_fp8x4(s[0][4], s[0][5], s[0][6], s[0][7]);
-          pb0.z = pack_fp8x4(s[0][8], s[0][9], s[0][10], s[0][11]);
-          pb0.w = pack_fp8x4(s[0][12], s[0][13], s[0][14], s[0][15]);
-          pb1.x = pack_fp8x4(s[1][0], s[1][1], s[1][2], s[1][3]);
-          pb1.y = pack_fp8x4(s[1][4], s[1][5], s[1][6], s[1][7]);
-          pb1.z = pack_fp8x4(s[1][8], s[1][9], s[1][10], s[1][11]);
-          pb1.w = pack_fp8x4(s[1][12], s[1][13], s[1][14], s[1][15]);
+          pb0.x = pack_fp8x4(s[0][0], s[0][1], s[0][2], s[0][3], pb0_prev.x);
+          pb0.y = pack_fp8x4(s[0][4], s[0][5], s[0][6], s[0][7], pb0_prev.y);
+          pb0.z = pack_fp8x4(s[0][8], s[0][9], s[0][10], s[0][11], pb0_prev.z);
+          pb0.w = pack_fp8x4(s[0][12], s[0][13], s[0][14], s[0][15], pb0_prev.w);
+          pb1.x = pack_fp8x4(s[1][0], s[1][1], s[1][2], s[1][3], pb1_prev.x);
+          pb1.y = pack_fp8x4(s[1][4], s[1][5], s[1][6], s[1][7], pb1_prev.y);
+          pb1.z = pack_fp8x4(s[1][8], s[1][9], s[1][10], s[1][11], pb1_prev.z);
+          pb1.w = pack_fp8x4(s[1][12], s[1][13], s[1][14], s[1][15], pb1_prev.w);
         }
       }
       __builtin_amdgcn_sched_barrier(0);

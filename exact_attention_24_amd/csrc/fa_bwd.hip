@@ -752,8 +752,17 @@ __device__ __forceinline__ void dq_item(const BwdArgs &a, int b, int h, int qt) 
       for (int part = 0; part < 4; ++part) pack_ds(part / 2, part % 2);
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) drop_rounds(kk);
+      // S = -inf for a sub-tile these rows do not see.  Written by volatile asm
+      // so that the compiler keeps the 32 moves on this path: as plain
+      // assignments it hoisted them above the branch, onto the visible path.
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[0][e] = s[1][e] = -INFINITY;
+      for (int e = 0; e < 16; ++e) {
+        float x0, x1;
+        asm volatile("v_mov_b32 %0, 0xff800000" : "=v"(x0));
+        asm volatile("v_mov_b32 %0, 0xff800000" : "=v"(x1));
+        s[0][e] = x0;
+        s[1][e] = x1;
+      }
     }
     if (MASK) {
 #pragma unroll

@@ -505,8 +505,14 @@ constexpr int kPPLds = (4 * BC * D > 256 * kOP<D>) ? 4 * BC * D : 256 * kOP<D>;
 // (packed calls, where short sequences make most tiles edge tiles); else
 // against each limit in turn, which holds fewer registers through the loop
 // (measured 1-2% faster on dense calls, whose edge tiles are few).
-template <int D, bool RANGE, int BC>
-__device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, uint16_t *smem) {
+// With CHAIN (dense persistent launches, no window) the item's Q fragments
+// and its first K tile were fetched by the previous item (pre) into qreg and
+// K slot 0, and this item fetches those of the next one (nb, nh, nqt when
+// has_next) right after its loop, so that their latency passes under its own
+// epilogue; the epilogue then stages O in the top of the LDS, clear of K slot 0.
+template <int D, bool RANGE, int BC, bool CHAIN = false>
+__device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, uint16_t *smem, uint4 (&qreg)[D / 16],
+                                        bool pre = false, bool has_next = false, int nb = 0, int nh = 0, int nqt = 0) {
   constexpr int BR = 256;
   constexpr int NKB = BC / 32, NKS = BC / 16;  // 32-key blocks of S, 16-key steps of P.V
   constexpr int TS = BC * D;                  // tile elements
@@ -564,8 +570,7 @@ __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, 
   auto kslot = [&](int jt) __attribute__((always_inline)) { return ((jt - jt0) & 1) * TS; };
   auto vslot = [&](int jt) __attribute__((always_inline)) { return 2 * TS + ((jt - jt0) & 1) * TS; };
 
-  uint4 qreg[NKK];
-  {
+  if (!CHAIN || !pre) {
     const uint32_t qoff = (uint32_t)my_q * (uint32_t)a.q_st * 2 + hf * 16;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) qreg[kk] = bload16(qrs, qoff + kk * 32);
@@ -767,11 +772,13 @@ __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, 
 
   if (jt0 < jt1) {
     // K(jt0) whole (every wave BPW blocks of each group's half)
+    if (!CHAIN || !pre) {
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-      const uint32_t gk = (uint32_t)(jt0 * BC) * kst2;
-      const int q = (wave & 3) * BPW + i + grp * (NBLK / 2);
-      dma16_at(kw, lds0 + (uint32_t)(kslot(jt0) * 2 + q * 1024), gk + kgo[i]);
+      for (int i = 0; i < BPW; ++i) {
+        const uint32_t gk = (uint32_t)(jt0 * BC) * kst2;
+        const int q = (wave & 3) * BPW + i + grp * (NBLK / 2);
+        dma16_at(kw, lds0 + (uint32_t)(kslot(jt0) * 2 + q * 1024), gk + kgo[i]);
+      }
     }
     wait_dma();
     __syncthreads();
@@ -800,6 +807,34 @@ __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, 
     }
   }
 
+  // O staging base: the top of the LDS when the next item's first K tile is
+  // already on its way into K slot 0
+  constexpr int OST = CHAIN ? kPPLds<D, BC> - 256 * kOP<D> : 0;
+  static_assert(!CHAIN || OST >= TS, "staged O must clear K slot 0");
+  if constexpr (CHAIN) {
+    if (has_next) {
+      // the next item's Q fragments and K tile 0 (every K/V slot is free
+      // once the loop's last barrier has passed); dense calls only, so the
+      // next item shares nq, nk and the strides
+      const int q0n = nqt * BR;
+      const uint16_t *qbn = (const uint16_t *)a.q + nb * a.q_sb + nh * a.q_sh;
+      const __amdgpu_buffer_rsrc_t qrsn = slice_rsrc(qbn, slice_bytes(nq, a.q_st, D, 2));
+      const uint32_t qoff = (uint32_t)(q0n + 32 * wave + ql) * (uint32_t)a.q_st * 2 + hf * 16;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) qreg[kk] = bload16(qrsn, qoff + kk * 32);
+      const int kv_hin = causal ? min(nk, min(q0n + BR, nq) - 1 + off + 1) : nk;
+      if (kv_hin > 0) {
+        const uint16_t *kbn = (const uint16_t *)a.k + nb * a.k_sb + nh * a.k_sh;
+        const i32x4 kwn = buffer_words(kbn, slice_bytes(nk, a.k_st, D, 2));
+#pragma unroll
+        for (int i = 0; i < BPW; ++i) {
+          const int q = (wave & 3) * BPW + i + grp * (NBLK / 2);
+          dma16_at(kwn, lds0 + (uint32_t)(q * 1024), kgo[i]);
+        }
+      }
+    }
+  }
+
   // epilogue: O = acc / l (bf16, round to nearest even), LSE = (m + log2 l) ln 2.
   // O goes through LDS (the K/V tiles are free once the loop's last barrier
   // has passed) so that it leaves as whole 16-byte-per-lane rows: scattered
@@ -807,7 +842,7 @@ __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, 
   const float lt = half_swap_sum(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   {
-    uint16_t *ot = smem + (32 * wave + ql) * kOP<D>;
+    uint16_t *ot = smem + OST + (32 * wave + ql) * kOP<D>;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -826,7 +861,7 @@ __device__ __forceinline__ void pp_item(const FwdArgs &a, int b, int h, int qt, 
 #pragma unroll
   for (int i = 0; i < BR * CPR / 512; ++i) {
     const int idx = tid + i * 512, row = idx / CPR, ch = idx % CPR;
-    const uint4 v = *(const uint4 *)(smem + row * kOP<D> + ch * 8);
+    const uint4 v = *(const uint4 *)(smem + OST + row * kOP<D> + ch * 8);
     if (q0 + row < nq) *(uint4 *)(obase + (int64_t)row * a.o_st + ch * 8) = v;
   }
 }
@@ -848,7 +883,8 @@ __device__ __forceinline__ void pp_varlen_persistent(const FwdArgs &a, uint16_t 
     const int st = packed_schedule_item(ps, i, a.causal, sq, h, qt);
     if (st < 0) break;
     if (st == 0) continue;
-    pp_item<D, true, 64>(a, sq, h, qt, smem);
+    uint4 qreg[D / 16];
+    pp_item<D, true, 64>(a, sq, h, qt, smem, qreg);
     lds_barrier();  // the next item's DMA reuses the LDS that the epilogue read
   }
 }
@@ -865,13 +901,36 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_pp_kernel(FwdArgs a) {
     return;
   }
   const UnitRange r = launch_units(a.persist, a.batch, a.heads, a.nqt, a.causal);
+  uint4 qreg[D / 16];
+  if constexpr (BC == 128) {
+    if (a.persist == 1) {
+      // the work-group's items in order, each fetching the next one's Q and
+      // first K tile under its epilogue
+      int u = r.lo, j = 0, b = 0, h = 0, qt = 0;
+      auto next = [&](int &nu, int &nj, int &nb, int &nh, int &nqt) __attribute__((always_inline)) {
+        for (; nu < r.hi; nu += r.step, nj = 0)
+          if (nj < 2 && launch_tile(1, r, nu, nj, a.batch, a.heads, a.nqt, false, a.causal, false, nb, nh, nqt))
+            return true;
+        return false;
+      };
+      bool have = next(u, j, b, h, qt), pre = false;
+      while (have) {
+        int nu = u, nj = j + 1, nb = 0, nh = 0, nqt = 0;
+        const bool more = next(nu, nj, nb, nh, nqt);
+        pp_item<D, false, BC, true>(a, b, h, qt, smem, qreg, pre, more, nb, nh, nqt);
+        lds_barrier();  // the next item's DMA reuses the LDS that the epilogue read
+        u = nu, j = nj, b = nb, h = nh, qt = nqt, have = more, pre = more;
+      }
+      return;
+    }
+  }
   for (int u = r.lo; u < r.hi; u += r.step)
     for (int j = 0; j < 2; ++j) {
       int b, h, qt;
       if (!launch_tile(a.persist, r, u, j, a.batch, a.heads, a.nqt, a.cu_seqlens != nullptr, a.causal, false, b, h,
                        qt))
         break;
-      pp_item<D, false, BC>(a, b, h, qt, smem);
+      pp_item<D, false, BC>(a, b, h, qt, smem, qreg);
       lds_barrier();  // the next item's DMA reuses the LDS that the epilogue read
     }
 }

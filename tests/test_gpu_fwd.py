@@ -126,6 +126,8 @@ PERSISTENT = [
     (1, 1100, 1500, 64, 128, False, 0),   # non-causal, Nq < Nk
     (2, 900, 1400, 64, 64, True, 0),      # bottom-right causal, Nq < Nk
     (1, 1000, 1000, 64, 128, False, 200), # window without causal
+    (2, 1000, 600, 64, 128, True, 0),     # Nq > Nk: whole query tiles see no key (items without key tiles)
+    (2, 1100, 700, 48, 64, True, 0),      # the same at d = 64, 5 query tiles
 ]
 
 

@@ -85,6 +85,7 @@ __device__ __forceinline__ void store_grad4(void *base, int64_t elem_off, bool f
 // kStartRows positions) are computed by bwd_start_kernel in fp32.
 constexpr int kStartRows = 64;
 constexpr int kDsumRows = 4;  // rows per lane group of the D = rowsum(dO * O) kernel
+constexpr int kDsumSeqs = 255;  // packed calls with up to this many sequences look them up in LDS
 
 __device__ __forceinline__ float load_grad(const void *base, int64_t off, bool f32) {
   return f32 ? ((const float *)base)[off] : bf16_to_f32(((const uint16_t *)base)[off]);
@@ -107,39 +108,59 @@ __global__ __launch_bounds__(256) void bwd_dsum_kernel(BwdArgs a, int64_t total)
   constexpr int R = kDsumRows;
   const int tid = threadIdx.x, sub = tid % LPR;
   const int64_t row0 = ((int64_t)blockIdx.x * GPB + tid / LPR) * R;  // (b, h, q) or (h, token) order
+  // packed causal calls: cu_seqlens staged in LDS (read together with the
+  // rows' O and dO), so each row's sequence lookup costs no global round trip
+  __shared__ int cus[kDsumSeqs + 1];
+  const bool cu_lds = a.cu_seqlens && a.causal && a.batch <= kDsumSeqs;
+  const int cu_mine = cu_lds && tid <= a.batch ? a.cu_seqlens[tid] : 0;
   uint4 ov[R], dv[R];
+  int tok[R];  // packed calls: the row's token
   bool start_row[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t row = row0 + r;
     ov[r] = dv[r] = uint4{0u, 0u, 0u, 0u};
     start_row[r] = false;
+    tok[r] = -1;
     if (row < total) {
-      int b = 0, h, q, pos, off;  // q: token row of the tensors; pos: position in its sequence
+      int b = 0, h, q;  // q: token row of the tensors
       if (a.cu_seqlens) {
         const int ntok = (int)a.lse_sh;
         h = (int)(row / ntok);
         q = (int)(row % ntok);
-        int lo = 0, hi = a.batch;  // the sequence s with cu[s] <= q < cu[s + 1]
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (a.cu_seqlens[mid] <= q) lo = mid;
-          else hi = mid;
-        }
-        pos = q - a.cu_seqlens[lo];
-        off = 0;
+        tok[r] = q;
       } else {
         q = (int)(row % a.nq);
         const int64_t bh = row / a.nq;
         h = (int)(bh % a.heads);
         b = (int)(bh / a.heads);
-        pos = q;
-        off = a.nk - a.nq;
+        const int pos = q + a.nk - a.nq;
+        start_row[r] = a.causal && pos >= 0 && pos < kStartRows;
       }
-      start_row[r] = a.causal && pos + off >= 0 && pos + off < kStartRows;
       ov[r] = *(const uint4 *)((const uint16_t *)a.o + b * a.o_sb + (int64_t)q * a.o_st + h * a.o_sh + sub * 8);
       dv[r] = *(const uint4 *)((const uint16_t *)a.dout + b * a.do_sb + (int64_t)q * a.do_st + h * a.do_sh + sub * 8);
     }
+  }
+  // position of token q in its sequence s (cu[s] <= q < cu[s + 1]) below kStartRows
+  auto starts = [&](const int *cu, int q) __attribute__((always_inline)) {
+    int lo = 0, hi = a.batch;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (cu[mid] <= q) lo = mid;
+      else hi = mid;
+    }
+    return q - cu[lo] < kStartRows;
+  };
+  if (cu_lds) {
+    if (tid <= a.batch) cus[tid] = cu_mine;
+    __syncthreads();  // uniform
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (tok[r] >= 0) start_row[r] = starts(cus, tok[r]);
+  } else if (a.cu_seqlens && a.causal) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (tok[r] >= 0) start_row[r] = starts(a.cu_seqlens, tok[r]);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -942,7 +963,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 //    and a D taken from the bf16 O would then cost these rows most of the
 //    accuracy the gradients have elsewhere.
 // ---------------------------------------------------------------------------
-constexpr int kStartSplit = 4;  // work-groups per (sequence, head), each 1/4 of the head dims
+// work-groups per (sequence, head), each 1/4 of the head dims; one work-group
+// per pair (4x the fp32 work each) measured no faster on the 11-sequence
+// packed backward, which launches 308 pairs
+constexpr int kStartSplit = 4;
 
 template <int D>
 __global__ __launch_bounds__(256) void bwd_start_kernel(BwdArgs a) {

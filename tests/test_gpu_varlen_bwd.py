@@ -46,6 +46,24 @@ def test_varlen_bwd_small_elementwise(lengths, h, d, causal, window):
     assert_close(f64(dv), rv, what="dV")
 
 
+@pytest.mark.parametrize("nseq", [64, 300, 600])
+def test_varlen_bwd_many_sequences_elementwise(nseq):
+    """Many short sequences, empty ones included: up to 255 the D kernel looks
+    each row's sequence up in LDS, beyond that in global memory; beyond 512
+    the dQ kernel takes one work-group per tile instead of its schedule."""
+    rng = np.random.default_rng(nseq)
+    lengths = [int(x) for x in rng.integers(0, 300, nseq)]
+    lengths[3] = 0
+    lengths[10] = 128
+    print(f"[varlen bwd many] {nseq} sequences, {sum(lengths)} tokens", flush=True)
+    q, k, v, cu, do = varlen_inputs(lengths, 2, 64, "bf16", seed=nseq + 5, with_dout=True)
+    dq, dk, dv = _fwd_bwd(q, k, v, do, cu, True, 0)
+    rq, rk, rv = oracle.varlen_bwd(f64(q), f64(k), f64(v), f64(do), cu.numpy(), 1 / np.sqrt(64), True, 0)
+    assert_close(f64(dq), rq, what="dQ")
+    assert_close(f64(dk), rk, what="dK")
+    assert_close(f64(dv), rv, what="dV")
+
+
 def test_varlen_bwd_equals_dense_per_sequence_bitwise():
     lengths = [300, 1, 513, 64, 0, 129]
     print(f"[varlen bwd bitwise] lengths={lengths}", flush=True)

@@ -130,3 +130,4 @@ def test_units_of_a_sequence_carry_equal_work(window):
         work = [key_tiles(n, qt, window) for qt in range(f, nt - 1)]
         work += [key_tiles(n, f - 1 - j, window) + key_tiles(n, j, window) for j in range(f // 2)]
         assert max(work) - min(work) <= 5, (window, n, work)
+

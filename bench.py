@@ -232,10 +232,11 @@ def config_rows(torch, fa, steps, headline_cpu):
     w = WORKLOADS["b2_h16_n1024"]
     t = workload_inputs("b2_h16_n1024")
     q, k, v = (t[x].cuda() for x in ("q", "k", "v"))
-    o, _ = fa.fa_fwd(q, k, v, causal=True)
+    o, lse2 = fa.fa_fwd(q, k, v, causal=True)
     (ro, _), secs = _oracle_timed(lambda: oracle.mha_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), w.scale, True, 0))
     F = fwd_flops(2, 16, 1024, 64, True)
-    mfma_row("cfg2_fwd_bf16_b2_h16_n1024_d64_causal", lambda: fa.fa_fwd(q, k, v, causal=True), F,
+    o2 = torch.empty_like(o)  # outputs allocated once, as in the timed headline step
+    mfma_row("cfg2_fwd_bf16_b2_h16_n1024_d64_causal", lambda: fa.fa_fwd(q, k, v, causal=True, out=o2, lse=lse2), F,
              2 * (4 * 2 * 1024 * 16 * 64) + 4 * 2 * 16 * 1024, PEAK_BF16_TFLOPS, _errors(f64(o), ro), secs, F,
              "the whole config")
 
@@ -429,7 +430,8 @@ def kvcache_step(torch, fa, page=0):
     return fn, nbytes
 
 
-WORKLOAD_CHOICES = ("fwd_causal", "fwd_noncausal", "bwd", "varlen", "varlen_bwd", "fp8", "merge", "kvcache")
+WORKLOAD_CHOICES = ("fwd_causal", "fwd_noncausal", "fwd_short", "bwd", "varlen", "varlen_bwd", "fp8", "merge",
+                    "kvcache")
 
 
 def make_step(name, torch, fa):
@@ -446,6 +448,14 @@ def make_step(name, torch, fa):
         desc = f"fwd B1 H32 N8192 d128 bf16 {'causal' if causal else 'non-causal'} (Llama-7B attention shape)"
         return (lambda: fa.fa_fwd(q, k, v, causal=causal, out=o, lse=lse),
                 fwd_flops(1, 32, 8192, 128, causal), desc, "bf16", PEAK_BF16_TFLOPS, "fa_fwd.hip", "TFLOP/s")
+    if name == "fwd_short":
+        t = workload_inputs("b2_h16_n1024")
+        q, k, v = (t[x].cuda() for x in ("q", "k", "v"))
+        o = torch.empty_like(q)
+        lse = torch.empty((2, 16, 1024), dtype=torch.float32, device="cuda")
+        return (lambda: fa.fa_fwd(q, k, v, causal=True, out=o, lse=lse), fwd_flops(2, 16, 1024, 64, True),
+                "fwd B2 H16 N1024 d64 bf16 causal (the MindSpore API example; split-key launch)", "bf16",
+                PEAK_BF16_TFLOPS, "fa_fwd_split.hip", "TFLOP/s")
     if name == "bwd":
         t = {k_: v_.cuda() for k_, v_ in workload_inputs("bwd_n8192").items()}
         o, lse = fa.fa_fwd(t["q"], t["k"], t["v"], causal=True)

@@ -21,6 +21,7 @@
 #include <string>
 
 #include "fa_internal.h"
+#include "fa_split.h"
 
 namespace {
 
@@ -357,6 +358,7 @@ fa_status fa_fwd(const fa_fwd_params *p, void *stream) {
   a.v_descale = p->v_descale;
   a.lazy = lazy_threshold(p->causal, p->window);
   set_dropout(a, p->dropout_p, p->dropout_seed, p->dropout_offset);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // short causal calls (a table choice below 256 rows): the keys of each
   // 32-row block split over the work-group's waves
   if (p->qkv_dtype == FA_BF16 && a.br < 256 &&
@@ -364,8 +366,8 @@ fa_status fa_fwd(const fa_fwd_params *p, void *stream) {
                          fa::persistent_groups())) {
     a.br = fa::kFwdSplitRows;
     a.nqt = (int32_t)ceil_div(p->seqlen_q, a.br);
+    return launched(fa::launch_fwd_bf16_split(a, p->head_dim, s));
   }
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   switch (p->qkv_dtype) {
     case FA_F32: return launched(fa::launch_fwd_f32(a, p->head_dim, s));
     case FA_BF16: return launched(fa::launch_fwd_bf16(a, p->head_dim, s));

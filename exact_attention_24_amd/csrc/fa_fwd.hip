@@ -1118,7 +1118,6 @@ void launch_drop_kernel(const FwdArgs &p, dim3 g, hipStream_t s) {
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, int head_dim, hipStream_t s) {
-  if (a.br == kFwdSplitRows) return launch_fwd_bf16_split(a, head_dim, s);
   FwdArgs p = a;
   dim3 g((unsigned)(a.nqt * a.heads * a.batch));
   const int cus = persistent_groups();

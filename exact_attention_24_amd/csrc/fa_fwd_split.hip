@@ -26,6 +26,7 @@
 
 #include "fa_device.h"
 #include "fa_internal.h"
+#include "fa_split.h"
 
 namespace fa {
 namespace {

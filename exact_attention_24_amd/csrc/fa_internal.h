@@ -91,12 +91,6 @@ struct DecodeArgs {
 // Launchers (defined in the kernel translation units).  Each returns the
 // HIP status of its launch(es).
 hipError_t launch_fwd_bf16(const FwdArgs &a, int head_dim, hipStream_t s);
-// Short causal bf16 calls without a window or dropout: 32-row work-groups whose
-// 4 waves split the keys (fa_fwd_split.hip).
-constexpr int kFwdSplitRows = 32;
-constexpr int kFwdSplitMaxRows = 2048;
-bool fwd_split_keys(int causal, int window, uint32_t drop_k, int64_t nq, int64_t nk, int64_t batch_heads, int cus);
-hipError_t launch_fwd_bf16_split(const FwdArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_fwd_fp8(const FwdArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs &a, int head_dim, hipStream_t s);

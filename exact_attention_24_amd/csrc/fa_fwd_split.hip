@@ -137,7 +137,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_split_kernel(FwdArgs a) {
   if (jt < nt) dma_tile(kw, kl, kst2, jt);
   for (; jt < nt; jt += NW) {
     wait_dma();  // K(jt), and V of this wave's previous tile, in its slots
-    // S(jt)
+    // the deferred P.V of the previous tile first, so that the V slot frees
+    // (and this tile's V is on its way) before S(jt) is formed
+    if (prev) pv();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    dma_tile(vw, vl, vst2, jt);
+    // S(jt); then the K slot frees for the next tile's K
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       s[kb] = (f32x16){};
@@ -145,11 +150,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_split_kernel(FwdArgs a) {
       for (int kk = 0; kk < NKK; ++kk)
         s[kb] = mfma_bf16(*(const uint4 *)(ks + ((kbase_off ^ (16 * kk)) + kb * 32 * D)), qreg[kk], s[kb]);
     }
-    if (prev) pv();  // V of the previous tile is still in the V slot
-    // K and V slots free once their reads have returned: next K, this V
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (jt + NW < nt) dma_tile(kw, kl, kst2, jt + NW);
-    dma_tile(vw, vl, vst2, jt);
     if (edge(jt)) {
       const uint32_t vo = vis_offset(vr, jt * BC + 4 * hf);
 #pragma unroll
